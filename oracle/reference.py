@@ -1,0 +1,347 @@
+"""Plain float64 numpy oracle (test infrastructure only; see the package docstring).
+
+Conventions fixed here (readings of the pages where they are silent):
+  * LSE is the natural log of the softmax denominator including the scale, the
+    quantity the pages exponentiate with ``torch.exp`` when they merge partial
+    results ([DCA] ``_merge_attn_outputs``).
+  * LSE is token-major ``[N, H]``, the layout the pages hand to ``merge_state_v2``
+    after ``softmax_lse.T.contiguous()`` ([FA] ``forward_extend``, cascade branch).
+  * An empty key set gives O = 0 and LSE = -inf ([DCA]
+    ``_dual_chunk_flash_attn_decoding_with_exp_sums``, which forces exactly that
+    for zero-length rows). Merging only -inf parts gives (0, -inf).
+  * Page-table entries past a request's last page are 0.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+
+# ---------------------------------------------------------------------------
+# Integer metadata
+# ---------------------------------------------------------------------------
+
+def cu_seqlens(lens) -> np.ndarray:
+    """Exclusive prefix sum with a leading zero: lengths [4, 6] -> [0, 4, 10].
+
+    [DCA] ``DualChunkFlashAttentionMetadata`` (the ``query_start_loc`` /
+    ``seq_start_loc`` fields and their worked example); [FA]
+    ``init_forward_metadata`` builds ``cu_seqlens_k`` as ``cumsum`` padded with
+    one leading zero.
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    out = np.zeros(len(lens) + 1, dtype=np.int64)
+    total = 0
+    for i, n in enumerate(lens):
+        total += int(n)
+        out[i + 1] = total
+    return out.astype(np.int32)
+
+
+def page_table_strided(req_to_token, req_pool_indices, seq_lens, page_size, width):
+    """Token-level ``req_to_token`` rows -> page table of page ids.
+
+    [FA] ``init_forward_metadata``: the row ``req_to_token[req_pool_indices[b]]``
+    is taken, then "converted to a strided format": every ``page_size``-th
+    column, integer-divided by ``page_size``. [DCA] ``init_forward_metadata``
+    does the same for ``block_tables``. Columns past ``ceil(L_b / page_size)``
+    are 0. ``kv_lens`` is ``seq_lens`` as int32 and ``cu_seqlens_k`` its
+    zero-led prefix sum (``cache_seqlens_int32`` / ``cu_seqlens_k``).
+    """
+    req_to_token = np.asarray(req_to_token)
+    rpi = np.asarray(req_pool_indices)
+    seq_lens = np.asarray(seq_lens)
+    batch = len(rpi)
+    pt = np.zeros((batch, width), dtype=np.int32)
+    for b in range(batch):
+        r = int(rpi[b])
+        n_pages = -(-int(seq_lens[b]) // page_size)
+        for p in range(n_pages):
+            pt[b, p] = int(req_to_token[r, p * page_size]) // page_size
+    kv_lens = seq_lens.astype(np.int32).copy()
+    return pt, kv_lens, cu_seqlens(kv_lens)
+
+
+def page_table_pa_swa(req_to_token, req_pool_indices, seq_lens, prefill_lens, window, width):
+    """Prefill-aware sliding-window token table, by the formula on the page.
+
+    [FA] ``_build_pa_page_table_kernel`` and its wrapper ``_build_pa_page_table``:
+    per request, ``pf`` is read from the pool-sized ``prefill_lens`` through the
+    request's pool row; ``decode_start = max(pf, sl - window)``;
+    ``gap = decode_start - pf`` if positive, else 0; ``kv_len = sl - gap``;
+    destination column ``j < kv_len`` takes ``req_to_token[row, j]`` when
+    ``j < pf`` and ``req_to_token[row, j + gap]`` otherwise. The destination
+    buffer starts zeroed, so columns ``>= kv_len`` are 0.
+    """
+    req_to_token = np.asarray(req_to_token)
+    rpi = np.asarray(req_pool_indices)
+    seq_lens = np.asarray(seq_lens)
+    prefill_lens = np.asarray(prefill_lens)
+    batch = len(rpi)
+    pt = np.zeros((batch, width), dtype=np.int32)
+    kv_lens = np.zeros(batch, dtype=np.int32)
+    for b in range(batch):
+        r = int(rpi[b])
+        sl = int(seq_lens[b])
+        pf = int(prefill_lens[r])
+        decode_start = max(pf, sl - window)
+        gap = decode_start - pf if decode_start > pf else 0
+        kv_len = sl - gap
+        kv_lens[b] = kv_len
+        for j in range(kv_len):
+            pos = j if j < pf else j + gap
+            pt[b, j] = int(req_to_token[r, pos])
+    return pt, kv_lens, cu_seqlens(kv_lens)
+
+
+def page_table_pa_swa_bruteforce(req_to_token, req_pool_indices, seq_lens, prefill_lens,
+                                 window, width):
+    """The same table by set construction, from the kernel's docstring alone.
+
+    [FA] ``_build_pa_page_table_kernel`` docstring: the row is the tokens of
+    ``[0, prefill_len)`` together with ``[decode_start, seq_len)``, in increasing
+    order, ``decode_start = max(prefill_len, seq_len - window)``. Tokens are
+    limited to the ``seq_len`` tokens that exist.
+    """
+    req_to_token = np.asarray(req_to_token)
+    batch = len(req_pool_indices)
+    pt = np.zeros((batch, width), dtype=np.int32)
+    kv_lens = np.zeros(batch, dtype=np.int32)
+    for b in range(batch):
+        r = int(req_pool_indices[b])
+        sl = int(seq_lens[b])
+        pf = int(prefill_lens[r])
+        decode_start = max(pf, sl - window)
+        keep = set(range(0, pf)) | set(range(decode_start, sl))
+        keep = sorted(t for t in keep if t < sl)
+        kv_lens[b] = len(keep)
+        for j, t in enumerate(keep):
+            pt[b, j] = int(req_to_token[r, t])
+    return pt, kv_lens, cu_seqlens(kv_lens)
+
+
+def visible_key_counts(num_new, kv_len, causal=True) -> np.ndarray:
+    """How many leading keys each of a request's new query rows may see.
+
+    The new rows are the last ``num_new`` positions of a ``kv_len``-token
+    sequence, so row ``j`` sits at absolute position ``kv_len - num_new + j`` and
+    sees keys ``[0, kv_len - num_new + j]`` (bottom-right causal alignment).
+    [NSA] ``_cal_indexer_k_start_end`` (``seq_lens_expanded`` runs from
+    ``kv_len - extend_len + 1`` to ``kv_len``, with the printed two-request
+    example); [DCA] ``_dual_chunk_flash_attn_prefill_func`` starts at
+    ``begin = k_length - q_len``. Non-causal rows see all ``kv_len`` keys.
+    """
+    if not causal:
+        return np.full(num_new, kv_len, dtype=np.int64)
+    return np.array([kv_len - num_new + j + 1 for j in range(num_new)], dtype=np.int64)
+
+
+def causal_key_ranges(extend_lens, seq_lens):
+    """Per new token, the key range ``[ks, ke)`` in a batch-concatenated key axis.
+
+    [NSA] ``_cal_indexer_k_start_end``: ``ks`` is the request's key offset (the
+    running sum of earlier ``seq_lens``) and ``ke = ks + visible count``.
+    """
+    ks, ke = [], []
+    k_offset = 0
+    for m, L in zip(extend_lens, seq_lens):
+        counts = visible_key_counts(int(m), int(L), causal=True)
+        for c in counts:
+            ks.append(k_offset)
+            ke.append(k_offset + int(c))
+        k_offset += int(L)
+    return np.array(ks, dtype=np.int64), np.array(ke, dtype=np.int64)
+
+
+def kv_head_of(q_head, num_q_heads, num_kv_heads) -> int:
+    """GQA: q head ``h`` reads kv head ``h // (Hq / Hkv)``.
+
+    [DCA] ``_dual_chunk_flash_attn_prefill_func``: ``current_k[..., head_id //
+    group_size, :]`` with ``group_size = num_heads // num_kv_heads``.
+    """
+    group = num_q_heads // num_kv_heads
+    return q_head // group
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def gather_paged(cache, page_row, length, page_size) -> np.ndarray:
+    """Logical token ``t`` of a request lives at ``cache[page_row[t // P], t % P]``.
+
+    [FA] ``forward_extend`` views the KV buffer as
+    ``[num_pages, page_size, H_kv, D]`` and passes the page table; [DCA]
+    ``_get_block`` / the prefill loop gathers whole pages, flattens them and
+    truncates to the sequence length.
+    """
+    out = np.empty((length,) + tuple(cache.shape[2:]), dtype=np.float64)
+    for t in range(length):
+        out[t] = cache[int(page_row[t // page_size]), t % page_size]
+    return out
+
+
+def softmax_attention(q, keys, values, scale):
+    """One query vector against a key set: ``(O, LSE)`` in float64.
+
+    ``s_t = scale * <q, k_t>``; ``LSE = m + ln sum_t exp(s_t - m)`` with
+    ``m = max_t s_t``; ``O = sum_t exp(s_t - LSE) v_t``. An empty key set gives
+    ``(0, -inf)`` ([DCA] ``_dual_chunk_flash_attn_decoding_with_exp_sums``).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    if keys.shape[0] == 0:
+        return np.zeros(values.shape[-1], dtype=np.float64), NEG_INF
+    s = scale * (keys @ q)
+    m = np.max(s)
+    lse = m + math.log(np.sum(np.exp(s - m)))
+    p = np.exp(s - lse)
+    return p @ values, lse
+
+
+def paged_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, page_size,
+                  scale, causal=True):
+    """Varlen extend/prefill over a paged cache.
+
+    [FA] ``forward_extend``: ``flash_attn_with_kvcache`` with
+    ``cache_seqlens`` = prefix + new length, ``cu_seqlens_q`` over the new
+    tokens and ``causal=True``; the new tokens' keys are already in the cache, so
+    each row attends to prefix and new keys through the page table.
+
+    q: [total_q, Hq, D]; caches: [pages, P, Hkv, Dk|Dv]. Returns
+    O [total_q, Hq, Dv] and LSE [total_q, Hq], float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_cache = np.asarray(k_cache)
+    v_cache = np.asarray(v_cache)
+    total_q, num_q_heads, _ = q.shape
+    num_kv_heads = k_cache.shape[2]
+    dv = v_cache.shape[3]
+    out = np.zeros((total_q, num_q_heads, dv), dtype=np.float64)
+    lse = np.full((total_q, num_q_heads), NEG_INF, dtype=np.float64)
+    batch = len(kv_lens)
+    for b in range(batch):
+        q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        L = int(kv_lens[b])
+        keys = gather_paged(k_cache, page_table[b], L, page_size)
+        vals = gather_paged(v_cache, page_table[b], L, page_size)
+        counts = visible_key_counts(q1 - q0, L, causal)
+        for j in range(q1 - q0):
+            n = int(counts[j])
+            for h in range(num_q_heads):
+                kvh = kv_head_of(h, num_q_heads, num_kv_heads)
+                o, l_ = softmax_attention(q[q0 + j, h], keys[:n, kvh], vals[:n, kvh], scale)
+                out[q0 + j, h] = o
+                lse[q0 + j, h] = l_
+    return out, lse
+
+
+def paged_decode_splitkv(q, k_cache, v_cache, page_table, kv_lens, page_size, scale,
+                         kv_chunk, num_splits):
+    """Decode (one new token per request) with the key axis cut into chunks.
+
+    Split ``s`` covers keys ``[s*C, min((s+1)*C, L_b))`` and yields the partial
+    ``(O_s, LSE_s)`` over that range alone; an empty range yields ``(0, -inf)``.
+    [FA] ``forward_decode`` (``flash_attn_with_kvcache`` with ``num_splits``);
+    [DCA] ``_dual_chunk_flash_attn_decoding`` runs several paged decodes over
+    disjoint key ranges with ``return_softmax_lse=True`` and merges them, and
+    ``_dual_chunk_flash_attn_decoding_with_exp_sums`` fixes empty ranges to
+    ``(0, -inf)``. ``kv_chunk = 0`` means a single split over all keys.
+
+    q: [B, Hq, D]. Returns o_partial [S, B, Hq, Dv] and lse_partial [S, B, Hq].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    batch, num_q_heads, _ = q.shape
+    num_kv_heads = k_cache.shape[2]
+    dv = v_cache.shape[3]
+    o_part = np.zeros((num_splits, batch, num_q_heads, dv), dtype=np.float64)
+    lse_part = np.full((num_splits, batch, num_q_heads), NEG_INF, dtype=np.float64)
+    for b in range(batch):
+        L = int(kv_lens[b])
+        keys = gather_paged(k_cache, page_table[b], L, page_size)
+        vals = gather_paged(v_cache, page_table[b], L, page_size)
+        for s in range(num_splits):
+            if kv_chunk == 0:
+                lo, hi = (0, L) if s == 0 else (L, L)
+            else:
+                lo, hi = min(s * kv_chunk, L), min((s + 1) * kv_chunk, L)
+            for h in range(num_q_heads):
+                kvh = kv_head_of(h, num_q_heads, num_kv_heads)
+                o, l_ = softmax_attention(q[b, h], keys[lo:hi, kvh], vals[lo:hi, kvh], scale)
+                o_part[s, b, h] = o
+                lse_part[s, b, h] = l_
+    return o_part, lse_part
+
+
+def merge_state(o_parts, lse_parts):
+    """Combine partial states ``(O_s, LSE_s)`` computed over disjoint key sets.
+
+    [DCA] ``_merge_attn_outputs`` and the end of ``_dual_chunk_flash_attn_decoding``:
+    ``m = max_s LSE_s``, ``w_s = exp(LSE_s - m)``, ``O = sum_s w_s O_s / sum_s w_s``;
+    the merged LSE is ``m + ln sum_s w_s`` (for two parts the page writes it as
+    ``max + log1p(exp(-|l0 - l1|))``). [FA] ``forward_extend`` merges a prefix
+    pass and an expand pass with ``merge_state_v2(o_a, lse_a, o_b, lse_b)``.
+    All parts at -inf give ``(0, -inf)``.
+
+    o_parts: [S, N, H, Dv]; lse_parts: [S, N, H].
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    S, N, H, Dv = o_parts.shape
+    out = np.zeros((N, H, Dv), dtype=np.float64)
+    lse = np.full((N, H), NEG_INF, dtype=np.float64)
+    for n in range(N):
+        for h in range(H):
+            m = max(lse_parts[s, n, h] for s in range(S))
+            if m == NEG_INF:
+                continue
+            w = [math.exp(lse_parts[s, n, h] - m) for s in range(S)]
+            total = math.fsum(w)
+            acc = np.zeros(Dv, dtype=np.float64)
+            for s in range(S):
+                if w[s] != 0.0:
+                    acc += w[s] * o_parts[s, n, h]
+            out[n, h] = acc / total
+            lse[n, h] = m + math.log(total)
+    return out, lse
+
+
+def sparse_topk_decode(q, kv_cache, req_to_token, req_pool_indices, topk_idx, scale,
+                       head_dim_v):
+    """Top-k index-gathered MLA decode over one latent KV head.
+
+    [NSA] ``forward_decode``: the top-k *logical* token indices are mapped to
+    cache slots through the request's token table
+    (``transform_index_page_table_decode`` with page size 1), and entries equal
+    to -1 are padding that is skipped (``_pad_topk_indices`` pads with -1;
+    ``_forward_aiter`` keeps only entries ``!= -1``). [NSA] ``_forward_fa3``
+    fixes the arithmetic: the cache row is ``[c_kv (first Dv) | k_rope (rest)]``,
+    the score adds ``q_rope . k_rope`` and ``q_nope . c_kv`` -- a dot product over
+    the whole row with ``q = [q_nope | q_rope]`` -- and the value is ``c_kv``.
+
+    q: [B, Hq, Dqk]; kv_cache: [slots, Dqk]; topk_idx: [B, K] (may hold -1).
+    Returns O [B, Hq, Dv] and LSE [B, Hq], float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kv_cache = np.asarray(kv_cache)
+    batch, num_heads, _ = q.shape
+    out = np.zeros((batch, num_heads, head_dim_v), dtype=np.float64)
+    lse = np.full((batch, num_heads), NEG_INF, dtype=np.float64)
+    for b in range(batch):
+        r = int(req_pool_indices[b])
+        slots = [int(req_to_token[r, int(i)]) for i in topk_idx[b] if int(i) != -1]
+        rows = np.zeros((len(slots), kv_cache.shape[-1]), dtype=np.float64)
+        for j, s in enumerate(slots):
+            rows[j] = kv_cache[s]
+        keys = rows
+        vals = rows[:, :head_dim_v]
+        for h in range(num_heads):
+            o, l_ = softmax_attention(q[b, h], keys, vals, scale)
+            out[b, h] = o
+            lse[b, h] = l_
+    return out, lse

@@ -1,0 +1,420 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+None of these retypes the oracle's formulas: the references are the pages'
+printed examples (tests/golden), closed forms, torch's own attention / logsumexp
+routines on dense tensors, brute-force set construction, and invariants.
+The planted-mistake tests at the end show that each pin bites.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.reference as ref
+import workloads
+from conftest import f64, i64
+
+# ---------------------------------------------------------------------------
+# Library-routine references (dense, built from req_to_token, not the page table)
+# ---------------------------------------------------------------------------
+
+
+def dense_request_kv(cache, req_to_token, row, L):
+    """Logical [L, Hkv, D] keys of one request, read through the token-level table."""
+    flat = cache.reshape(-1, cache.shape[2], cache.shape[3])
+    slots = req_to_token[row, :L].long()
+    return flat[slots].to(torch.float64)
+
+
+def sdpa_reference(q_rows, keys, vals, scale, causal):
+    """torch SDPA (float64, explicit mask) and torch.logsumexp for LSE.
+
+    q_rows [M, Hq, D]; keys/vals [L, Hkv, D]. Causal uses torch.tril's
+    bottom-right diagonal offset L - M.
+    """
+    M, Hq, _ = q_rows.shape
+    L, Hkv, _ = keys.shape
+    g = Hq // Hkv
+    q = q_rows.permute(1, 0, 2).unsqueeze(0)                       # [1, Hq, M, D]
+    k = keys.permute(1, 0, 2).repeat_interleave(g, dim=0).unsqueeze(0)
+    v = vals.permute(1, 0, 2).repeat_interleave(g, dim=0).unsqueeze(0)
+    mask = torch.ones(M, L, dtype=torch.bool)
+    if causal:
+        mask = torch.tril(mask, diagonal=L - M)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    logits = torch.matmul(q, k.transpose(-1, -2)) * scale
+    logits = logits.masked_fill(~mask, -math.inf)
+    lse = torch.logsumexp(logits, dim=-1)                          # [1, Hq, M]
+    return o[0].permute(1, 0, 2).numpy(), lse[0].permute(1, 0).numpy()
+
+
+def _worst(acc, x):
+    """Running max error where a NaN anywhere counts as an infinite error."""
+    x = float(x)
+    return math.inf if math.isnan(x) else max(acc, x)
+
+
+def prefill_error_vs_sdpa(case):
+    pt, kv_lens, _ = oracle.page_table_strided(i64(case.req_to_token), i64(case.req_pool_indices),
+                                               i64(case.seq_lens), case.page_size, case.table_width)
+    o, lse = oracle.paged_prefill(f64(case.q), f64(case.k_cache), f64(case.v_cache), pt,
+                                  i64(case.cu_seqlens_q), kv_lens, case.page_size, case.scale)
+    err_o = err_l = 0.0
+    cu = i64(case.cu_seqlens_q)
+    qd = case.q.to(torch.float64)
+    for b in range(len(kv_lens)):
+        L = int(kv_lens[b])
+        row = int(case.req_pool_indices[b])
+        K = dense_request_kv(case.k_cache, case.req_to_token, row, L)
+        V = dense_request_kv(case.v_cache, case.req_to_token, row, L)
+        o_ref, l_ref = sdpa_reference(qd[cu[b]:cu[b + 1]], K, V, case.scale, causal=True)
+        err_o = _worst(err_o, np.abs(o[cu[b]:cu[b + 1]] - o_ref).max())
+        err_l = _worst(err_l, np.abs(lse[cu[b]:cu[b + 1]] - l_ref).max())
+    return err_o, err_l
+
+
+def decode_error_vs_sdpa(case):
+    pt, kv_lens, _ = oracle.page_table_strided(i64(case.req_to_token), i64(case.req_pool_indices),
+                                               i64(case.seq_lens), case.page_size, case.table_width)
+    o, lse = oracle.paged_decode_splitkv(f64(case.q), f64(case.k_cache), f64(case.v_cache), pt,
+                                         kv_lens, case.page_size, case.scale, 0, 1)
+    err_o = err_l = 0.0
+    qd = case.q.to(torch.float64)
+    for b in range(len(kv_lens)):
+        L = int(kv_lens[b])
+        row = int(case.req_pool_indices[b])
+        K = dense_request_kv(case.k_cache, case.req_to_token, row, L)
+        V = dense_request_kv(case.v_cache, case.req_to_token, row, L)
+        o_ref, l_ref = sdpa_reference(qd[b:b + 1], K, V, case.scale, causal=False)
+        err_o = _worst(err_o, np.abs(o[0, b] - o_ref[0]).max())
+        err_l = _worst(err_l, np.abs(lse[0, b] - l_ref[0]).max())
+    return err_o, err_l
+
+
+def small_prefill(seed=21, dtype=torch.float32):
+    return workloads.make_prefill_case(seed, prefix_lens=[0, 5, 17, 3], extend_lens=[7, 1, 9, 4],
+                                       num_q_heads=6, num_kv_heads=2, head_dim=8, page_size=4,
+                                       num_pages=40, dtype=dtype)
+
+
+def small_decode(seed=22, dtype=torch.float32, page_size=4, kv_chunk=0):
+    return workloads.make_decode_case(seed, seq_lens=[1, 13, 30, 8], num_q_heads=8, num_kv_heads=2,
+                                      head_dim=16, page_size=page_size, num_pages=64, dtype=dtype,
+                                      kv_chunk=kv_chunk, ctx=32)
+
+
+# ---------------------------------------------------------------------------
+# Printed examples
+# ---------------------------------------------------------------------------
+
+
+def test_cu_seqlens_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "cu_seqlens_example.json")))
+    assert oracle.cu_seqlens(g["lens"]).tolist() == g["cu_seqlens"]
+
+
+def test_causal_alignment_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "causal_ranges_example.json")))
+    ks, ke = oracle.causal_key_ranges(g["extend_seq_lens"], g["seq_lens"])
+    assert ks.tolist() == g["ks"] and ke.tolist() == g["ke"]
+    # the figure: rows are new tokens, columns the two requests' keys side by side
+    rows = []
+    for m, L in zip(g["extend_seq_lens"], g["seq_lens"]):
+        counts = oracle.visible_key_counts(m, L)
+        for c in counts:
+            rows.append((m, L, int(c)))
+    total = sum(g["seq_lens"])
+    drawn = []
+    r = 0
+    for b, (m, L) in enumerate(zip(g["extend_seq_lens"], g["seq_lens"])):
+        for j in range(m):
+            c = rows[r][2]
+            line = ["-"] * total
+            off = sum(g["seq_lens"][:b])
+            for t in range(c):
+                line[off + t] = "*"
+            s = "".join(line)
+            drawn.append(s[:g["seq_lens"][0]] + "|" + s[g["seq_lens"][0]:])
+            r += 1
+    assert drawn == g["mask_figure"]
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+
+def test_uniform_scores_give_mean_of_values():
+    rng = np.random.default_rng(0)
+    for n in [1, 2, 7, 64]:
+        V = rng.standard_normal((n, 5))
+        K = rng.standard_normal((n, 3))
+        o, lse = oracle.softmax_attention(np.zeros(3), K, V, scale=0.7)
+        assert np.allclose(o, V.mean(axis=0), atol=1e-14, rtol=0)
+        assert abs(lse - math.log(n)) < 1e-14
+
+
+def test_single_key_and_equal_pair():
+    q = np.array([0.5, -1.0, 2.0])
+    k = np.array([[1.0, 2.0, 0.25]])
+    v = np.array([[3.0, -4.0]])
+    o, lse = oracle.softmax_attention(q, k, v, scale=0.5)
+    s = 0.5 * (0.5 * 1.0 - 1.0 * 2.0 + 2.0 * 0.25)
+    assert np.array_equal(o, v[0]) and abs(lse - s) < 1e-15
+    k2 = np.vstack([k, k])
+    v2 = np.array([[1.0, 0.0], [3.0, 4.0]])
+    o, lse = oracle.softmax_attention(q, k2, v2, scale=0.5)
+    assert np.allclose(o, [2.0, 2.0], atol=1e-15) and abs(lse - (s + math.log(2))) < 1e-14
+
+
+def test_empty_key_set():
+    o, lse = oracle.softmax_attention(np.ones(4), np.zeros((0, 4)), np.zeros((0, 3)), 1.0)
+    assert lse == -math.inf and np.array_equal(o, np.zeros(3))
+
+
+def test_merge_closed_forms():
+    rng = np.random.default_rng(1)
+    oa, ob = rng.standard_normal((2, 1, 1, 4))
+    # equal LSE: plain average, LSE + ln 2
+    o, l = oracle.merge_state(np.stack([oa, ob]), np.full((2, 1, 1), 0.3))
+    assert np.allclose(o, (oa + ob) / 2, atol=1e-15) and abs(l[0, 0] - (0.3 + math.log(2))) < 1e-15
+    # the page's two-part LSE expression: max + log1p(exp(-|l0 - l1|))
+    for l0, l1 in [(0.1, 2.5), (-7.0, 3.0), (5.0, 5.0)]:
+        _, l = oracle.merge_state(np.stack([oa, ob]), np.array([l0, l1]).reshape(2, 1, 1))
+        assert abs(l[0, 0] - (max(l0, l1) + math.log1p(math.exp(-abs(l0 - l1))))) < 1e-14
+    # a -inf part carries no weight; all -inf gives (0, -inf)
+    o, l = oracle.merge_state(np.stack([oa, ob]), np.array([-math.inf, 1.5]).reshape(2, 1, 1))
+    assert np.array_equal(o, ob) and l[0, 0] == 1.5
+    o, l = oracle.merge_state(np.stack([oa, ob]), np.full((2, 1, 1), -math.inf))
+    assert np.array_equal(o, np.zeros_like(oa)) and l[0, 0] == -math.inf
+
+
+# ---------------------------------------------------------------------------
+# Library routines on dense tensors
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_matches_torch_sdpa(dtype):
+    e_o, e_l = prefill_error_vs_sdpa(small_prefill(dtype=dtype))
+    assert e_o < 1e-12 and e_l < 1e-12
+
+
+@pytest.mark.parametrize("page_size", [1, 4, 16])
+def test_decode_matches_torch_sdpa(page_size):
+    e_o, e_l = decode_error_vs_sdpa(small_decode(page_size=page_size))
+    assert e_o < 1e-12 and e_l < 1e-12
+
+
+def test_sparse_all_tokens_matches_torch_sdpa():
+    """Top-k = every context token (shuffled) is dense MLA attention, Dqk 576 / Dv 512."""
+    case = workloads.make_sparse_case(31, batch=2, ctx=40, topk=40, num_q_heads=4,
+                                      head_dim_qk=576, head_dim_v=512, dtype=torch.float32)
+    o, lse = oracle.sparse_topk_decode(f64(case.q), f64(case.kv_cache), i64(case.req_to_token),
+                                       i64(case.req_pool_indices), i64(case.topk_idx),
+                                       case.scale, case.head_dim_v)
+    for b in range(2):
+        row = int(case.req_pool_indices[b])
+        rows = case.kv_cache[case.req_to_token[row, :40].long()].to(torch.float64)
+        q = case.q[b].to(torch.float64)[None, :, None, :]             # [1, H, 1, 576]
+        k = rows[None, None].expand(1, 4, 40, 576)
+        v = rows[:, :512][None, None].expand(1, 4, 40, 512)
+        o_ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=case.scale)
+        lse_ref = torch.logsumexp(torch.matmul(q, k.transpose(-1, -2)) * case.scale, dim=-1)
+        assert np.abs(o[b] - o_ref[0, :, 0].numpy()).max() < 1e-12
+        assert np.abs(lse[b] - lse_ref[0, :, 0].numpy()).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("page_size,chunk", [(4, 4), (4, 8), (4, 12), (16, 16), (1, 5), (4, 64)])
+def test_split_then_merge_equals_unsplit(page_size, chunk):
+    case = small_decode(page_size=page_size)
+    pt, kv_lens, _ = oracle.page_table_strided(i64(case.req_to_token), i64(case.req_pool_indices),
+                                               i64(case.seq_lens), page_size, case.table_width)
+    args = (f64(case.q), f64(case.k_cache), f64(case.v_cache), pt, kv_lens, page_size, case.scale)
+    o1, l1 = oracle.paged_decode_splitkv(*args, 0, 1)
+    S = -(-int(kv_lens.max()) // chunk) + 1          # one extra, always empty, split
+    op, lp = oracle.paged_decode_splitkv(*args, chunk, S)
+    assert np.all(np.isneginf(lp[-1]))
+    o2, l2 = oracle.merge_state(op, lp)
+    assert np.abs(o2 - o1[0]).max() < 1e-12 and np.abs(l2 - l1[0]).max() < 1e-12
+
+
+def _permute_pages(case, seed):
+    """Move every physical page to a new place and rewrite req_to_token to match."""
+    P = case.page_size
+    n = case.k_cache.shape[0]
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(seed))
+    k = torch.empty_like(case.k_cache)
+    v = torch.empty_like(case.v_cache)
+    k[perm] = case.k_cache
+    v[perm] = case.v_cache
+    r2t = case.req_to_token.long()
+    r2t = perm[r2t // P] * P + r2t % P
+    return k, v, r2t.to(torch.int32)
+
+
+def test_page_permutation_is_bit_identical():
+    case = small_decode(page_size=4)
+    k, v, r2t = _permute_pages(case, 5)
+    outs = []
+    for kc, vc, rt in [(case.k_cache, case.v_cache, case.req_to_token), (k, v, r2t)]:
+        pt, kv_lens, _ = oracle.page_table_strided(i64(rt), i64(case.req_pool_indices),
+                                                   i64(case.seq_lens), 4, case.table_width)
+        outs.append(oracle.paged_decode_splitkv(f64(case.q), f64(kc), f64(vc), pt, kv_lens, 4,
+                                                case.scale, 8, 4))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_strided_table_invariant():
+    case = small_decode(page_size=4)
+    r2t, rpi, sl = i64(case.req_to_token), i64(case.req_pool_indices), i64(case.seq_lens)
+    pt, kv_lens, cu = oracle.page_table_strided(r2t, rpi, sl, 4, case.table_width)
+    assert kv_lens.tolist() == sl.tolist() and cu.tolist() == [0] + np.cumsum(sl).tolist()
+    for b in range(len(rpi)):
+        L = int(sl[b])
+        for t in range(L):
+            assert r2t[rpi[b], t] // 4 == pt[b, t // 4]
+        assert np.all(pt[b, -(-L // 4):] == 0)
+
+
+def _random_swa_inputs(rng, batch, ctx):
+    rows = 2 * batch
+    r2t = rng.integers(0, 10_000, size=(rows, ctx))
+    rpi = rng.permutation(rows)[:batch]
+    pf_pool = rng.integers(0, ctx, size=rows)
+    sl = rng.integers(1, ctx + 1, size=batch)
+    return r2t, rpi, sl, pf_pool
+
+
+def test_pa_swa_formula_matches_set_construction():
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        batch = int(rng.integers(1, 6))
+        ctx = int(rng.integers(1, 60))
+        r2t, rpi, sl, pf = _random_swa_inputs(rng, batch, ctx)
+        window = int(rng.integers(0, 70))
+        a = oracle.page_table_pa_swa(r2t, rpi, sl, pf, window, ctx)
+        b = oracle.page_table_pa_swa_bruteforce(r2t, rpi, sl, pf, window, ctx)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y), trial
+
+
+def test_pa_swa_edge_cases():
+    r2t = np.arange(40).reshape(2, 20) + 100
+    rpi = np.array([1])
+    # window reaches back into the prefill: nothing is dropped
+    pt, kv, _ = oracle.page_table_pa_swa(r2t, rpi, [12], np.array([0, 10]), 5, 20)
+    assert kv.tolist() == [12] and pt[0, :12].tolist() == list(range(120, 132))
+    # a gap: keep [0, 4) and the last 3 of 15
+    pt, kv, _ = oracle.page_table_pa_swa(r2t, rpi, [15], np.array([0, 4]), 3, 20)
+    assert kv.tolist() == [7] and pt[0, :7].tolist() == [120, 121, 122, 123, 132, 133, 134]
+    assert np.all(pt[0, 7:] == 0)
+    # kv_len 1: no prefill, window 1
+    pt, kv, _ = oracle.page_table_pa_swa(r2t, rpi, [9], np.array([0, 0]), 1, 20)
+    assert kv.tolist() == [1] and pt[0, 0] == 128
+
+
+def test_sparse_invariants():
+    case = workloads.make_sparse_case(32, batch=2, ctx=200, topk=50, num_q_heads=4,
+                                      head_dim_qk=576, head_dim_v=512, dtype=torch.bfloat16)
+    args = (f64(case.q), f64(case.kv_cache), i64(case.req_to_token), i64(case.req_pool_indices))
+    idx = i64(case.topk_idx)
+    o, l = oracle.sparse_topk_decode(*args, idx, case.scale, 512)
+    # order of the top-k list does not matter
+    rng = np.random.default_rng(3)
+    shuffled = np.stack([rng.permutation(r) for r in idx])
+    o2, l2 = oracle.sparse_topk_decode(*args, shuffled, case.scale, 512)
+    assert np.abs(o - o2).max() < 1e-12 and np.abs(l - l2).max() < 1e-12
+    # -1 entries are skipped: same as dropping them
+    padded = idx.copy()
+    padded[:, 40:] = -1
+    o3, l3 = oracle.sparse_topk_decode(*args, padded, case.scale, 512)
+    o4, l4 = oracle.sparse_topk_decode(*args, idx[:, :40], case.scale, 512)
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+    # an all -1 row is the empty set
+    o5, l5 = oracle.sparse_topk_decode(*args, np.full_like(idx, -1), case.scale, 512)
+    assert np.all(o5 == 0) and np.all(np.isneginf(l5))
+
+
+def test_workload_configs_have_the_stated_shapes():
+    c1 = workloads.config1()
+    assert c1.q.shape == (2, 4, 64) and c1.k_cache.shape == (16, 16, 2, 64)
+    assert c1.seq_lens.tolist() == [37, 100] and c1.num_splits == 2 and c1.q.dtype == torch.float32
+    c2 = workloads.config2()
+    assert c2.q.shape == (849, 32, 128) and c2.seq_lens.tolist() == [256, 192, 1024, 1017]
+    assert c2.cu_seqlens_q.tolist() == [0, 256, 320, 832, 849]
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each pin above must catch a plausible error in the oracle
+# ---------------------------------------------------------------------------
+
+
+def test_planted_wrong_gqa_mapping_is_caught(monkeypatch):
+    monkeypatch.setattr(ref, "kv_head_of", lambda h, hq, hkv: h % hkv)
+    e_o, _ = prefill_error_vs_sdpa(small_prefill())
+    assert e_o > 1e-3
+
+
+def test_planted_off_by_one_causal_is_caught(monkeypatch, golden_dir):
+    real = ref.visible_key_counts
+    monkeypatch.setattr(ref, "visible_key_counts",
+                        lambda m, L, causal=True: real(m, L, causal) - (1 if causal else 0))
+    e_o, _ = prefill_error_vs_sdpa(small_prefill())
+    assert e_o > 1e-3
+    with pytest.raises(AssertionError):
+        test_causal_alignment_worked_example(golden_dir)
+
+
+def test_planted_wrong_gather_is_caught(monkeypatch):
+    def bad_gather(cache, page_row, length, page_size):
+        out = np.empty((length,) + tuple(cache.shape[2:]))
+        for t in range(length):
+            out[t] = cache[int(page_row[t // page_size]), (page_size - 1 - t % page_size)]
+        return out
+    monkeypatch.setattr(ref, "gather_paged", bad_gather)
+    e_o, _ = decode_error_vs_sdpa(small_decode(page_size=4))
+    assert not (e_o < 1e-3)          # wrong values or NaN from unowned slots
+
+
+def test_planted_missing_scale_is_caught(monkeypatch):
+    real = ref.softmax_attention
+    monkeypatch.setattr(ref, "softmax_attention", lambda q, k, v, scale: real(q, k, v, 1.0))
+    e_o, e_l = decode_error_vs_sdpa(small_decode())
+    assert e_o > 1e-3 or e_l > 1e-3
+
+
+def test_planted_unnormalised_merge_is_caught(monkeypatch):
+    def bad_merge(o_parts, lse_parts):
+        w = np.exp(lse_parts - lse_parts.max(axis=0))
+        return (w[..., None] * o_parts).sum(0), lse_parts.max(axis=0)
+    monkeypatch.setattr(oracle, "merge_state", bad_merge)
+    with pytest.raises(AssertionError):
+        test_split_then_merge_equals_unsplit(4, 8)
+
+
+def test_planted_pa_swa_gap_mistake_is_caught(monkeypatch):
+    def bad(req_to_token, rpi, seq_lens, prefill_lens, window, width):
+        pt = np.zeros((len(rpi), width), dtype=np.int32)
+        kv = np.zeros(len(rpi), dtype=np.int32)
+        for b in range(len(rpi)):
+            r, sl, pf = int(rpi[b]), int(seq_lens[b]), int(prefill_lens[int(rpi[b])])
+            ds = max(pf, sl - window)
+            gap = ds - pf
+            kv[b] = sl - gap
+            for j in range(kv[b]):
+                pt[b, j] = req_to_token[r, j if j <= pf else j + gap]   # <= instead of <
+        return pt, kv, oracle.cu_seqlens(kv)
+    monkeypatch.setattr(oracle, "page_table_pa_swa", bad)
+    with pytest.raises(AssertionError):
+        test_pa_swa_formula_matches_set_construction()
