@@ -1,0 +1,211 @@
+/*
+ * pkv.h -- paged, variable-length attention over a page-table-indexed KV cache,
+ * for AMD Instinct MI355X (gfx950). C ABI of libpkv.so.
+ *
+ * Passages cited below are from these pages (title; section = function/class):
+ *   [DCA] "sglang 0.4.10.post2 -> 0.5.0rc0: sglang/srt/layers/attention/
+ *          dual_chunk_flashattention_backend.py"
+ *   [FA]  "sgl-project--sglang/python/sglang/srt/layers/attention/
+ *          flashattention_backend.py"
+ *   [NSA] "sglang/srt/layers/attention/nsa_backend.py"
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a caller-owned DEVICE pointer (hipMalloc'd or a
+ *     torch tensor's data_ptr()), dense and row-major in the layout given.
+ *     The library allocates nothing, keeps no state between calls and is
+ *     reentrant.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on
+ *     it and the call returns without synchronising.
+ *   - Return value is a pkv_status_t. Argument errors that the host can see
+ *     (NULL required pointers, bad sizes, unsupported head dims or dtypes) are
+ *     reported synchronously before anything is enqueued; PKV_ELAUNCH reports a
+ *     failed kernel launch. pkv_last_error() gives a human-readable detail for
+ *     the calling thread.
+ *   - Device-data preconditions (index ranges, lengths that fit the tables) are
+ *     not validated; kernels clamp every index they dereference to the array
+ *     sizes passed in, so a violated precondition gives wrong numbers, never an
+ *     out-of-bounds access.
+ *   - bf16 is IEEE binary16-brain (1-8-7), stored as 16-bit words; results in
+ *     bf16 are rounded to nearest even. Arithmetic is fp32. LSE is the natural
+ *     log of the softmax denominator (scale included); an empty key set gives
+ *     O = 0 and LSE = -inf ([DCA] _dual_chunk_flash_attn_decoding_with_exp_sums).
+ *   - LSE arrays are token-major [tokens, heads] ([FA] forward_extend passes
+ *     softmax_lse.T.contiguous() to merge_state_v2).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,       /* bad argument (NULL, negative size, inconsistent sizes) */
+  PKV_EUNSUPPORTED = 2, /* well-formed but not instantiated (head dim, dtype, group) */
+  PKV_ELAUNCH = 3       /* the HIP runtime rejected a launch */
+} pkv_status_t;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype_t;
+
+/* Static string naming a status code. */
+const char* pkv_status_string(int status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+/*
+ * build_page_table -- integer metadata for one forward pass.
+ *
+ * Strided mode (prefill_lens == NULL), [FA] init_forward_metadata (decode and
+ * extend branches, "strided format" conversion); [DCA] init_forward_metadata:
+ *   page_table[b, p] = req_to_token[r, p * page_size] / page_size
+ *       for p < ceil(L_b / page_size), else 0,   r = req_pool_indices[b],
+ *   kv_lens[b] = L_b = seq_lens[b].
+ * Prefill-aware sliding-window mode (prefill_lens != NULL, page_size must be 1),
+ * [FA] _build_pa_page_table_kernel / _build_pa_page_table:
+ *   pf = prefill_lens[r]  (pool-sized array, indexed by the pool row),
+ *   decode_start = max(pf, seq_lens[b] - window),
+ *   gap = decode_start > pf ? decode_start - pf : 0,
+ *   kv_lens[b] = seq_lens[b] - gap,
+ *   page_table[b, j] = req_to_token[r, j < pf ? j : j + gap] for j < kv_lens[b],
+ *   else 0.
+ * Both modes, when cu_seqlens_k != NULL: cu_seqlens_k = [0, cumsum(kv_lens)].
+ *
+ * req_to_token  [req_to_token_rows, req_to_token_stride] int32 token slot ids
+ * req_pool_indices [batch] int32 rows of req_to_token
+ * seq_lens      [batch] int32
+ * prefill_lens  [req_to_token_rows] int32, or NULL
+ * page_table    [batch, width] int32 (out; every element written)
+ * kv_lens       [batch] int32 (out)
+ * cu_seqlens_k  [batch + 1] int32 (out) or NULL
+ * Errors: PKV_EINVAL for NULL required pointers, batch < 0, width < 0,
+ * page_size < 1, rows/stride < 1 with batch > 0, window < 0 or page_size != 1
+ * in sliding-window mode. batch == 0 is a no-op apart from cu_seqlens_k[0] = 0.
+ */
+pkv_status_t build_page_table(const int32_t* req_to_token, int64_t req_to_token_rows,
+                              int64_t req_to_token_stride, const int32_t* req_pool_indices,
+                              const int32_t* seq_lens, const int32_t* prefill_lens,
+                              int32_t window, int32_t batch, int32_t page_size, int32_t width,
+                              int32_t* page_table, int32_t* kv_lens, int32_t* cu_seqlens_k,
+                              void* stream);
+
+/*
+ * paged_attn_varlen_prefill -- causal extend over a paged cache.
+ * [FA] forward_extend (flash_attn_with_kvcache with cache_seqlens = prefix + new,
+ * cu_seqlens_q over the new tokens, causal=True). Request b owns q rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) = M_b rows; its L_b = kv_lens[b] keys
+ * are read through page_table row b (key t at k_cache[page_table[b, t / P], t % P]).
+ * New row j sits at position L_b - M_b + j and, when causal, sees keys
+ * [0, L_b - M_b + j] (bottom-right alignment, [NSA] _cal_indexer_k_start_end);
+ * otherwise all L_b keys. q head h reads kv head h / (Hq / Hkv).
+ *
+ * q        [total_q, num_q_heads, head_dim]         dtype
+ * k_cache, v_cache [num_pages, page_size, num_kv_heads, head_dim] dtype
+ * page_table [batch, pt_stride] int32 page ids; cu_seqlens_q [batch + 1];
+ * kv_lens [batch] int32 (requires M_b <= L_b <= pt_stride * page_size)
+ * out      [total_q, num_q_heads, head_dim] dtype (out); lse [total_q, num_q_heads]
+ *          fp32 (out) or NULL.
+ * Supported: dtype PKV_BF16, head_dim 64 or 128, Hq % Hkv == 0,
+ * Hq / Hkv <= 16, causal 0 or 1. max_seqlen_q >= every M_b (a launch bound).
+ */
+pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void* k_cache,
+                                       const void* v_cache, int64_t num_pages,
+                                       const int32_t* page_table, int32_t pt_stride,
+                                       const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                       int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t page_size, float softmax_scale,
+                                       int32_t causal, void* out, float* lse, void* stream);
+
+/*
+ * paged_attn_decode_splitkv -- one query token per request, key axis split.
+ * [FA] forward_decode (flash_attn_with_kvcache, num_splits); [DCA]
+ * _dual_chunk_flash_attn_decoding (partial decodes over disjoint key ranges
+ * returning LSE, empty ranges forced to (0, -inf)).
+ * Split s of request b covers keys [s * kv_chunk, min((s + 1) * kv_chunk, L_b));
+ * it yields the attention output normalised over that range alone, O_s, and
+ * LSE_s; an empty range yields (0, -inf). kv_chunk == 0 means one split.
+ *
+ * q        [batch, num_q_heads, head_dim] dtype
+ * k_cache, v_cache [num_pages, page_size, num_kv_heads, head_dim] dtype
+ * page_table [batch, pt_stride] int32; kv_lens [batch] int32
+ *          (requires L_b <= pt_stride * page_size and L_b <= num_splits * kv_chunk)
+ * num_splits == 1: writes out [batch, num_q_heads, head_dim] (dtype) and, if
+ *          non-NULL, lse [batch, num_q_heads]; o_partial/lse_partial unused.
+ * num_splits > 1: writes o_partial [num_splits, batch, num_q_heads, head_dim]
+ *          fp32 and lse_partial [num_splits, batch, num_q_heads] fp32 (combine
+ *          them with merge_state); out/lse unused.
+ * Supported: dtype PKV_F32 or PKV_BF16, head_dim 64 or 128, Hq % Hkv == 0,
+ * Hq / Hkv <= 16. kv_chunk must be a multiple of page_size ([DCA]
+ * _dual_chunk_flash_attn_prefill_func rejects chunks not divisible by the
+ * block size) and of 32.
+ */
+pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void* k_cache,
+                                       const void* v_cache, int64_t num_pages,
+                                       const int32_t* page_table, int32_t pt_stride,
+                                       const int32_t* kv_lens, int32_t batch,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t page_size, float softmax_scale,
+                                       int32_t kv_chunk, int32_t num_splits, float* o_partial,
+                                       float* lse_partial, void* out, float* lse, void* stream);
+
+/*
+ * merge_state -- combine partial attention states over disjoint key sets.
+ * [DCA] _merge_attn_outputs and the merge closing _dual_chunk_flash_attn_decoding;
+ * [FA] forward_extend / forward_decode call merge_state_v2(o_a, lse_a, o_b, lse_b)
+ * (this is its S-way form):
+ *   m = max_s lse[s], w_s = exp(lse[s] - m),
+ *   out = sum_s w_s o[s] / sum_s w_s, lse_out = m + ln(sum_s w_s);
+ *   m == -inf gives (0, -inf).
+ * o_parts [num_parts, n_tokens, num_heads, head_dim_v] fp32;
+ * lse_parts [num_parts, n_tokens, num_heads] fp32;
+ * out [n_tokens, num_heads, head_dim_v] of out_dtype (out);
+ * lse_out [n_tokens, num_heads] fp32 (out) or NULL.
+ * Errors: PKV_EINVAL for NULL, num_parts < 1, negative sizes.
+ */
+pkv_status_t merge_state(const float* o_parts, const float* lse_parts, int32_t num_parts,
+                         int32_t n_tokens, int32_t num_heads, int32_t head_dim_v, void* out,
+                         int32_t out_dtype, float* lse_out, void* stream);
+
+/*
+ * sparse_topk_decode -- top-k index-gathered MLA decode over one latent KV head.
+ * [NSA] forward_decode: logical top-k indices map to cache slots through the
+ * request's token table (transform_index_page_table_decode, page size 1);
+ * entries equal to -1 are padding and are skipped (_pad_topk_indices,
+ * _forward_aiter). [NSA] _forward_fa3: the cache row is
+ * [c_kv (head_dim_v) | k_rope (head_dim_qk - head_dim_v)]; the score is the dot
+ * product of q = [q_nope | q_rope] with the whole row; the value is c_kv.
+ *   slot_j = req_to_token[req_pool_indices[b], topk_idx[b, j]] (topk_idx != -1)
+ *   s_j = softmax_scale * <q[b, h], kv_cache[slot_j]>
+ *   out[b, h] = sum_j softmax(s)_j * kv_cache[slot_j, :head_dim_v]
+ *
+ * q        [batch, num_q_heads, head_dim_qk] bf16
+ * kv_cache [num_slots, head_dim_qk] bf16
+ * req_to_token [req_to_token_rows, req_to_token_stride] int32
+ * topk_idx [batch, topk] int32 logical indices in [0, stride) or -1
+ * workspace: device scratch of at least sparse_topk_decode_workspace_size(...)
+ *          bytes (may be NULL when that size is 0); contents on entry ignored.
+ * out      [batch, num_q_heads, head_dim_v] bf16 (out); lse [batch, num_q_heads]
+ *          fp32 (out) or NULL.
+ * Supported: head_dim_qk 576, head_dim_v 512, num_q_heads a multiple of 16.
+ */
+size_t sparse_topk_decode_workspace_size(int32_t batch, int32_t topk, int32_t num_q_heads,
+                                         int32_t head_dim_v);
+
+pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num_slots,
+                                const int32_t* req_to_token, int64_t req_to_token_rows,
+                                int64_t req_to_token_stride, const int32_t* req_pool_indices,
+                                const int32_t* topk_idx, int32_t topk, int32_t batch,
+                                int32_t num_q_heads, int32_t head_dim_qk, int32_t head_dim_v,
+                                float softmax_scale, void* workspace, size_t workspace_bytes,
+                                void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

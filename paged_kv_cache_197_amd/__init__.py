@@ -1,0 +1,290 @@
+"""Python binding of libpkv.so: paged, variable-length attention for MI355X.
+
+Argument marshalling only: each function checks tensor dtypes, shapes and
+devices, allocates missing output tensors with torch, and calls the C entry
+point of the same name on torch's current HIP stream. Every step of the
+computation runs in the HIP kernels of libpkv.so; there is no fallback. If the
+library has not been built, every call raises ``PkvLibraryMissing``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PkvError", "PkvLibraryMissing", "load_library", "library_path", "declared_symbols",
+    "build_page_table", "paged_attn_varlen_prefill", "paged_attn_decode_splitkv",
+    "merge_state", "sparse_topk_decode", "sparse_topk_decode_workspace_size",
+    "PKV_F32", "PKV_BF16",
+]
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+PKV_F32 = 0
+PKV_BF16 = 1
+
+_STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_ELAUNCH"}
+
+
+class PkvError(RuntimeError):
+    """A non-OK status from libpkv.so."""
+
+    def __init__(self, func, status, detail):
+        self.status = status
+        super().__init__(f"{func}: {_STATUS.get(status, status)}: {detail}")
+
+
+class PkvLibraryMissing(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return os.environ.get("PKV_LIBRARY", os.path.join(PKG_DIR, "libpkv.so"))
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "build_page_table": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                        _P, _P, _P, _P]),
+    "paged_attn_varlen_prefill": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _P,
+                                                 _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F,
+                                                 _I32, _P, _P, _P]),
+    "paged_attn_decode_splitkv": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _I32,
+                                                 _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _P,
+                                                 _P, _P, _P]),
+    "merge_state": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P, _P]),
+    "sparse_topk_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+    "sparse_topk_decode": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _I64, _P, _P, _I32, _I32, _I32,
+                                          _I32, _I32, _F, _P, _SZ, _P, _P, _P]),
+}
+
+
+def load_library():
+    """Load libpkv.so (once). Raises PkvLibraryMissing if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise PkvLibraryMissing(
+            f"{path} not found: build it with `python -m paged_kv_cache_197_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def declared_symbols(header: str = HEADER):
+    """Function names declared in include/pkv.h."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([A-Za-z_]\w*)\s*\(", text)) - {"if", "defined"})
+
+
+def _check(func, status):
+    if status != 0:
+        detail = load_library().pkv_last_error().decode(errors="replace")
+        raise PkvError(func, status, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype=None, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return PKV_BF16
+    if dt == torch.float32:
+        return PKV_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _i32(t, name, device):
+    """Index tensors are passed as int32 (int64 inputs are narrowed here)."""
+    if t.dtype == torch.int64:
+        t = t.to(torch.int32)
+    return _need(t.contiguous(), name, torch.int32, device)
+
+
+def build_page_table(req_to_token, req_pool_indices, seq_lens, page_size, width, *,
+                     prefill_lens=None, window=0, page_table=None, kv_lens=None,
+                     cu_seqlens_k=None, with_cu_seqlens=True):
+    """Page table, kv_lens and cu_seqlens_k (see include/pkv.h). Returns the three
+    tensors (cu_seqlens_k is None when ``with_cu_seqlens`` is False)."""
+    lib = load_library()
+    dev = req_to_token.device
+    r2t = _i32(req_to_token, "req_to_token", dev)
+    rpi = _i32(req_pool_indices, "req_pool_indices", dev)
+    sl = _i32(seq_lens, "seq_lens", dev)
+    pf = None if prefill_lens is None else _i32(prefill_lens, "prefill_lens", dev)
+    batch = rpi.numel()
+    if page_table is None:
+        page_table = torch.empty((batch, width), dtype=torch.int32, device=dev)
+    if kv_lens is None:
+        kv_lens = torch.empty((batch,), dtype=torch.int32, device=dev)
+    if cu_seqlens_k is None and with_cu_seqlens:
+        cu_seqlens_k = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
+    _need(page_table, "page_table", torch.int32, dev)
+    _need(kv_lens, "kv_lens", torch.int32, dev)
+    st = lib.build_page_table(_ptr(r2t), r2t.shape[0], r2t.shape[1], _ptr(rpi), _ptr(sl), _ptr(pf),
+                              int(window), batch, int(page_size), int(width), _ptr(page_table),
+                              _ptr(kv_lens), _ptr(cu_seqlens_k), _stream(dev))
+    _check("build_page_table", st)
+    return page_table, kv_lens, cu_seqlens_k
+
+
+def paged_attn_decode_splitkv(q, k_cache, v_cache, page_table, kv_lens, softmax_scale, *,
+                              kv_chunk=0, num_splits=1, out=None, lse=None, o_partial=None,
+                              lse_partial=None):
+    """Split-KV paged decode. Returns (out, lse) for one split, else
+    (o_partial [S,B,Hq,D] fp32, lse_partial [S,B,Hq] fp32)."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", None, dev, 3)
+    _need(k_cache, "k_cache", q.dtype, dev, 4)
+    _need(v_cache, "v_cache", q.dtype, dev, 4)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    pt = _i32(page_table, "page_table", dev)
+    kl = _i32(kv_lens, "kv_lens", dev)
+    batch, hq, d = q.shape
+    num_pages, page_size, hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head_dim of q and cache differ")
+    if num_splits == 1:
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    else:
+        if o_partial is None:
+            o_partial = torch.empty((num_splits, batch, hq, d), dtype=torch.float32, device=dev)
+        if lse_partial is None:
+            lse_partial = torch.empty((num_splits, batch, hq), dtype=torch.float32, device=dev)
+    st = lib.paged_attn_decode_splitkv(
+        _ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(pt),
+        pt.shape[1], _ptr(kl), batch, hq, hkv, d, page_size, float(softmax_scale), int(kv_chunk),
+        int(num_splits), _ptr(o_partial), _ptr(lse_partial),
+        _ptr(out) if num_splits == 1 else None, _ptr(lse) if num_splits == 1 else None,
+        _stream(dev))
+    _check("paged_attn_decode_splitkv", st)
+    return (out, lse) if num_splits == 1 else (o_partial, lse_partial)
+
+
+def merge_state(o_parts, lse_parts, *, out_dtype=torch.bfloat16, out=None, lse_out=None):
+    """S-way merge of partial (O, LSE). o_parts [S, N, H, Dv] fp32, lse_parts [S, N, H]."""
+    lib = load_library()
+    dev = o_parts.device
+    _need(o_parts, "o_parts", torch.float32, dev, 4)
+    _need(lse_parts, "lse_parts", torch.float32, dev, 3)
+    S, N, H, Dv = o_parts.shape
+    if tuple(lse_parts.shape) != (S, N, H):
+        raise ValueError("lse_parts shape does not match o_parts")
+    if out is None:
+        out = torch.empty((N, H, Dv), dtype=out_dtype, device=dev)
+    if lse_out is None:
+        lse_out = torch.empty((N, H), dtype=torch.float32, device=dev)
+    st = lib.merge_state(_ptr(o_parts), _ptr(lse_parts), S, N, H, Dv, _ptr(out),
+                         _dtype_code(out.dtype), _ptr(lse_out), _stream(dev))
+    _check("merge_state", st)
+    return out, lse_out
+
+
+def paged_attn_varlen_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens,
+                              max_seqlen_q, softmax_scale, *, causal=True, out=None, lse=None,
+                              return_lse=True):
+    """Causal varlen extend over a paged cache. Returns (out, lse or None)."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(k_cache, "k_cache", q.dtype, dev, 4)
+    _need(v_cache, "v_cache", q.dtype, dev, 4)
+    pt = _i32(page_table, "page_table", dev)
+    cu = _i32(cu_seqlens_q, "cu_seqlens_q", dev)
+    kl = _i32(kv_lens, "kv_lens", dev)
+    total_q, hq, d = q.shape
+    num_pages, page_size, hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev)
+    st = lib.paged_attn_varlen_prefill(
+        _ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(pt),
+        pt.shape[1], _ptr(cu), _ptr(kl), kl.numel(), total_q, int(max_seqlen_q), hq, hkv, d,
+        page_size, float(softmax_scale), int(bool(causal)), _ptr(out), _ptr(lse), _stream(dev))
+    _check("paged_attn_varlen_prefill", st)
+    return out, lse
+
+
+def sparse_topk_decode_workspace_size(batch, topk, num_q_heads, head_dim_v=512):
+    return int(load_library().sparse_topk_decode_workspace_size(batch, topk, num_q_heads,
+                                                                head_dim_v))
+
+
+def sparse_topk_decode(q, kv_cache, req_to_token, req_pool_indices, topk_idx, softmax_scale, *,
+                       head_dim_v=512, workspace=None, out=None, lse=None):
+    """Top-k sparse MLA decode. q [B, Hq, Dqk] bf16, kv_cache [slots, Dqk] bf16.
+    Returns (out [B, Hq, Dv] bf16, lse [B, Hq] fp32)."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    kv = kv_cache.reshape(kv_cache.shape[0], -1)
+    _need(kv, "kv_cache", torch.bfloat16, dev, 2)
+    r2t = _i32(req_to_token, "req_to_token", dev)
+    rpi = _i32(req_pool_indices, "req_pool_indices", dev)
+    idx = _i32(topk_idx, "topk_idx", dev)
+    batch, hq, dqk = q.shape
+    topk = idx.shape[1] if idx.dim() == 2 else 0
+    if out is None:
+        out = torch.empty((batch, hq, head_dim_v), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    need = sparse_topk_decode_workspace_size(batch, topk, hq, head_dim_v)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.sparse_topk_decode(_ptr(q), _ptr(kv), kv.shape[0], _ptr(r2t), r2t.shape[0],
+                                r2t.shape[1], _ptr(rpi), _ptr(idx), topk, batch, hq, dqk,
+                                head_dim_v, float(softmax_scale), _ptr(workspace), ws_bytes,
+                                _ptr(out), _ptr(lse), _stream(dev))
+    _check("sparse_topk_decode", st)
+    return out, lse

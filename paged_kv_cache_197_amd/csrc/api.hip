@@ -1,0 +1,292 @@
+// C ABI of libpkv.so (declared in include/pkv.h): host-side argument checks,
+// then one launcher call per entry point. No allocation, no synchronisation.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "args.hpp"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace pkv_host {
+
+static thread_local char g_last_error[512] = "";
+
+pkv_status_t fail(pkv_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static pkv_status_t ok() {
+  g_last_error[0] = '\0';
+  return PKV_OK;
+}
+
+static pkv_status_t from_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PKV_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+static float scale_log2(float softmax_scale) {
+  return static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+}
+
+}  // namespace pkv_host
+
+using pkv_host::fail;
+
+#define PKV_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_EINVAL: return "PKV_EINVAL";
+    case PKV_EUNSUPPORTED: return "PKV_EUNSUPPORTED";
+    case PKV_ELAUNCH: return "PKV_ELAUNCH";
+    default: return "PKV_UNKNOWN";
+  }
+}
+
+const char* pkv_last_error(void) { return pkv_host::g_last_error; }
+
+pkv_status_t build_page_table(const int32_t* req_to_token, int64_t req_to_token_rows,
+                              int64_t req_to_token_stride, const int32_t* req_pool_indices,
+                              const int32_t* seq_lens, const int32_t* prefill_lens,
+                              int32_t window, int32_t batch, int32_t page_size, int32_t width,
+                              int32_t* page_table, int32_t* kv_lens, int32_t* cu_seqlens_k,
+                              void* stream) {
+  PKV_REQUIRE(batch >= 0, PKV_EINVAL, "build_page_table: batch %d < 0", batch);
+  PKV_REQUIRE(width >= 0, PKV_EINVAL, "build_page_table: width %d < 0", width);
+  PKV_REQUIRE(page_size >= 1, PKV_EINVAL, "build_page_table: page_size %d < 1", page_size);
+  PKV_REQUIRE(width <= 65535 * 256, PKV_EUNSUPPORTED, "build_page_table: width %d too large",
+              width);
+  if (prefill_lens != nullptr) {
+    PKV_REQUIRE(page_size == 1, PKV_EINVAL,
+                "build_page_table: the sliding-window table is token-level (page_size 1), got %d",
+                page_size);
+    PKV_REQUIRE(window >= 0, PKV_EINVAL, "build_page_table: window %d < 0", window);
+  }
+  if (batch > 0) {
+    PKV_REQUIRE(req_to_token && req_pool_indices && seq_lens && page_table && kv_lens,
+                PKV_EINVAL, "build_page_table: NULL required pointer");
+    PKV_REQUIRE(req_to_token_rows >= 1 && req_to_token_stride >= 1, PKV_EINVAL,
+                "build_page_table: req_to_token is %lld x %lld", (long long)req_to_token_rows,
+                (long long)req_to_token_stride);
+  }
+  pkv::PageTableArgs a;
+  a.r2t = req_to_token;
+  a.rows = req_to_token_rows;
+  a.stride = req_to_token_stride;
+  a.rpi = req_pool_indices;
+  a.seq_lens = seq_lens;
+  a.prefill_lens = prefill_lens;
+  a.window = window;
+  a.batch = batch;
+  a.page_size = page_size;
+  a.width = width;
+  a.page_table = page_table;
+  a.kv_lens = kv_lens;
+  a.cu_seqlens_k = cu_seqlens_k;
+  if (batch == 0 && cu_seqlens_k == nullptr) return pkv_host::ok();
+  return pkv_host::from_hip(pkv_launch::page_table(a, static_cast<hipStream_t>(stream)),
+                            "build_page_table launch");
+}
+
+pkv_status_t merge_state(const float* o_parts, const float* lse_parts, int32_t num_parts,
+                         int32_t n_tokens, int32_t num_heads, int32_t head_dim_v, void* out,
+                         int32_t out_dtype, float* lse_out, void* stream) {
+  PKV_REQUIRE(num_parts >= 1, PKV_EINVAL, "merge_state: num_parts %d < 1", num_parts);
+  PKV_REQUIRE(n_tokens >= 0 && num_heads >= 0 && head_dim_v >= 1, PKV_EINVAL,
+              "merge_state: bad sizes n_tokens %d num_heads %d head_dim_v %d", n_tokens,
+              num_heads, head_dim_v);
+  PKV_REQUIRE(out_dtype == PKV_F32 || out_dtype == PKV_BF16, PKV_EUNSUPPORTED,
+              "merge_state: out_dtype %d", out_dtype);
+  const int64_t rows = static_cast<int64_t>(n_tokens) * num_heads;
+  if (rows == 0) return pkv_host::ok();
+  PKV_REQUIRE(o_parts && lse_parts && out, PKV_EINVAL, "merge_state: NULL required pointer");
+  return pkv_host::from_hip(
+      pkv_launch::merge_state(o_parts, lse_parts, num_parts, rows, head_dim_v, out, out_dtype,
+                              lse_out, static_cast<hipStream_t>(stream)),
+      "merge_state launch");
+}
+
+pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void* k_cache,
+                                       const void* v_cache, int64_t num_pages,
+                                       const int32_t* page_table, int32_t pt_stride,
+                                       const int32_t* kv_lens, int32_t batch,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t page_size, float softmax_scale,
+                                       int32_t kv_chunk, int32_t num_splits, float* o_partial,
+                                       float* lse_partial, void* out, float* lse, void* stream) {
+  PKV_REQUIRE(dtype == PKV_F32 || dtype == PKV_BF16, PKV_EUNSUPPORTED,
+              "decode: dtype %d not supported", dtype);
+  PKV_REQUIRE(head_dim == 64 || head_dim == 128, PKV_EUNSUPPORTED,
+              "decode: head_dim %d not supported (64, 128)", head_dim);
+  PKV_REQUIRE(batch >= 0 && num_q_heads >= 1 && num_kv_heads >= 1, PKV_EINVAL,
+              "decode: bad sizes batch %d Hq %d Hkv %d", batch, num_q_heads, num_kv_heads);
+  PKV_REQUIRE(num_q_heads % num_kv_heads == 0, PKV_EINVAL,
+              "decode: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+              num_kv_heads);
+  PKV_REQUIRE(num_q_heads / num_kv_heads <= 16, PKV_EUNSUPPORTED,
+              "decode: GQA group %d > 16", num_q_heads / num_kv_heads);
+  PKV_REQUIRE(page_size >= 1 && pt_stride >= 1 && num_pages >= 1, PKV_EINVAL,
+              "decode: page_size %d pt_stride %d num_pages %lld", page_size, pt_stride,
+              (long long)num_pages);
+  PKV_REQUIRE(kv_chunk >= 0, PKV_EINVAL, "decode: kv_chunk %d < 0", kv_chunk);
+  PKV_REQUIRE(kv_chunk % page_size == 0, PKV_EINVAL,
+              "decode: kv_chunk %d is not a multiple of page_size %d", kv_chunk, page_size);
+  PKV_REQUIRE(kv_chunk % 32 == 0, PKV_EINVAL, "decode: kv_chunk %d is not a multiple of 32",
+              kv_chunk);
+  PKV_REQUIRE(num_splits >= 1, PKV_EINVAL, "decode: num_splits %d < 1", num_splits);
+  PKV_REQUIRE(kv_chunk > 0 || num_splits == 1, PKV_EINVAL,
+              "decode: kv_chunk 0 (one split) needs num_splits 1, got %d", num_splits);
+  if (batch == 0) return pkv_host::ok();
+  PKV_REQUIRE(q && k_cache && v_cache && page_table && kv_lens, PKV_EINVAL,
+              "decode: NULL required pointer");
+  if (num_splits == 1) {
+    PKV_REQUIRE(out != nullptr, PKV_EINVAL, "decode: num_splits 1 needs out");
+  } else {
+    PKV_REQUIRE(o_partial && lse_partial, PKV_EINVAL,
+                "decode: num_splits %d needs o_partial and lse_partial", num_splits);
+  }
+  const int64_t grid = static_cast<int64_t>(num_kv_heads) * batch * num_splits;
+  PKV_REQUIRE(grid <= 0x7fffffff, PKV_EUNSUPPORTED, "decode: grid too large");
+  const int64_t cap = static_cast<int64_t>(pt_stride) * page_size;
+  pkv::DecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.pt = page_table;
+  a.pt_stride = pt_stride;
+  a.kv_lens = kv_lens;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.scale_log2 = pkv_host::scale_log2(softmax_scale);
+  // one split: a chunk that covers every representable key position
+  a.chunk = kv_chunk > 0 ? kv_chunk
+                         : static_cast<int32_t>(((cap < 0x40000000LL ? cap : 0x40000000LL) + 31) /
+                                                32 * 32);
+  a.num_splits = num_splits;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  a.out = out;
+  a.lse = lse;
+  return pkv_host::from_hip(
+      pkv_launch::decode_splitkv(a, dtype, head_dim, static_cast<hipStream_t>(stream)),
+      "decode launch");
+}
+
+pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void* k_cache,
+                                       const void* v_cache, int64_t num_pages,
+                                       const int32_t* page_table, int32_t pt_stride,
+                                       const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                       int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t page_size, float softmax_scale,
+                                       int32_t causal, void* out, float* lse, void* stream) {
+  PKV_REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "prefill: dtype %d not supported (bf16)",
+              dtype);
+  PKV_REQUIRE(head_dim == 64 || head_dim == 128, PKV_EUNSUPPORTED,
+              "prefill: head_dim %d not supported (64, 128)", head_dim);
+  PKV_REQUIRE(batch >= 0 && total_q >= 0 && max_seqlen_q >= 0 && num_q_heads >= 1 &&
+                  num_kv_heads >= 1,
+              PKV_EINVAL, "prefill: bad sizes");
+  PKV_REQUIRE(num_q_heads % num_kv_heads == 0, PKV_EINVAL,
+              "prefill: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+              num_kv_heads);
+  PKV_REQUIRE(num_q_heads / num_kv_heads <= 16, PKV_EUNSUPPORTED, "prefill: GQA group %d > 16",
+              num_q_heads / num_kv_heads);
+  PKV_REQUIRE(page_size >= 1 && pt_stride >= 1 && num_pages >= 1, PKV_EINVAL,
+              "prefill: page_size %d pt_stride %d num_pages %lld", page_size, pt_stride,
+              (long long)num_pages);
+  PKV_REQUIRE(causal == 0 || causal == 1, PKV_EINVAL, "prefill: causal %d", causal);
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return pkv_host::ok();
+  PKV_REQUIRE(q && k_cache && v_cache && page_table && cu_seqlens_q && kv_lens && out,
+              PKV_EINVAL, "prefill: NULL required pointer");
+  pkv::PrefillArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.pt = page_table;
+  a.pt_stride = pt_stride;
+  a.cu_q = cu_seqlens_q;
+  a.kv_lens = kv_lens;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.max_seqlen_q = max_seqlen_q;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.scale_log2 = pkv_host::scale_log2(softmax_scale);
+  a.causal = causal;
+  a.out = out;
+  a.lse = lse;
+  return pkv_host::from_hip(pkv_launch::prefill(a, head_dim, static_cast<hipStream_t>(stream)),
+                            "prefill launch");
+}
+
+size_t sparse_topk_decode_workspace_size(int32_t batch, int32_t topk, int32_t num_q_heads,
+                                         int32_t head_dim_v) {
+  if (batch <= 0 || topk <= 0 || num_q_heads <= 0 || head_dim_v <= 0) return 0;
+  return pkv_launch::sparse_workspace_bytes(batch, topk, num_q_heads, head_dim_v);
+}
+
+pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num_slots,
+                                const int32_t* req_to_token, int64_t req_to_token_rows,
+                                int64_t req_to_token_stride, const int32_t* req_pool_indices,
+                                const int32_t* topk_idx, int32_t topk, int32_t batch,
+                                int32_t num_q_heads, int32_t head_dim_qk, int32_t head_dim_v,
+                                float softmax_scale, void* workspace, size_t workspace_bytes,
+                                void* out, float* lse, void* stream) {
+  PKV_REQUIRE(head_dim_qk == 576 && head_dim_v == 512, PKV_EUNSUPPORTED,
+              "sparse_topk_decode: head dims %d/%d not supported (576/512)", head_dim_qk,
+              head_dim_v);
+  PKV_REQUIRE(batch >= 0 && topk >= 0 && num_q_heads >= 1, PKV_EINVAL,
+              "sparse_topk_decode: bad sizes batch %d topk %d heads %d", batch, topk, num_q_heads);
+  PKV_REQUIRE(num_q_heads % 16 == 0, PKV_EUNSUPPORTED,
+              "sparse_topk_decode: num_q_heads %d not a multiple of 16", num_q_heads);
+  if (batch == 0) return pkv_host::ok();
+  PKV_REQUIRE(q && kv_cache && req_to_token && req_pool_indices && out, PKV_EINVAL,
+              "sparse_topk_decode: NULL required pointer");
+  PKV_REQUIRE(topk == 0 || topk_idx != nullptr, PKV_EINVAL, "sparse_topk_decode: NULL topk_idx");
+  PKV_REQUIRE(num_slots >= 1 && req_to_token_rows >= 1 && req_to_token_stride >= 1, PKV_EINVAL,
+              "sparse_topk_decode: empty cache or token table");
+  const size_t need = sparse_topk_decode_workspace_size(batch, topk, num_q_heads, head_dim_v);
+  PKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr), PKV_EINVAL,
+              "sparse_topk_decode: workspace of %zu bytes, need %zu", workspace_bytes, need);
+  pkv::SparseArgs a;
+  a.q = q;
+  a.kv = kv_cache;
+  a.num_slots = num_slots;
+  a.r2t = req_to_token;
+  a.r2t_rows = req_to_token_rows;
+  a.r2t_stride = req_to_token_stride;
+  a.rpi = req_pool_indices;
+  a.topk_idx = topk_idx;
+  a.topk = topk;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.dqk = head_dim_qk;
+  a.dv = head_dim_v;
+  a.scale_log2 = pkv_host::scale_log2(softmax_scale);
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  a.out = out;
+  a.lse = lse;
+  return pkv_host::from_hip(pkv_launch::sparse_topk(a, static_cast<hipStream_t>(stream)),
+                            "sparse_topk_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Kernel argument blocks shared by the launchers and the C ABI (plain data).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct PageTableArgs {
+  const int32_t* r2t;
+  int64_t rows, stride;
+  const int32_t* rpi;
+  const int32_t* seq_lens;
+  const int32_t* prefill_lens;  // nullptr: strided mode
+  int32_t window, batch, page_size, width;
+  int32_t* page_table;
+  int32_t* kv_lens;
+  int32_t* cu_seqlens_k;        // may be nullptr
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* pt;
+  int32_t pt_stride;
+  const int32_t* kv_lens;
+  int32_t batch, hq, hkv, page_size;
+  int64_t num_pages;
+  float scale_log2;   // softmax_scale * log2(e)
+  int32_t chunk;      // tokens per split (> 0)
+  int32_t num_splits;
+  float* o_part;      // [S, B, Hq, D] (num_splits > 1)
+  float* lse_part;    // [S, B, Hq]
+  void* out;          // [B, Hq, D] dtype (num_splits == 1)
+  float* lse;         // [B, Hq] or nullptr
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* pt;
+  int32_t pt_stride;
+  const int32_t* cu_q;
+  const int32_t* kv_lens;
+  int32_t batch, total_q, max_seqlen_q, hq, hkv, page_size;
+  int64_t num_pages;
+  float scale_log2;
+  int32_t causal;
+  void* out;
+  float* lse;
+};
+
+struct SparseArgs {
+  const void* q;
+  const void* kv;
+  int64_t num_slots;
+  const int32_t* r2t;
+  int64_t r2t_rows, r2t_stride;
+  const int32_t* rpi;
+  const int32_t* topk_idx;
+  int32_t topk, batch, hq, dqk, dv;
+  float scale_log2;
+  void* workspace;
+  size_t workspace_bytes;
+  void* out;
+  float* lse;
+};
+
+}  // namespace pkv

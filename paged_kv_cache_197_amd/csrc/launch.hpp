@@ -1,0 +1,23 @@
+// Internal launchers (one per kernel family), called by the C ABI in api.cpp
+// after argument validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+struct PageTableArgs;
+struct DecodeArgs;
+struct PrefillArgs;
+struct SparseArgs;
+}  // namespace pkv
+
+namespace pkv_launch {
+hipError_t page_table(const pkv::PageTableArgs& a, hipStream_t stream);
+hipError_t merge_state(const float* o_parts, const float* lse_parts, int num_parts, int64_t rows,
+                       int dv, void* out, int out_dtype, float* lse_out, hipStream_t stream);
+hipError_t decode_splitkv(const pkv::DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+hipError_t prefill(const pkv::PrefillArgs& a, int head_dim, hipStream_t stream);
+size_t sparse_workspace_bytes(int batch, int topk, int num_q_heads, int head_dim_v);
+hipError_t sparse_topk(const pkv::SparseArgs& a, hipStream_t stream);
+}  // namespace pkv_launch

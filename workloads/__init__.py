@@ -191,7 +191,7 @@ def _draw_kv(gv, dev, lens, num_kv_heads, head_dim, dtype):
 
 def make_decode_case(seed, *, seq_lens, num_q_heads, num_kv_heads, head_dim, page_size,
                      num_pages, dtype=torch.bfloat16, kv_chunk=0, ctx=None,
-                     value_device="cpu", name="") -> DecodeCase:
+                     value_device="cpu", with_values=True, name="") -> DecodeCase:
     """Paged GQA decode: one query token per request over ``seq_lens`` keys.
 
     ``seq_lens`` is either an explicit list or a ``(batch, lo, hi)`` tuple for
@@ -209,13 +209,17 @@ def make_decode_case(seed, *, seq_lens, num_q_heads, num_kv_heads, head_dim, pag
         ctx = max(max_len, 1)
     ctx = -(-ctx // page_size) * page_size
     r2t, rpi, owned, _poison, pool_pages = _place_pages(g, batch, lens, page_size, num_pages, ctx)
-    gv, dev = _value_generator(seed, value_device)
-    q = _normal(gv, dev, (batch, num_q_heads, head_dim), dtype)
-    k_parts, v_parts = _draw_kv(gv, dev, lens, num_kv_heads, head_dim, dtype)
-    k_cache = _fill_cache(k_parts, owned, lens, page_size, pool_pages, num_kv_heads,
-                          head_dim, dtype, dev)
-    v_cache = _fill_cache(v_parts, owned, lens, page_size, pool_pages, num_kv_heads,
-                          head_dim, dtype, dev)
+    q = k_cache = v_cache = None
+    if with_values:
+        gv, dev = _value_generator(seed, value_device)
+        q = _normal(gv, dev, (batch, num_q_heads, head_dim), dtype)
+        k_parts, v_parts = _draw_kv(gv, dev, lens, num_kv_heads, head_dim, dtype)
+        k_cache = _fill_cache(k_parts, owned, lens, page_size, pool_pages, num_kv_heads,
+                              head_dim, dtype, dev)
+        del k_parts
+        v_cache = _fill_cache(v_parts, owned, lens, page_size, pool_pages, num_kv_heads,
+                              head_dim, dtype, dev)
+        del v_parts
     if kv_chunk:
         num_splits = max(1, -(-max_len // kv_chunk))
     else:
@@ -263,7 +267,7 @@ def make_prefill_case(seed, *, prefix_lens, extend_lens, num_q_heads, num_kv_hea
 
 def make_swa_case(seed, *, batch, prefill_range, decode_range, window, num_q_heads,
                   num_kv_heads, head_dim, pool_slots, dtype=torch.bfloat16, kv_chunk=0,
-                  value_device="cpu", name="") -> SwaCase:
+                  value_device="cpu", with_values=True, name="") -> SwaCase:
     """Decode over a prefill-aware sliding-window table (token-level, page size 1).
 
     ``prefill_len ~ U[prefill_range]`` and ``seq_len = prefill_len + U[decode_range]``.
@@ -277,11 +281,17 @@ def make_swa_case(seed, *, batch, prefill_range, decode_range, window, num_q_hea
     r2t, rpi, owned, _poison, pool_pages = _place_pages(g, batch, lens, 1, pool_slots, ctx)
     prefill_pool = _randint_incl(g, 0, 7, 2 * batch)   # rows no request uses: junk
     prefill_pool[rpi] = pf
-    gv, dev = _value_generator(seed, value_device)
-    q = _normal(gv, dev, (batch, num_q_heads, head_dim), dtype)
-    k_parts, v_parts = _draw_kv(gv, dev, lens, num_kv_heads, head_dim, dtype)
-    k_cache = _fill_cache(k_parts, owned, lens, 1, pool_pages, num_kv_heads, head_dim, dtype, dev)
-    v_cache = _fill_cache(v_parts, owned, lens, 1, pool_pages, num_kv_heads, head_dim, dtype, dev)
+    q = k_cache = v_cache = None
+    if with_values:
+        gv, dev = _value_generator(seed, value_device)
+        q = _normal(gv, dev, (batch, num_q_heads, head_dim), dtype)
+        k_parts, v_parts = _draw_kv(gv, dev, lens, num_kv_heads, head_dim, dtype)
+        k_cache = _fill_cache(k_parts, owned, lens, 1, pool_pages, num_kv_heads, head_dim, dtype,
+                              dev)
+        del k_parts
+        v_cache = _fill_cache(v_parts, owned, lens, 1, pool_pages, num_kv_heads, head_dim, dtype,
+                              dev)
+        del v_parts
     width = min(int(pf.max()) + window, int(lens.max()))
     num_splits = max(1, -(-width // kv_chunk)) if kv_chunk else 1
     return SwaCase(q=q, k_cache=k_cache, v_cache=v_cache, req_to_token=r2t.to(torch.int32),
@@ -343,22 +353,23 @@ def config2(value_device="cpu"):
                              num_pages=8192, value_device=value_device, name="config2")
 
 
-def config3(value_device="cpu"):
+def config3(value_device="cpu", with_values=True):
     """Batched split-KV GQA decode, bf16: B 64, L ~ U[1024, 32768], 32 q / 8 kv
     heads, D 128, page 64 over a 40000-page pool, chunks of 4096 tokens."""
     return make_decode_case(3, seq_lens=(64, 1024, 32768), num_q_heads=32, num_kv_heads=8,
                             head_dim=128, page_size=64, num_pages=40000, kv_chunk=4096,
-                            ctx=32768, value_device=value_device, name="config3")
+                            ctx=32768, value_device=value_device, with_values=with_values,
+                            name="config3")
 
 
-def config4(value_device="cpu", kv_chunk=2048):
+def config4(value_device="cpu", kv_chunk=2048, with_values=True):
     """Sliding-window decode over the prefill-aware table, bf16: B 32,
     prefill ~ U[2048, 8192], seq = prefill + U[1, 8192], window 4096,
     64 q / 8 kv heads, D 128, page 1 over 32*16384 slots."""
     return make_swa_case(4, batch=32, prefill_range=(2048, 8192), decode_range=(1, 8192),
                          window=4096, num_q_heads=64, num_kv_heads=8, head_dim=128,
                          pool_slots=32 * 16384, kv_chunk=kv_chunk,
-                         value_device=value_device, name="config4")
+                         value_device=value_device, with_values=with_values, name="config4")
 
 
 def config5(value_device="cpu", num_pad=0):
