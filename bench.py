@@ -1,0 +1,442 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Prints ONE JSON line. The timed step is the batched split-KV GQA decode
+workload (config3: B=64, L ~ U[1024, 32768], 32 q / 8 kv heads, D=128, page 64,
+40000-page pool, 4096-token chunks): build the strided page table, run the
+split-KV decode, merge the partial states. ``value`` is that step's
+algorithmic HBM bytes (K + V rows read, q, the bf16 output, the page table)
+divided by the measured step time. The prefill (config2), sliding-window
+decode (config4) and sparse MLA decode (config5) workloads are timed in the
+same run and reported beside it; the CPU oracle is timed on a bounded sample.
+
+Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dense bf16
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--only", choices=["all", "decode", "prefill", "swa", "sparse", "copy"],
+                   default="all", help="restrict to one workload (for profiler runs)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU work budget for the oracle sample")
+    return p.parse_args(argv)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_197_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Timer:
+    """Wall-clock step timing plus per-launch HIP-event timing of one kernel."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.torch.cuda.current_stream())
+        return e
+
+    def kernel_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(len(self.pairs), 1)
+
+
+def timed_loop(torch, step, steps, warmup):
+    """W untimed steps, then exactly K timed steps between synchronisations.
+
+    step(timer_or_None) enqueues one step; with a timer it records events
+    around the dominant kernel.
+    """
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, timer.kernel_ms()
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work
+# ---------------------------------------------------------------------------
+
+def decode_bytes(seq_lens, batch, hq, hkv, d, page_size, elem=2):
+    """K and V rows of every visible token, q, the output, and the page-table reads."""
+    sum_l = int(seq_lens.sum())
+    n_pages = int(((seq_lens + page_size - 1) // page_size).sum())
+    kv = 2 * sum_l * hkv * d * elem
+    return kv + batch * hq * d * elem * 2 + 4 * n_pages, sum_l
+
+
+def prefill_flops(extend_lens, kv_lens, hq, d):
+    """4 * D * Hq * (visible (q, k) pairs), causal bottom-right."""
+    pairs = 0
+    for m, L in zip(extend_lens, kv_lens):
+        m, L = int(m), int(L)
+        pairs += sum(L - m + j + 1 for j in range(m))
+    return 4 * d * hq * pairs, pairs
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+def run_decode(torch, pkv, workloads, args):
+    dev = torch.device("cuda:0")
+    c = workloads.config3(value_device=dev)
+    r2t, rpi, sl = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev))
+    B, hq, d = c.q.shape
+    _, P, hkv, _ = c.k_cache.shape
+    S = c.num_splits
+    pt = torch.empty((B, c.table_width), dtype=torch.int32, device=dev)
+    kl = torch.empty((B,), dtype=torch.int32, device=dev)
+    op = torch.empty((S, B, hq, d), dtype=torch.float32, device=dev)
+    lp = torch.empty((S, B, hq), dtype=torch.float32, device=dev)
+    out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+
+    def step(timer):
+        pkv.build_page_table(r2t, rpi, sl, P, c.table_width, page_table=pt, kv_lens=kl,
+                             with_cu_seqlens=False)
+        e0 = timer.mark() if timer else None
+        pkv.paged_attn_decode_splitkv(c.q, c.k_cache, c.v_cache, pt, kl, c.scale,
+                                      kv_chunk=c.kv_chunk, num_splits=S, o_partial=op,
+                                      lse_partial=lp)
+        if timer:
+            timer.pairs.append((e0, timer.mark()))
+        pkv.merge_state(op, lp, out=out, lse_out=lse)
+
+    ms, kern_ms = timed_loop(torch, step, args.steps, args.warmup)
+    nbytes, sum_l = decode_bytes(c.seq_lens.long(), B, hq, hkv, d, P)
+    res = dict(ms=ms, kernel_ms=kern_ms, bytes=nbytes, sum_l=sum_l, batch=B, splits=S,
+               case=c)
+    return res
+
+
+def run_swa(torch, pkv, workloads, args):
+    dev = torch.device("cuda:0")
+    c = workloads.config4(value_device=dev)
+    r2t, rpi, sl, pf = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev),
+                        c.prefill_lens.to(dev))
+    B, hq, d = c.q.shape
+    hkv = c.k_cache.shape[2]
+    S = c.num_splits
+    pt = torch.empty((B, c.table_width), dtype=torch.int32, device=dev)
+    kl = torch.empty((B,), dtype=torch.int32, device=dev)
+    op = torch.empty((S, B, hq, d), dtype=torch.float32, device=dev)
+    lp = torch.empty((S, B, hq), dtype=torch.float32, device=dev)
+    out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    build_t = Timer(torch)
+
+    def step(timer):
+        e_b = build_t.mark() if timer else None
+        pkv.build_page_table(r2t, rpi, sl, 1, c.table_width, prefill_lens=pf, window=c.window,
+                             page_table=pt, kv_lens=kl, with_cu_seqlens=False)
+        e0 = timer.mark() if timer else None
+        if timer:
+            build_t.pairs.append((e_b, e0))
+        pkv.paged_attn_decode_splitkv(c.q, c.k_cache, c.v_cache, pt, kl, c.scale,
+                                      kv_chunk=c.kv_chunk, num_splits=S, o_partial=op,
+                                      lse_partial=lp)
+        if timer:
+            timer.pairs.append((e0, timer.mark()))
+        pkv.merge_state(op, lp, out=out, lse_out=lse)
+
+    ms, kern_ms = timed_loop(torch, step, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    kv_lens = kl.cpu().long()
+    nbytes, sum_l = decode_bytes(kv_lens, B, hq, hkv, d, 1)
+    return dict(ms=ms, kernel_ms=kern_ms, build_ms=build_t.kernel_ms(), bytes=nbytes,
+                sum_kv_len=sum_l, splits=S)
+
+
+def run_prefill(torch, pkv, workloads, args):
+    dev = torch.device("cuda:0")
+    c = workloads.config2(value_device=dev)
+    r2t, rpi, sl, cu = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev),
+                        c.cu_seqlens_q.to(dev))
+    B = sl.numel()
+    pt = torch.empty((B, c.table_width), dtype=torch.int32, device=dev)
+    kl = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(c.q)
+    lse = torch.empty(c.q.shape[:2], dtype=torch.float32, device=dev)
+
+    def step(timer):
+        pkv.build_page_table(r2t, rpi, sl, c.page_size, c.table_width, page_table=pt,
+                             kv_lens=kl, with_cu_seqlens=False)
+        e0 = timer.mark() if timer else None
+        pkv.paged_attn_varlen_prefill(c.q, c.k_cache, c.v_cache, pt, cu, kl, c.max_seqlen_q,
+                                      c.scale, causal=True, out=out, lse=lse)
+        if timer:
+            timer.pairs.append((e0, timer.mark()))
+
+    ms, kern_ms = timed_loop(torch, step, max(args.steps, 50), args.warmup)
+    flops, pairs = prefill_flops(c.extend_lens.tolist(), c.seq_lens.tolist(), c.q.shape[1],
+                                 c.q.shape[2])
+    return dict(ms=ms, kernel_ms=kern_ms, flops=flops, pairs=pairs)
+
+
+def run_sparse(torch, pkv, workloads, args):
+    dev = torch.device("cuda:0")
+    c = workloads.config5(value_device=dev)
+    r2t, rpi, idx = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.topk_idx.to(dev))
+    B, hq, dqk = c.q.shape
+    dv = c.head_dim_v
+    K = idx.shape[1]
+    out = torch.empty((B, hq, dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    need = pkv.sparse_topk_decode_workspace_size(B, K, hq, dv)
+    ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    # a buffer larger than the 256 MB last-level cache, rewritten before each
+    # timed step so the 85 MB working set is read from HBM
+    flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+
+    def one(timer):
+        e0 = timer.mark() if timer else None
+        pkv.sparse_topk_decode(c.q, c.kv_cache, r2t, rpi, idx, c.scale, head_dim_v=dv,
+                               workspace=ws, out=out, lse=lse)
+        if timer:
+            timer.pairs.append((e0, timer.mark()))
+
+    warm_ms, warm_kern = timed_loop(torch, one, max(args.steps, 50), args.warmup)
+    # cold: flush between launches (outside the event pair)
+    cold = Timer(torch)
+    for _ in range(args.warmup):
+        one(None)
+    for _ in range(max(args.steps, 20)):
+        flush.fill_(1)
+        one(cold)
+    torch.cuda.synchronize()
+    cold_ms = cold.kernel_ms()
+    n_valid = int((c.topk_idx >= 0).sum())
+    nbytes = (n_valid * dqk * 2 + B * hq * dqk * 2 + B * hq * dv * 2 + B * K * 4 * 2)
+    flops = 2 * n_valid * hq * (dqk + dv)
+    return dict(warm_ms=warm_kern, cold_ms=cold_ms, bytes=nbytes, flops=flops)
+
+
+def run_copy(torch, args):
+    """A plain copy kernel of known size (1 GiB read + 1 GiB written), for
+    calibrating the FETCH_SIZE / WRITE_SIZE counters."""
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    a = torch.ones((n // 4,), dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    return dict(bytes_read=n, bytes_written=n)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle on a bounded sample of the decode workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline_decode(torch, res, budget_s):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    c = res["case"]
+    pt_all, kl_all, _ = oracle.page_table_strided(
+        c.req_to_token.cpu().numpy(), c.req_pool_indices.cpu().numpy(),
+        c.seq_lens.cpu().numpy(), c.page_size, c.table_width)
+    P = c.page_size
+    done_bytes = 0
+    spent = 0.0
+    n_req = 0
+    sum_l = 0
+    B, hq, d = c.q.shape
+    hkv = c.k_cache.shape[2]
+    for b in range(B):
+        L = int(kl_all[b])
+        n = -(-L // P)
+        pages = torch.as_tensor(pt_all[b, :n].astype(np.int64), device=c.k_cache.device)
+        k = c.k_cache[pages].to(torch.float64).cpu().numpy()   # host copy: not timed
+        v = c.v_cache[pages].to(torch.float64).cpu().numpy()
+        q = c.q[b:b + 1].to(torch.float64).cpu().numpy()
+        pt = np.arange(n, dtype=np.int64)[None, :]
+        t0 = time.perf_counter()
+        op, lp = oracle.paged_decode_splitkv(q, k, v, pt, np.array([L]), P, c.scale,
+                                             c.kv_chunk, c.num_splits)
+        oracle.merge_state(op, lp)
+        spent += time.perf_counter() - t0
+        done_bytes += 2 * L * hkv * d * 2 + hq * d * 2 * 2 + 4 * n
+        sum_l += L
+        n_req += 1
+        if spent >= budget_s:
+            break
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s",
+            "cores": blas_threads, "kind": "oracle",
+            "sample": f"config3 requests 0..{n_req - 1} ({n_req} of {B}, {sum_l} keys, all "
+                      f"{hq} heads, {c.num_splits} splits + merge), float64 numpy; "
+                      f"{spent:.1f} s on a host with {cores} cores available"}
+
+
+# ---------------------------------------------------------------------------
+
+def stored_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("traffic_bytes")
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the hot path runs on a single MI355X here)", file=sys.stderr)
+        return 2
+    import torch
+    sys.path.insert(0, ROOT)
+    import paged_kv_cache_197_amd as pkv
+    import workloads
+    pkv.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    if args.only == "copy":
+        print(json.dumps({"copy": run_copy(torch, args)}))
+        return 0
+
+    line = {}
+    extra = {}
+    if args.only in ("all", "decode"):
+        r = run_decode(torch, pkv, workloads, args)
+        gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+        achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+        src = source_hash("decode.hip", "common.hpp")
+        line = {
+            "metric": "decode KV GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)",
+            "value": round(gbs, 2),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(r["ms"], 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {
+                "workload": "config3: batched split-KV GQA decode (page-table build + decode + "
+                            "merge_state), B=64, L~U[1024,32768], 32 q / 8 kv heads, D=128, "
+                            "page 64, 40000-page pool, 4096-token chunks",
+                "batch": r["batch"], "sum_kv_len": r["sum_l"], "num_splits": r["splits"],
+                "algorithmic_bytes_per_step": r["bytes"],
+            },
+            "roofline": {
+                "kernel": "decode_splitkv_kernel<bf16,128,uniform-page>",
+                "bound": "hbm",
+                "achieved": round(achieved, 2),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "kernel_ms": round(r["kernel_ms"], 4),
+                "traffic": stored_traffic("decode_config3", src),
+                "source_hash": src,
+            },
+        }
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_decode(torch, r, args.cpu_seconds)
+        del r
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "swa"):
+        try:
+            r = run_swa(torch, pkv, workloads, args)
+            extra["swa_decode"] = {
+                "workload": "config4: prefill-aware sliding-window decode, B=32, window 4096, "
+                            "64 q / 8 kv heads, D=128, page 1 (table built on GPU)",
+                "ms_per_step": round(r["ms"], 4), "decode_kernel_ms": round(r["kernel_ms"], 4),
+                "table_build_ms": round(r["build_ms"], 4),
+                "GB/s": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 2),
+                "kernel_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
+                "kernel_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4),
+                "sum_kv_len": r["sum_kv_len"], "num_splits": r["splits"]}
+        except Exception as e:  # report, do not hide
+            extra["swa_decode"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "prefill"):
+        try:
+            r = run_prefill(torch, pkv, workloads, args)
+            tf = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+            extra["prefill"] = {
+                "workload": "config2: varlen causal extend, prefix [0,128,512,1000] + new "
+                            "[256,64,512,17], 32 q / 8 kv heads, D=128, page 1",
+                "kernel_ms": round(r["kernel_ms"], 5), "ms_per_step": round(r["ms"], 5),
+                "TFLOP/s": round(tf, 2), "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS,
+                "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": r["flops"],
+                "visible_pairs_per_head": r["pairs"]}
+        except Exception as e:
+            extra["prefill"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "sparse"):
+        try:
+            r = run_sparse(torch, pkv, workloads, args)
+            extra["sparse_mla"] = {
+                "workload": "config5: top-k sparse MLA decode, B=32, ctx 65536, top-k 2048, "
+                            "128 heads, Dqk 576, Dv 512",
+                "cold_kernel_ms": round(r["cold_ms"], 5), "warm_kernel_ms": round(r["warm_ms"], 5),
+                "cold_GB/s": round(r["bytes"] / (r["cold_ms"] * 1e-3) / 1e9, 2),
+                "cold_frac_hbm": round(r["bytes"] / (r["cold_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       4),
+                "warm_GB/s": round(r["bytes"] / (r["warm_ms"] * 1e-3) / 1e9, 2),
+                "cold_TFLOP/s": round(r["flops"] / (r["cold_ms"] * 1e-3) / 1e12, 2),
+                "bytes": r["bytes"], "flops": r["flops"]}
+        except Exception as e:
+            extra["sparse_mla"] = {"error": repr(e)}
+
+    if line:
+        line["other_workloads"] = extra
+    else:
+        line = {"other_workloads": extra}
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

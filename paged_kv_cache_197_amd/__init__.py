@@ -280,7 +280,8 @@ def sparse_topk_decode(q, kv_cache, req_to_token, req_pool_indices, topk_idx, so
         lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
     need = sparse_topk_decode_workspace_size(batch, topk, hq, head_dim_v)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+        # zero-filled once: the kernel leaves its completion counters at zero
+        workspace = torch.zeros((need,), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.sparse_topk_decode(_ptr(q), _ptr(kv), kv.shape[0], _ptr(r2t), r2t.shape[0],
                                 r2t.shape[1], _ptr(rpi), _ptr(idx), topk, batch, hq, dqk,

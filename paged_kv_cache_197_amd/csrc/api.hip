@@ -211,6 +211,8 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
               "prefill: page_size %d pt_stride %d num_pages %lld", page_size, pt_stride,
               (long long)num_pages);
   PKV_REQUIRE(causal == 0 || causal == 1, PKV_EINVAL, "prefill: causal %d", causal);
+  PKV_REQUIRE(max_seqlen_q <= total_q, PKV_EINVAL, "prefill: max_seqlen_q %d > total_q %d",
+              max_seqlen_q, total_q);
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return pkv_host::ok();
   PKV_REQUIRE(q && k_cache && v_cache && page_table && cu_seqlens_q && kv_lens && out,
               PKV_EINVAL, "prefill: NULL required pointer");
@@ -255,8 +257,8 @@ pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num
               head_dim_v);
   PKV_REQUIRE(batch >= 0 && topk >= 0 && num_q_heads >= 1, PKV_EINVAL,
               "sparse_topk_decode: bad sizes batch %d topk %d heads %d", batch, topk, num_q_heads);
-  PKV_REQUIRE(num_q_heads % 16 == 0, PKV_EUNSUPPORTED,
-              "sparse_topk_decode: num_q_heads %d not a multiple of 16", num_q_heads);
+  PKV_REQUIRE(num_q_heads % 32 == 0, PKV_EUNSUPPORTED,
+              "sparse_topk_decode: num_q_heads %d not a multiple of 32", num_q_heads);
   if (batch == 0) return pkv_host::ok();
   PKV_REQUIRE(q && kv_cache && req_to_token && req_pool_indices && out, PKV_EINVAL,
               "sparse_topk_decode: NULL required pointer");

@@ -83,7 +83,7 @@ def test_merge_and_sparse_and_prefill_argument_errors():
     sp = lib.sparse_topk_decode
     assert sp(None, None, 10, None, 2, 10, None, None, 4, 1, 128, 512, 512, 0.1, None, 0, None,
               None, None) == EUNSUP
-    assert sp(None, None, 10, None, 2, 10, None, None, 4, 1, 120, 576, 512, 0.1, None, 0, None,
+    assert sp(None, None, 10, None, 2, 10, None, None, 4, 1, 112, 576, 512, 0.1, None, 0, None,
               None, None) == EUNSUP
     assert sp(None, None, 10, None, 2, 10, None, None, 4, 1, 128, 576, 512, 0.1, None, 0, None,
               None, None) == EINVAL

@@ -1,0 +1,102 @@
+"""Top-k sparse MLA decode on the GPU versus the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_197_amd as pkv
+import workloads
+from helpers import LSE_TOL, O_TOL, assert_close, np_f, np_i, say, to_device
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def compact_sparse(c, rows):
+    """Host copies of only the cache rows the given requests' top-k lists name.
+
+    Returns (q, kv, req_to_token, req_pool_indices, topk_idx) for the oracle:
+    the token table is rewritten to point into the compact cache, so the
+    oracle still translates each logical index through a token table.
+    """
+    r2t = np_i(c.req_to_token)
+    rpi = np_i(c.req_pool_indices)
+    idx = np_i(c.topk_idx)
+    needed = []
+    for b in rows:
+        for i in idx[b]:
+            if i >= 0:
+                needed.append(r2t[rpi[b], i])
+    uniq = np.unique(np.array(needed, dtype=np.int64))
+    kv = np_f(c.kv_cache[torch.as_tensor(uniq, device=c.kv_cache.device)])
+    remap = {int(s): j for j, s in enumerate(uniq)}
+    ctx = r2t.shape[1]
+    r2t_small = np.zeros((len(rows), ctx), dtype=np.int64)
+    for j, b in enumerate(rows):
+        for i in idx[b]:
+            if i >= 0:
+                r2t_small[j, i] = remap[int(r2t[rpi[b], i])]
+    q = np_f(c.q[torch.as_tensor(rows, device=c.q.device)])
+    return q, kv, r2t_small, np.arange(len(rows)), idx[rows]
+
+
+def run_case(c, rows=None):
+    out = torch.full((c.q.shape[0], c.q.shape[1], c.head_dim_v), float("nan"),
+                     dtype=torch.bfloat16, device=DEV)
+    lse = torch.full(c.q.shape[:2], float("nan"), device=DEV)
+    pkv.sparse_topk_decode(c.q, c.kv_cache, c.req_to_token, c.req_pool_indices, c.topk_idx,
+                           c.scale, head_dim_v=c.head_dim_v, out=out, lse=lse)
+    torch.cuda.synchronize()
+    if rows is None:
+        rows = list(range(c.q.shape[0]))
+    q, kv, r2t, rpi, idx = compact_sparse(c, rows)
+    ro, rl = oracle.sparse_topk_decode(q, kv, r2t, rpi, idx, c.scale, c.head_dim_v)
+    assert_close("out", np_f(out)[rows], ro, O_TOL)
+    assert_close("lse", np_f(lse)[rows], rl, LSE_TOL)
+    return out, lse
+
+
+def test_small_config5():
+    c = to_device(workloads.small_config5(), DEV)
+    say("small_config5")
+    run_case(c)
+
+
+def test_small_config5_with_padding():
+    c = to_device(workloads.small_config5(seed=16, num_pad=37), DEV)
+    say("small_config5 with -1 padding")
+    run_case(c)
+
+
+def test_config5_full_size_sampled():
+    c = to_device(workloads.config5(value_device=DEV), DEV)
+    say("config5 full, rows 0 7 18 31")
+    run_case(c, rows=[0, 7, 18, 31])
+
+
+@pytest.mark.parametrize("batch,topk,heads,pad", [(1, 1, 32, 0), (1, 2048, 32, 0), (2, 33, 64, 0),
+                                                  (5, 700, 96, 100), (1, 4096, 32, 0),
+                                                  (3, 64, 32, 64)])
+def test_sparse_edge_shapes(batch, topk, heads, pad):
+    c = workloads.make_sparse_case(80 + batch + topk, batch=batch, ctx=max(topk, 5000), topk=topk,
+                                   num_q_heads=heads, head_dim_qk=576, head_dim_v=512,
+                                   num_pad=pad)
+    c = to_device(c, DEV)
+    say(f"sparse batch={batch} topk={topk} heads={heads} pad={pad}")
+    run_case(c)
+
+
+def test_sparse_repeat_calls_and_order_invariance():
+    c = to_device(workloads.small_config5(seed=17), DEV)
+    say("sparse repeat / shuffled top-k")
+    a = run_case(c)
+    b = run_case(c)      # the split counters were reset by the first call
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    g = torch.Generator().manual_seed(5)
+    perm = torch.stack([torch.randperm(c.topk_idx.shape[1], generator=g)
+                        for _ in range(c.topk_idx.shape[0])]).to(DEV)
+    c2 = workloads.SparseCase(**{**c.__dict__, "topk_idx": torch.gather(c.topk_idx, 1, perm)})
+    d = run_case(c2)
+    assert_close("shuffled out", np_f(d[0]), np_f(a[0]), 1e-2)
+    assert_close("shuffled lse", np_f(d[1]), np_f(a[1]), 1e-4)
