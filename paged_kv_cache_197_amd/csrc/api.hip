@@ -30,6 +30,14 @@ static pkv_status_t from_hip(hipError_t e, const char* what) {
   return ok();
 }
 
+// log2(v) when v is a power of two, else -1
+static int32_t log2_if_pow2(int32_t v) {
+  if (v <= 0 || (v & (v - 1)) != 0) return -1;
+  int32_t k = 0;
+  while ((1 << k) != v) ++k;
+  return k;
+}
+
 static float scale_log2(float softmax_scale) {
   return static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
 }
@@ -230,6 +238,7 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
   a.hq = num_q_heads;
   a.hkv = num_kv_heads;
   a.page_size = page_size;
+  a.page_shift = pkv_host::log2_if_pow2(page_size);
   a.num_pages = num_pages;
   a.scale_log2 = pkv_host::scale_log2(softmax_scale);
   a.causal = causal;

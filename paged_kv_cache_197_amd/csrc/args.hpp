@@ -45,6 +45,7 @@ struct PrefillArgs {
   const int32_t* cu_q;
   const int32_t* kv_lens;
   int32_t batch, total_q, max_seqlen_q, hq, hkv, page_size;
+  int32_t page_shift;   // log2(page_size) when it is a power of two, else -1
   int64_t num_pages;
   float scale_log2;
   int32_t causal;

@@ -35,8 +35,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 h = static_cast<__bf16>(f);
   return __builtin_bit_cast(uint16_t, h);
 }
+// Two fp32 -> packed bf16 pair (lo in bits 0-15), one v_cvt_pk_bf16_f32, RNE.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Pair the low halves / high halves of two packed words: (a.lo, b.lo), (a.hi, b.hi).
@@ -65,6 +69,11 @@ __device__ __forceinline__ float sum_over_groups16(float v) {
 }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Make the load that produced `v` complete here: an empty asm statement that
+// reads the register, so the waitcnt inserted for it lands before a loop
+// instead of inside it.
+__device__ __forceinline__ void retire(uint32_t v) { asm volatile("" ::"v"(v)); }
 
 // Clamp an index read from device memory into [0, n): a violated precondition
 // turns into a wrong (but in-bounds) access instead of a fault.

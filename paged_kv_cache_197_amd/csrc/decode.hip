@@ -40,18 +40,24 @@ struct Chunk {
   uint32_t w[NDW];
 };
 
-template <int NDW>
+// NT: non-temporal (streaming) load. Not used for K / V: on this kernel's
+// access pattern (64-byte half-line pieces of 256-byte rows) it raised the
+// fetched bytes by ~4% and lowered throughput, although a plain linear read
+// sweep streams faster with it.
+template <int NDW, bool NT = false>
 __device__ __forceinline__ Chunk<NDW> load_chunk(const void* p) {
   Chunk<NDW> c;
   if constexpr (NDW == 2) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 v = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p))
+                       : *reinterpret_cast<const u32x2*>(p);
     c.w[0] = v.x;
     c.w[1] = v.y;
   } else {
     static_assert(NDW % 4 == 0, "chunk of 8, 16 or 32 bytes");
 #pragma unroll
     for (int i = 0; i < NDW / 4; ++i) {
-      const u32x4 v = reinterpret_cast<const u32x4*>(p)[i];
+      const u32x4 v = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i)
+                         : reinterpret_cast<const u32x4*>(p)[i];
       c.w[4 * i + 0] = v.x;
       c.w[4 * i + 1] = v.y;
       c.w[4 * i + 2] = v.z;
@@ -95,18 +101,29 @@ struct DecodeKernel {
     return (e < 4) ? (4 * g + e) : (16 + 4 * g + (e - 4));
   }
 
-  // --- index stage: what the lane needs to compute row addresses ----------
-  // Uniform pages (page_size % 32 == 0): every token of a tile is on one page;
-  // the index is that page's first slot for the tile. Otherwise each lane
-  // resolves the slot of token (lane % 32) of the tile, shared by shuffles.
-  static __device__ __forceinline__ int64_t fetch_index(const DecodeArgs& a, const int32_t* pt_row,
-                                                        int tile_start, int end, int lane) {
+  // --- index stage -----------------------------------------------------------
+  // Uniform pages (page_size % 32 == 0, tiles page-aligned): every token of a
+  // tile is on one page, so the wave loads one page-table entry per tile.
+  // Otherwise lane l loads the entry of token (l % 32) of the tile and the
+  // slots are shared by shuffles. The raw entry is fetched one tile ahead of
+  // its use; the address arithmetic waits until the tile's loads are issued.
+  static __device__ __forceinline__ int32_t fetch_raw(const DecodeArgs& a, const int32_t* pt_row,
+                                                      int tile_start, int end, int lane) {
     if constexpr (UNIFORM_PAGE) {
-      const int64_t page = clamp_index(pt_row[tile_start / a.page_size], a.num_pages);
+      return pt_row[tile_start / a.page_size];
+    } else {
+      const int t = min(tile_start + (lane & 31), end - 1);
+      return pt_row[t / a.page_size];
+    }
+  }
+
+  static __device__ __forceinline__ int64_t slot_base(const DecodeArgs& a, int32_t raw,
+                                                      int tile_start, int end, int lane) {
+    const int64_t page = clamp_index(raw, a.num_pages);
+    if constexpr (UNIFORM_PAGE) {
       return page * a.page_size + (tile_start % a.page_size);
     } else {
       const int t = min(tile_start + (lane & 31), end - 1);
-      const int64_t page = clamp_index(pt_row[t / a.page_size], a.num_pages);
       return page * a.page_size + (t % a.page_size);
     }
   }
@@ -138,6 +155,86 @@ struct DecodeKernel {
       const int64_t slot = slot_of(idx, tok_of(g, e), tile_start, end);
       const char* row = vbase + ((slot * row_elems) + static_cast<int64_t>(kvh) * D) * EB;
       t.v[e] = load_chunk<VDW>(row + (CH * c) * EB);
+    }
+  }
+
+  // One tile: S^T = K . Q^T, online softmax (base 2), O^T += V^T . P^T.
+  static __device__ __forceinline__ void consume(const Tile& cur, int ts, int end, int g,
+                                                 float scale_log2, const Chunk<KDW> (&qop)[NK],
+                                                 f32x4 (&acc)[NB], float& m_run, float& l_run) {
+    f32x4 st[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      st[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        if constexpr (IS_BF16) {
+          u32x4 kw = {cur.k[u][j].w[0], cur.k[u][j].w[1], cur.k[u][j].w[2], cur.k[u][j].w[3]};
+          u32x4 qw = {qop[j].w[0], qop[j].w[1], qop[j].w[2], qop[j].w[3]};
+          st[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), as_bf16x8(qw), st[u], 0,
+                                                          0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            st[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(word_f32(cur.k[u][j].w[e]),
+                                                         word_f32(qop[j].w[e]), st[u], 0, 0, 0);
+        }
+      }
+    }
+
+    float x[8];
+    const int valid = end - ts;  // tokens of this tile inside the split (may exceed 32)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sv = st[e >> 2][e & 3] * scale_log2;
+      x[e] = (tok_of(g, e) < valid) ? sv : neg_inf();
+    }
+    float mt = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
+    mt = max_over_groups16(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2(x[e] - m_new);
+      psum += p[e];
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] *= alpha;
+
+    if constexpr (IS_BF16) {
+      u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                  pack_bf16x2(p[6], p[7])};
+      const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        u32x4 vw;
+        if ((n & 1) == 0) {
+          vw.x = pair_lo(cur.v[0].w[n >> 1], cur.v[1].w[n >> 1]);
+          vw.y = pair_lo(cur.v[2].w[n >> 1], cur.v[3].w[n >> 1]);
+          vw.z = pair_lo(cur.v[4].w[n >> 1], cur.v[5].w[n >> 1]);
+          vw.w = pair_lo(cur.v[6].w[n >> 1], cur.v[7].w[n >> 1]);
+        } else {
+          vw.x = pair_hi(cur.v[0].w[n >> 1], cur.v[1].w[n >> 1]);
+          vw.y = pair_hi(cur.v[2].w[n >> 1], cur.v[3].w[n >> 1]);
+          vw.z = pair_hi(cur.v[4].w[n >> 1], cur.v[5].w[n >> 1]);
+          vw.w = pair_hi(cur.v[6].w[n >> 1], cur.v[7].w[n >> 1]);
+        }
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pb, acc[n], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(word_f32(cur.v[e].w[n]), p[e], acc[n], 0,
+                                                        0, 0);
+      }
     }
   }
 
@@ -195,9 +292,13 @@ struct DecodeKernel {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
         qop[j] = load_chunk<KDW>(qrow + (32 * j + 8 * g) * EB);
-        if (c >= G) {
+      }
 #pragma unroll
-          for (int w = 0; w < KDW; ++w) qop[j].w[w] = 0u;
+      for (int j = 0; j < NK; ++j) {
+#pragma unroll
+        for (int w = 0; w < KDW; ++w) {
+          qop[j].w[w] = (c < G) ? qop[j].w[w] : 0u;
+          retire(qop[j].w[w]);
         }
       }
     }
@@ -211,102 +312,41 @@ struct DecodeKernel {
     const int32_t* pt_row = a.pt + static_cast<int64_t>(b) * a.pt_stride;
     const int n_tiles = (end - start + 31) / 32;
 
-    int tile = wave;
-    Tile cur, nxt;
-    int64_t idx_nxt = 0;
+    // Ping-pong tile buffers: tile t+4 streams in while tile t is consumed,
+    // and no register copies sit between the loads and their consumer. The
+    // prefetch is unconditional (past the wave's last tile it re-reads the
+    // current tile, which the caches already hold) so the loop body has one
+    // path and every wait counts exactly the loads it must.
+    int tile = __builtin_amdgcn_readfirstlane(wave);
     if (tile < n_tiles) {
-      const int64_t idx_cur = fetch_index(a, pt_row, start + 32 * tile, end, lane);
-      if (tile + 4 < n_tiles) idx_nxt = fetch_index(a, pt_row, start + 32 * (tile + 4), end, lane);
-      fetch_data(a, idx_cur, start + 32 * tile, end, kvh, c, g, cur);
-    }
-    for (; tile < n_tiles; tile += 4) {
-      const int ts = start + 32 * tile;
-      const bool have_next = tile + 4 < n_tiles;
-      int64_t idx_nn = 0;
-      if (tile + 8 < n_tiles) idx_nn = fetch_index(a, pt_row, start + 32 * (tile + 8), end, lane);
-      if (have_next) fetch_data(a, idx_nxt, start + 32 * (tile + 4), end, kvh, c, g, nxt);
-
-      // ---- S^T = K . Q^T for the two 16-token halves ----
-      f32x4 st[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        st[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < NK; ++j) {
-          if constexpr (IS_BF16) {
-            u32x4 kw = {cur.k[u][j].w[0], cur.k[u][j].w[1], cur.k[u][j].w[2], cur.k[u][j].w[3]};
-            u32x4 qw = {qop[j].w[0], qop[j].w[1], qop[j].w[2], qop[j].w[3]};
-            st[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), as_bf16x8(qw), st[u], 0,
-                                                            0, 0);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              st[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(word_f32(cur.k[u][j].w[e]),
-                                                           word_f32(qop[j].w[e]), st[u], 0, 0, 0);
-          }
+      const int last = n_tiles - 1 - ((n_tiles - 1 - tile) & 3);   // this wave's last tile
+      auto ahead = [&](int t, int k) { return min(t + 4 * k, last); };
+      Tile ta, tb;
+      const int32_t raw0 = fetch_raw(a, pt_row, start + 32 * tile, end, lane);
+      int32_t raw_n = fetch_raw(a, pt_row, start + 32 * ahead(tile, 1), end, lane);
+      fetch_data(a, slot_base(a, raw0, start + 32 * tile, end, lane), start + 32 * tile, end, kvh,
+                 c, g, ta);
+      while (true) {
+        int32_t raw_nn = fetch_raw(a, pt_row, start + 32 * ahead(tile, 2), end, lane);
+        {
+          const int ts = start + 32 * ahead(tile, 1);
+          fetch_data(a, slot_base(a, raw_n, ts, end, lane), ts, end, kvh, c, g, tb);
         }
-      }
-
-      // ---- online softmax over this tile (base-2 domain) ----
-      float x[8];
-      const int valid = end - ts;  // tokens of this tile inside the split (may exceed 32)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float sv = st[e >> 2][e & 3] * a.scale_log2;
-        x[e] = (tok_of(g, e) < valid) ? sv : neg_inf();
-      }
-      float mt = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-      mt = max_over_groups16(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      float p[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(x[e] - m_new);
-        psum += p[e];
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int n = 0; n < NB; ++n) acc[n] *= alpha;
-
-      // ---- O^T += V^T . P^T ----
-      if constexpr (IS_BF16) {
-        u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                    pack_bf16x2(p[6], p[7])};
-        const bf16x8 pb = as_bf16x8(pw);
-#pragma unroll
-        for (int n = 0; n < NB; ++n) {
-          u32x4 vw;
-          if ((n & 1) == 0) {
-            vw.x = pair_lo(cur.v[0].w[n >> 1], cur.v[1].w[n >> 1]);
-            vw.y = pair_lo(cur.v[2].w[n >> 1], cur.v[3].w[n >> 1]);
-            vw.z = pair_lo(cur.v[4].w[n >> 1], cur.v[5].w[n >> 1]);
-            vw.w = pair_lo(cur.v[6].w[n >> 1], cur.v[7].w[n >> 1]);
-          } else {
-            vw.x = pair_hi(cur.v[0].w[n >> 1], cur.v[1].w[n >> 1]);
-            vw.y = pair_hi(cur.v[2].w[n >> 1], cur.v[3].w[n >> 1]);
-            vw.z = pair_hi(cur.v[4].w[n >> 1], cur.v[5].w[n >> 1]);
-            vw.w = pair_hi(cur.v[6].w[n >> 1], cur.v[7].w[n >> 1]);
-          }
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pb, acc[n], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
+        consume(ta, start + 32 * tile, end, g, a.scale_log2, qop, acc, m_run, l_run);
+        tile += 4;
+        if (tile > last) break;
+        raw_n = raw_nn;
+        raw_nn = fetch_raw(a, pt_row, start + 32 * ahead(tile, 2), end, lane);
+        {
+          const int ts = start + 32 * ahead(tile, 1);
+          fetch_data(a, slot_base(a, raw_n, ts, end, lane), ts, end, kvh, c, g, ta);
         }
-      } else {
-#pragma unroll
-        for (int n = 0; n < NB; ++n) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(word_f32(cur.v[e].w[n]), p[e], acc[n], 0,
-                                                          0, 0);
-        }
-      }
-
-      if (have_next) {
-        cur = nxt;
-        idx_nxt = idx_nn;
+        __builtin_amdgcn_sched_barrier(0);
+        consume(tb, start + 32 * tile, end, g, a.scale_log2, qop, acc, m_run, l_run);
+        tile += 4;
+        if (tile > last) break;
+        raw_n = raw_nn;
       }
     }
 

@@ -8,15 +8,18 @@
 // key split). The workgroup first translates its whole slice of the top-k
 // list into cache slots (kept in LDS), then walks it in 32-key tiles: each
 // tile's 32 rows (1152 B each) are gathered into double-buffered LDS and
-// shared by the four waves.
+// shared by the four waves. Per tile:
 //   * QK: wave w computes a partial S^T [32 keys x 32 heads] over score dims
-//     [144w, 144w + 144) (nine 32x32x16 MFMAs); the four partials are summed
-//     through LDS so every wave holds the full tile scores (C-layout: lane
-//     (head = lane % 32, h = lane / 32) holds keys 8*(r/4) + 4h + r%4).
-//   * softmax: online, per head column, identical in all four waves.
+//     [144w, 144w + 144) (nine 32x32x16 MFMAs) and publishes it in LDS.
+//   * softmax: wave w sums the four partials for heads [8w, 8w + 8) only, runs
+//     the online softmax for them and publishes P^T (bf16) and each head's
+//     rescale factor, so the softmax work is not repeated across waves.
 //   * PV: wave w accumulates O^T for value dims [128w, 128w + 128) (four
 //     32x32x16 blocks x two 16-key k-steps); the value rows are the first 512
 //     dims of the same LDS tile.
+// MFMA C-layout used throughout: lane (col = lane % 32, h = lane / 32) holds
+// column col (a head) and rows rho(h, r) = 8*(r/4) + 4h + r%4, r < 16 (keys
+// of S^T, dims of O^T).
 // Key splits (needed to fill the chip when batch x head blocks is small) are
 // merged inside the kernel: every split writes its normalised partial and LSE
 // to the workspace, and the last split to finish (device-scope counter) merges
@@ -42,8 +45,11 @@ struct SparseCfg {
   static constexpr int DV_SLICE = DV / 4;       // 128 value dims per wave
   static constexpr int NBLK = DV_SLICE / 32;    // 4
   static constexpr int MAX_KEYS_PER_SPLIT = 2048;   // slot list capacity in LDS
-  static constexpr int SP_BYTES = 4 * 64 * 16 * 4;  // partial S^T of 4 waves
-  static constexpr int LDS_BYTES = 2 * TILE_BYTES + SP_BYTES + MAX_KEYS_PER_SPLIT * 4 + 16;
+  static constexpr int SP_BYTES = 4 * 4 * 64 * 16;  // partial S^T: [wave][quad][lane] float4
+  static constexpr int PB_BYTES = 4 * 64 * 8;       // P^T bf16: [quad][lane] 4 x bf16
+  static constexpr int AUX_BYTES = 32 * 4 * 3;      // per head: rescale factor, final m, l
+  static constexpr int LDS_BYTES =
+      2 * TILE_BYTES + SP_BYTES + PB_BYTES + AUX_BYTES + MAX_KEYS_PER_SPLIT * 4;
 };
 
 // splits per (request, head block) so the grid has about 256 workgroups, each
@@ -85,7 +91,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
   extern __shared__ __align__(16) char smem[];
   auto lds_tile = [&](int i) { return smem + i * C::TILE_BYTES; };
   float* sp = reinterpret_cast<float*>(smem + 2 * C::TILE_BYTES);
-  int32_t* slots = reinterpret_cast<int32_t*>(smem + 2 * C::TILE_BYTES + C::SP_BYTES);
+  int32_t* slots = reinterpret_cast<int32_t*>(smem + 2 * C::TILE_BYTES + C::SP_BYTES +
+                                              C::PB_BYTES + C::AUX_BYTES);
 
   const int hblocks = a.hq / C::HB;
   const int units = a.batch * hblocks;
@@ -130,30 +137,41 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
 
   const char* kvb = static_cast<const char*>(a.kv);
   u32x4 stage[C::PPT];
+  // unconditional loads (skipped keys read row 0; their LDS rows are zeroed)
   auto load_tile = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < C::PPT; ++i) {
       const int piece = threadIdx.x + 256 * i;
       const int key = piece / (C::ROW_BYTES / 16);
       const int chunk = piece % (C::ROW_BYTES / 16);
-      const int32_t s = slots[tile * C::KT + key];
-      if (s >= 0) {
-        stage[i] = *reinterpret_cast<const u32x4*>(kvb + static_cast<int64_t>(s) * C::ROW_BYTES +
-                                                   chunk * 16);
-      } else {
-        stage[i] = u32x4{0u, 0u, 0u, 0u};   // skipped key: finite zeros, masked below
-      }
+      const int32_t sl = max(slots[tile * C::KT + key], 0);
+      stage[i] = *reinterpret_cast<const u32x4*>(kvb + static_cast<int64_t>(sl) * C::ROW_BYTES +
+                                                 chunk * 16);
     }
   };
-  auto store_tile = [&](char* dst) {
+  auto store_tile = [&](char* dst, uint32_t valid) {
+    const bool all_valid = (valid == 0xffffffffu);
 #pragma unroll
     for (int i = 0; i < C::PPT; ++i) {
       const int piece = threadIdx.x + 256 * i;
       const int key = piece / (C::ROW_BYTES / 16);
       const int chunk = piece % (C::ROW_BYTES / 16);
-      *reinterpret_cast<u32x4*>(dst + key * C::LDS_STRIDE + chunk * 16) = stage[i];
+      u32x4 v = stage[i];
+      if (!all_valid && !((valid >> key) & 1u)) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(dst + key * C::LDS_STRIDE + chunk * 16) = v;
     }
   };
+  // bit k set: key k of the tile has a slot (the same mask in every wave)
+  auto tile_valid = [&](int tile) -> uint32_t {
+    const bool ok = slots[tile * C::KT + (lane & 31)] >= 0;
+    return static_cast<uint32_t>(__ballot(ok) & 0xffffffffull);
+  };
+
+  float* aux = reinterpret_cast<float*>(smem + 2 * C::TILE_BYTES + C::SP_BYTES + C::PB_BYTES);
+  float* alpha_buf = aux;            // [32] per-head rescale of the current tile
+  float* m_buf = aux + 32;           // [32] final running max per head (raw units)
+  float* l_buf = aux + 64;           // [32] final denominator per head
+  char* pb = smem + 2 * C::TILE_BYTES + C::SP_BYTES;
 
   // Q^T operand for this wave's score slice: head col, dims 144w + 16j + 8h + [0, 8)
   const int head = hb * C::HB + col;
@@ -164,6 +182,13 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
 #pragma unroll
     for (int j = 0; j < C::QK_STEPS; ++j)
       qop[j] = *reinterpret_cast<const u32x4*>(qrow + (C::QK_SLICE * wave + 16 * j + 8 * h) * 2);
+#pragma unroll
+    for (int j = 0; j < C::QK_STEPS; ++j) {
+      retire(qop[j].x);
+      retire(qop[j].y);
+      retire(qop[j].z);
+      retire(qop[j].w);
+    }
   }
 
   f32x16 acc[C::NBLK];
@@ -171,12 +196,21 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
   for (int n = 0; n < C::NBLK; ++n)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[n][i] = 0.f;
-  float m_run = neg_inf();
-  float l_run = 0.f;
 
+  // softmax ownership: lane L of wave w handles head sc = 8w + (L & 7), the
+  // four S^T values of lane sl = sc + 32 * sh, register quad sq
+  const int sc = 8 * wave + (lane & 7);
+  const int sh = (lane >> 3) & 1;
+  const int sq = lane >> 4;
+  const int src_lane = sc + 32 * sh;
+  float m_run = neg_inf();   // raw score units, for head sc
+  float l_run = 0.f;         // partial denominator over this lane's keys
+
+  uint32_t valid_cur = 0xffffffffu;
   if (n_tiles > 0) {
+    valid_cur = tile_valid(0);
     load_tile(0);
-    store_tile(lds_tile(0));
+    store_tile(lds_tile(0), valid_cur);
   }
   __syncthreads();
 
@@ -184,104 +218,132 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
     const int buf = kt & 1;
     const bool more = kt + 1 < n_tiles;
     if (more) load_tile(kt + 1);
+    __builtin_amdgcn_sched_barrier(0);   // the next tile's loads go out before the MFMAs
     const char* tile = lds_tile(buf);
 
-    // ---- partial S^T over this wave's 144 score dims ----
-    f32x16 s;
+    // ---- partial S^T over this wave's 144 score dims -> LDS ----
+    {
+      f32x16 s;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
-    const char* krow = tile + col * C::LDS_STRIDE;     // A row: key col of the tile
+      for (int i = 0; i < 16; ++i) s[i] = 0.f;
+      const char* krow = tile + col * C::LDS_STRIDE;     // A row: key col of the tile
 #pragma unroll
-    for (int j = 0; j < C::QK_STEPS; ++j) {
-      const u32x4 kw = *reinterpret_cast<const u32x4*>(krow + (C::QK_SLICE * wave + 16 * j + 8 * h) * 2);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), as_bf16x8(qop[j]), s, 0, 0, 0);
-    }
-    float4* my = reinterpret_cast<float4*>(sp + (wave * 64 + lane) * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) my[i] = make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
-    __syncthreads();
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float4* src = reinterpret_cast<const float4*>(sp + (w * 64 + lane) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 v = src[i];
-        x[4 * i] += v.x;
-        x[4 * i + 1] += v.y;
-        x[4 * i + 2] += v.z;
-        x[4 * i + 3] += v.w;
+      for (int j = 0; j < C::QK_STEPS; ++j) {
+        const u32x4 kw =
+            *reinterpret_cast<const u32x4*>(krow + (C::QK_SLICE * wave + 16 * j + 8 * h) * 2);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), as_bf16x8(qop[j]), s, 0, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        reinterpret_cast<float4*>(sp)[(wave * 4 + i) * 64 + lane] =
+            make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
     }
+    const uint32_t valid_next = more ? tile_valid(kt + 1) : 0xffffffffu;
+    __syncthreads();   // A: partial scores visible; every wave is done with tile buf ^ 1
+    if (more) store_tile(lds_tile(buf ^ 1), valid_next);
 
-    // ---- online softmax for head col ----
-    float mt = neg_inf();
+    // ---- softmax for heads [8w, 8w + 8): 4 keys per lane ----
+    {
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = rho32(h, i);
-      const bool ok = slots[kt * C::KT + key] >= 0;
-      x[i] = ok ? x[i] * a.scale_log2 : neg_inf();
-      mt = fmaxf(mt, x[i]);
+      for (int w = 0; w < 4; ++w) {
+        const float4 v = reinterpret_cast<const float4*>(sp)[(w * 4 + sq) * 64 + src_lane];
+        x[0] += v.x;
+        x[1] += v.y;
+        x[2] += v.z;
+        x[3] += v.w;
+      }
+      if (valid_cur != 0xffffffffu) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {   // key of register 4*sq + j of lane half sh
+          const int key = 8 * sq + 4 * sh + j;
+          if (!((valid_cur >> key) & 1u)) x[j] = neg_inf();
+        }
+      }
+      float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mt = fmaxf(mt, __shfl_xor(mt, 8));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m_run, mt);
+      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+      const float alpha = fast_exp2((m_run - m_use) * a.scale_log2);
+      const float neg_mc = -m_use * a.scale_log2;
+      m_run = m_new;
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = fast_exp2(__builtin_fmaf(x[j], a.scale_log2, neg_mc));
+      l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+      u32x2 pw;
+      pw.x = pack_bf16x2(p[0], p[1]);
+      pw.y = pack_bf16x2(p[2], p[3]);
+      reinterpret_cast<u32x2*>(pb)[sq * 64 + src_lane] = pw;
+      if (lane < 8) alpha_buf[sc] = alpha;
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float p[16];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[i] = fast_exp2(x[i] - m_use);
-      psum += p[i];
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int n = 0; n < C::NBLK; ++n) acc[n] *= alpha;
+    __syncthreads();   // B: P^T and rescale factors visible
 
     // ---- O^T (this wave's 128 value dims) += V^T . P^T ----
+    {
+      const float alpha_c = alpha_buf[col];
+      if (__any(alpha_c != 1.f)) {   // rescale only when some head's running max moved
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      u32x4 pw = {pack_bf16x2(p[8 * t + 0], p[8 * t + 1]), pack_bf16x2(p[8 * t + 2], p[8 * t + 3]),
-                  pack_bf16x2(p[8 * t + 4], p[8 * t + 5]), pack_bf16x2(p[8 * t + 6], p[8 * t + 7])};
-      uint32_t vr[8][2];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = 16 * t + 8 * (e >> 2) + 4 * h + (e & 3);
-        const u32x2 w2 = *reinterpret_cast<const u32x2*>(tile + key * C::LDS_STRIDE +
-                                                          (C::DV_SLICE * wave + 4 * col) * 2);
-        vr[e][0] = w2.x;
-        vr[e][1] = w2.y;
+        for (int n = 0; n < C::NBLK; ++n) acc[n] *= alpha_c;
       }
 #pragma unroll
-      for (int n = 0; n < C::NBLK; ++n) {
-        u32x4 vw;
-        if ((n & 1) == 0) {
-          vw.x = pair_lo(vr[0][n >> 1], vr[1][n >> 1]);
-          vw.y = pair_lo(vr[2][n >> 1], vr[3][n >> 1]);
-          vw.z = pair_lo(vr[4][n >> 1], vr[5][n >> 1]);
-          vw.w = pair_lo(vr[6][n >> 1], vr[7][n >> 1]);
-        } else {
-          vw.x = pair_hi(vr[0][n >> 1], vr[1][n >> 1]);
-          vw.y = pair_hi(vr[2][n >> 1], vr[3][n >> 1]);
-          vw.z = pair_hi(vr[4][n >> 1], vr[5][n >> 1]);
-          vw.w = pair_hi(vr[6][n >> 1], vr[7][n >> 1]);
+      for (int t = 0; t < 2; ++t) {
+        const u32x2 p0 = reinterpret_cast<const u32x2*>(pb)[(2 * t) * 64 + lane];
+        const u32x2 p1 = reinterpret_cast<const u32x2*>(pb)[(2 * t + 1) * 64 + lane];
+        const u32x4 pw = {p0.x, p0.y, p1.x, p1.y};
+        uint32_t vr[8][2];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = 16 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+          const u32x2 w2 = *reinterpret_cast<const u32x2*>(tile + key * C::LDS_STRIDE +
+                                                            (C::DV_SLICE * wave + 4 * col) * 2);
+          vr[e][0] = w2.x;
+          vr[e][1] = w2.y;
         }
-        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), as_bf16x8(pw), acc[n], 0,
-                                                         0, 0);
+#pragma unroll
+        for (int n = 0; n < C::NBLK; ++n) {
+          u32x4 vw;
+          if ((n & 1) == 0) {
+            vw.x = pair_lo(vr[0][n >> 1], vr[1][n >> 1]);
+            vw.y = pair_lo(vr[2][n >> 1], vr[3][n >> 1]);
+            vw.z = pair_lo(vr[4][n >> 1], vr[5][n >> 1]);
+            vw.w = pair_lo(vr[6][n >> 1], vr[7][n >> 1]);
+          } else {
+            vw.x = pair_hi(vr[0][n >> 1], vr[1][n >> 1]);
+            vw.y = pair_hi(vr[2][n >> 1], vr[3][n >> 1]);
+            vw.z = pair_hi(vr[4][n >> 1], vr[5][n >> 1]);
+            vw.w = pair_hi(vr[6][n >> 1], vr[7][n >> 1]);
+          }
+          acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), as_bf16x8(pw), acc[n], 0,
+                                                           0, 0);
+        }
       }
     }
-
-    if (more) store_tile(lds_tile(buf ^ 1));
-    __syncthreads();   // partial scores and tile buf are free again
+    valid_cur = valid_next;
+    // the next iteration's barrier A orders these reads before buf / pb / sp are rewritten
   }
 
+  // ---- per-head totals: owners reduce their lanes' partial sums, publish ----
+  {
+    float l = l_run;
+    l += __shfl_xor(l, 8);
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (lane < 8) {
+      m_buf[sc] = m_run;
+      l_buf[sc] = l;
+    }
+  }
+  __syncthreads();
+  const float m_head = m_buf[col];
+  const float l_tot = l_buf[col];
+
   // ---- this split's result for head col, value dims 128w + 4*rho(h, i) + n ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse_val = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : neg_inf();
+  const float lse_val =
+      l_tot > 0.f ? (m_head * a.scale_log2 + fast_log2(l_tot)) * kLn2 : neg_inf();
 
   if (splits == 1) {
     bf16_t* dst = static_cast<bf16_t*>(a.out) + (static_cast<int64_t>(b) * a.hq + head) * C::DV +
