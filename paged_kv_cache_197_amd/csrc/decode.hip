@@ -408,6 +408,337 @@ struct DecodeKernel {
   }
 };
 
+// ---------------------------------------------------------------------------
+// bf16 decode over kv-head groups. The general kernel above reads one kv
+// head's 256-byte slice of each token row in 64-byte pieces; on a paged cache
+// that pattern streams well below what HBM sustains. Here a workgroup owns
+// HPW = 256 / D adjacent kv heads, so every token row contributes one
+// contiguous 512-byte run, fetched by half-waves (32 lanes x 16 B, two rows
+// per instruction, non-temporal: the cache is read once).
+//
+// Each wave takes 16-token tiles w, w+4, ... of the split. A tile is loaded
+// into registers one tile ahead, then written to the wave's private LDS
+// region, from which the MFMA operands are read in the layout they need; no
+// workgroup barrier is involved until the final merge.
+//
+// The HPW heads are treated as one virtual row of VD = 256 dims. The 16 MFMA
+// columns hold the HPW * G query heads of the group (G <= 16 / HPW); the
+// query operand is zero outside its own kv head's dims, so
+//   S^T [16 tok x 16 cols] = Krow [16 x 256] . Qpad^T [256 x 16]
+// is exact for every column (8 16x16x32 MFMAs), and
+//   O^T [256 x 16 cols] += Vrow^T [256 x 16 tok] . P^T [16 x 16]
+// (16 16x16x16 MFMAs) yields each column's output in the rows of its own kv
+// head; the other rows are discarded. Lane (c = lane % 16, g = lane / 16)
+// owns column c: its S^T accumulator holds tokens 4g..4g+3, the k-group its
+// P^T operand needs, so softmax state stays in the lane.
+// O^T block n, row r is virtual dim 128 * (n / 8) + 8 r + n % 8: a lane reads
+// two 16-byte pieces per token (dims 8c.. and 128 + 8c..), and sixteen lanes
+// of one token read 256 consecutive bytes (no bank conflicts).
+template <int D>
+struct DecodeGroupKernel {
+  static constexpr int HPW = 256 / D;             // kv heads per workgroup
+  static constexpr int TT = 16;                   // tokens per wave tile
+  static constexpr int ROW = 512;                 // bytes of the group's row slice
+  static constexpr int STRIDE = ROW + 16;         // LDS row stride (rows 4 banks apart)
+  static constexpr int WAVE_LDS = 2 * TT * STRIDE;
+  static constexpr int LDS_BYTES = 4 * WAVE_LDS;
+  static_assert(64 * 64 * 4 <= WAVE_LDS, "merge buffer fits a wave's tile region");
+
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+  struct Stage {
+    u32x4 k[8];
+    u32x4 v[8];
+  };
+
+  static __device__ __forceinline__ u32x4 ld_nt(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+
+  // Page-table entry for a tile: one per tile when pages hold whole tiles,
+  // else lane l holds the entry of token l % 16.
+  template <bool UNIFORM>
+  static __device__ __forceinline__ int32_t fetch_raw(const DecodeArgs& a, const int32_t* pt_row,
+                                                      int ts, int end, int lane) {
+    if constexpr (UNIFORM) {
+      return pt_row[ts / a.page_size];
+    } else {
+      const int t = min(ts + (lane & 15), end - 1);
+      return pt_row[t / a.page_size];
+    }
+  }
+
+  // Row r = 2i + lane / 32 of the tile, bytes [16 (lane % 32), +16) of the
+  // group's slice, for K and V.
+  template <bool UNIFORM>
+  static __device__ __forceinline__ void load(const DecodeArgs& a, int32_t raw, int ts, int end,
+                                              int lane, int64_t row_bytes, int64_t col,
+                                              Stage& st) {
+    const char* kb = static_cast<const char*>(a.k) + col + 16 * (lane & 31);
+    const char* vb = static_cast<const char*>(a.v) + col + 16 * (lane & 31);
+    const int half = lane >> 5;
+    if constexpr (UNIFORM) {
+      const int64_t slot0 = clamp_index(raw, a.num_pages) * a.page_size + ts % a.page_size;
+      const int lim = end - 1 - ts;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t off = (slot0 + min(2 * i + half, lim)) * row_bytes;
+        st.k[i] = ld_nt(kb + off);
+        st.v[i] = ld_nt(vb + off);
+      }
+    } else {
+      const int t = min(ts + (lane & 15), end - 1);
+      const int slot = static_cast<int>(clamp_index(raw, a.num_pages)) * a.page_size + t % a.page_size;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t off = static_cast<int64_t>(__shfl(slot, 2 * i + half)) * row_bytes;
+        st.k[i] = ld_nt(kb + off);
+        st.v[i] = ld_nt(vb + off);
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void stash(char* my, int lane, const Stage& st) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 2 * i + (lane >> 5);
+      *reinterpret_cast<u32x4*>(my + row * STRIDE + 16 * (lane & 31)) = st.k[i];
+      *reinterpret_cast<u32x4*>(my + (TT + row) * STRIDE + 16 * (lane & 31)) = st.v[i];
+    }
+  }
+
+  static __device__ __forceinline__ void compute(const char* my, int c, int g, int valid,
+                                                 float scale_log2, const u32x4 (&qop)[8],
+                                                 f32x4 (&acc)[16], float& m_run, float& l_run) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 kw = *reinterpret_cast<const u32x4*>(my + c * STRIDE + 64 * j + 16 * g);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), as_bf16x8(qop[j]), s, 0, 0, 0);
+    }
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (4 * g + i < valid) ? s[i] * scale_log2 : neg_inf();
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mt = max_over_groups16(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_new);
+    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int n = 0; n < 16; ++n) acc[n] *= alpha;
+    }
+    const u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    const s16x4 pb = __builtin_bit_cast(s16x4, pw);
+
+    // V rows 4g..4g+3: dims [8c, 8c + 8) and [128 + 8c, 128 + 8c + 8)
+    u32x4 lo[4], hi[4];
+    const char* vt = my + (TT + 4 * g) * STRIDE + 16 * c;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      lo[t] = *reinterpret_cast<const u32x4*>(vt + t * STRIDE);
+      hi[t] = *reinterpret_cast<const u32x4*>(vt + t * STRIDE + 256);
+    }
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const u32x4(&w)[4] = (n < 8) ? lo : hi;
+      const int k = (n & 7) >> 1;
+      u32x2 vw;
+      if ((n & 1) == 0) {
+        vw.x = pair_lo(w[0][k], w[1][k]);
+        vw.y = pair_lo(w[2][k], w[3][k]);
+      } else {
+        vw.x = pair_hi(w[0][k], w[1][k]);
+        vw.y = pair_hi(w[2][k], w[3][k]);
+      }
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vw), pb, acc[n],
+                                                         0, 0, 0);
+    }
+  }
+
+  template <bool UNIFORM>
+  static __device__ void run(const DecodeArgs& a) {
+    extern __shared__ __align__(16) char smem[];
+    __shared__ float sm_m[4][16];
+    __shared__ float sm_l[4][16];
+
+    const int G = a.hq / a.hkv;
+    const int ngrp = a.hkv / HPW;
+    const int grp = blockIdx.x % ngrp;
+    const int rest = blockIdx.x / ngrp;
+    const int b = rest % a.batch;
+    const int s = rest / a.batch;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int ncol = HPW * G;                 // query heads of the group
+    const int h0 = grp * ncol;                // first query head of the group
+
+    const int64_t cap = static_cast<int64_t>(a.pt_stride) * a.page_size;
+    const int L = static_cast<int>(min<int64_t>(max(a.kv_lens[b], 0), cap));
+    const int start = static_cast<int>(min<int64_t>(static_cast<int64_t>(s) * a.chunk, L));
+    const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(start) + a.chunk, L));
+    const bool single = (a.num_splits == 1);
+
+    if (start >= end) {   // empty split: (0, -inf)
+      for (int i = threadIdx.x; i < ncol * D; i += blockDim.x) {
+        const int64_t row = static_cast<int64_t>(b) * a.hq + h0 + i / D;
+        const int d = i % D;
+        if (single) static_cast<bf16_t*>(a.out)[row * D + d].bits = 0;
+        else a.o_part[(static_cast<int64_t>(s) * a.batch * a.hq + row) * D + d] = 0.f;
+      }
+      for (int i = threadIdx.x; i < ncol; i += blockDim.x) {
+        const int64_t row = static_cast<int64_t>(b) * a.hq + h0 + i;
+        if (single) {
+          if (a.lse) a.lse[row] = neg_inf();
+        } else {
+          a.lse_part[static_cast<int64_t>(s) * a.batch * a.hq + row] = neg_inf();
+        }
+      }
+      return;
+    }
+
+    // Qpad^T operand, k-step j: dims 32j + 8g + [0, 8) of the virtual row,
+    // nonzero only where they belong to column c's kv head.
+    const int kk = c / G;                     // column's kv head within the group
+    u32x4 qop[8];
+    {
+      const int head = h0 + min(c, ncol - 1);
+      const char* qrow = static_cast<const char*>(a.q) + (static_cast<int64_t>(b) * a.hq + head) * D * 2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qop[j] = *reinterpret_cast<const u32x4*>(qrow + ((32 * j + 8 * g) % D) * 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool mine = (c < ncol) && ((32 * j + 8 * g) / D == kk);
+        qop[j].x = mine ? qop[j].x : 0u;
+        qop[j].y = mine ? qop[j].y : 0u;
+        qop[j].z = mine ? qop[j].z : 0u;
+        qop[j].w = mine ? qop[j].w : 0u;
+        retire(qop[j].x);
+        retire(qop[j].y);
+        retire(qop[j].z);
+        retire(qop[j].w);
+      }
+    }
+
+    f32x4 acc[16];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = neg_inf();
+    float l_run = 0.f;
+
+    char* my = smem + wave * WAVE_LDS;
+    const int32_t* pt_row = a.pt + static_cast<int64_t>(b) * a.pt_stride;
+    const int64_t row_bytes = static_cast<int64_t>(a.hkv) * D * 2;
+    const int64_t col = static_cast<int64_t>(grp) * ROW;
+    const int n_tiles = (end - start + TT - 1) / TT;
+
+    int tile = wave;
+    if (tile < n_tiles) {
+      const int last = n_tiles - 1 - ((n_tiles - 1 - tile) & 3);   // this wave's last tile
+      auto ahead = [&](int t, int k) { return min(t + 4 * k, last); };
+      Stage st;
+      int32_t raw_n = fetch_raw<UNIFORM>(a, pt_row, start + TT * ahead(tile, 1), end, lane);
+      load<UNIFORM>(a, fetch_raw<UNIFORM>(a, pt_row, start + TT * tile, end, lane), start + TT * tile,
+                    end, lane, row_bytes, col, st);
+      stash(my, lane, st);
+      while (true) {
+        const int32_t raw_nn = fetch_raw<UNIFORM>(a, pt_row, start + TT * ahead(tile, 2), end, lane);
+        const bool more = tile + 4 <= last;
+        if (more)
+          load<UNIFORM>(a, raw_n, start + TT * (tile + 4), end, lane, row_bytes, col, st);
+        __builtin_amdgcn_sched_barrier(0);   // the next tile's loads go out before the MFMAs
+        compute(my, c, g, end - (start + TT * tile), a.scale_log2, qop, acc, m_run, l_run);
+        if (!more) break;
+        tile += 4;
+        stash(my, lane, st);   // same wave: its LDS reads above complete first
+        raw_n = raw_nn;
+      }
+    }
+
+    // ---- merge the four waves' states through LDS ----
+    // region of wave w: [lane][16-byte piece], piece 4i + n/4 holds acc[n..n+3][i],
+    // swizzled by lane % 16 so that a wave's stores and loads spread over the banks
+    const float l_tot = sum_over_groups16(l_run);
+    if (g == 0) {
+      sm_m[wave][c] = m_run;
+      sm_l[wave][c] = l_tot;
+    }
+    {
+      float4* reg = reinterpret_cast<float4*>(my) + lane * 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          reg[(4 * i + q4) ^ c] =
+              make_float4(acc[4 * q4][i], acc[4 * q4 + 1][i], acc[4 * q4 + 2][i], acc[4 * q4 + 3][i]);
+    }
+    __syncthreads();
+
+    // wave i writes row i of every block: lane (c, g) holds virtual dims
+    // 128 h + 32 g + 8 i + [0, 8); it is the owner when they are column c's.
+    const int i = wave;
+    const int hsel = (HPW == 2) ? kk : (kk >> 1);
+    const bool owner = (c < ncol) && (HPW == 2 || ((g >> 1) == (kk & 1)));
+    if (!owner) return;
+    float M = sm_m[0][c];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][c]);
+    float f[4];
+    float Ltot = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      f[w] = (sm_m[w][c] == neg_inf()) ? 0.f : fast_exp2(sm_m[w][c] - M);
+      Ltot += f[w] * sm_l[w][c];
+    }
+    const float inv = 1.f / Ltot;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4* reg = reinterpret_cast<const float4*>(smem + w * WAVE_LDS) + lane * 16;
+      const float4 u0 = reg[(4 * i + 2 * hsel) ^ c];
+      const float4 u1 = reg[(4 * i + 2 * hsel + 1) ^ c];
+      o[0] += f[w] * u0.x;
+      o[1] += f[w] * u0.y;
+      o[2] += f[w] * u0.z;
+      o[3] += f[w] * u0.w;
+      o[4] += f[w] * u1.x;
+      o[5] += f[w] * u1.y;
+      o[6] += f[w] * u1.z;
+      o[7] += f[w] * u1.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= inv;
+    const int d0 = (32 * g + 8 * i) % D;
+    const int64_t row = static_cast<int64_t>(b) * a.hq + h0 + c;
+    const float lse_val = (M + fast_log2(Ltot)) * kLn2;
+    const bool lse_lane = (i == 0) && (d0 == 0);
+    if (single) {
+      u32x4 w4 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                  pack_bf16x2(o[6], o[7])};
+      *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(a.out) + row * D + d0) = w4;
+      if (a.lse != nullptr && lse_lane) a.lse[row] = lse_val;
+    } else {
+      float* dst = a.o_part + (static_cast<int64_t>(s) * a.batch * a.hq + row) * D + d0;
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      if (lse_lane) a.lse_part[static_cast<int64_t>(s) * a.batch * a.hq + row] = lse_val;
+    }
+  }
+};
+
+template <int D, bool UNIFORM>
+__global__ __launch_bounds__(256, 2) void decode_group_kernel(DecodeArgs a) {
+  DecodeGroupKernel<D>::template run<UNIFORM>(a);
+}
+
 // bf16 tiles fit two workgroups per CU (<= 256 VGPRs); fp32 tiles are twice
 // as wide and get the whole register file.
 template <typename T, int D, bool UNIFORM_PAGE>
@@ -443,7 +774,32 @@ static hipError_t launch_decode_t(const pkv::DecodeArgs& a, bool uniform, hipStr
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_decode_group(const pkv::DecodeArgs& a, hipStream_t stream) {
+  constexpr int HPW = pkv::DecodeGroupKernel<D>::HPW;
+  const dim3 grid(static_cast<unsigned>(a.hkv / HPW) * a.batch * a.num_splits);
+  constexpr unsigned lds = pkv::DecodeGroupKernel<D>::LDS_BYTES;
+  // whole 16-token tiles on one page: page_size % 16 == 0 (splits start on pages)
+  if (a.page_size % 16 == 0)
+    hipLaunchKernelGGL((pkv::decode_group_kernel<D, true>), grid, dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL((pkv::decode_group_kernel<D, false>), grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t decode_splitkv(const pkv::DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
+  if (dtype == PKV_BF16) {
+    // kv-head groups: HPW = 256 / D heads whose G query heads fit 16 columns,
+    // and slot numbers that fit 32 bits (per-token pages are shuffled as int32)
+    const int hpw = 256 / head_dim;
+    const int G = a.hq / a.hkv;
+    const bool group = (a.hkv % hpw == 0) && (hpw * G <= 16) &&
+                       (a.num_pages * a.page_size <= INT_MAX);
+    if (group) {
+      if (head_dim == 128) return launch_decode_group<128>(a, stream);
+      return launch_decode_group<64>(a, stream);
+    }
+  }
   // tiles are 32 tokens starting at multiples of 32 inside a split; with
   // page_size % 32 == 0 and chunk % page_size == 0 a tile never crosses a page
   const bool uniform = (a.page_size % 32 == 0) && (a.chunk % a.page_size == 0);

@@ -149,28 +149,34 @@ def test_config4_full_size_sampled():
 EDGE_LENS = [0, 1, 31, 32, 33, 64, 65, 129, 255, 256, 257]
 
 
-@pytest.mark.parametrize("dtype,D,P,group,chunk", [
-    (torch.bfloat16, 128, 64, 4, 128),
-    (torch.bfloat16, 128, 1, 8, 64),
-    (torch.bfloat16, 128, 16, 1, 96),
-    (torch.bfloat16, 64, 32, 16, 64),
-    (torch.bfloat16, 64, 128, 2, 128),
-    (torch.bfloat16, 128, 2, 3, 32),
-    (torch.float32, 64, 16, 2, 64),
-    (torch.float32, 128, 64, 4, 128),
-    (torch.float32, 128, 1, 5, 32),
+# The bf16 rows with Hkv * D a multiple of 256 and (256 / D) * G <= 16 run the
+# kv-head-group kernel (D 128: pairs of kv heads; D 64: fours); the others, and
+# fp32, run the per-kv-head kernel.
+@pytest.mark.parametrize("dtype,D,P,group,chunk,hkv", [
+    (torch.bfloat16, 128, 64, 4, 128, 2),
+    (torch.bfloat16, 128, 1, 8, 64, 2),
+    (torch.bfloat16, 128, 16, 1, 96, 2),
+    (torch.bfloat16, 128, 2, 3, 32, 2),
+    (torch.bfloat16, 128, 64, 16, 128, 2),
+    (torch.bfloat16, 128, 32, 4, 64, 3),
+    (torch.bfloat16, 64, 32, 16, 64, 2),
+    (torch.bfloat16, 64, 128, 2, 128, 2),
+    (torch.bfloat16, 64, 16, 4, 64, 4),
+    (torch.bfloat16, 64, 1, 3, 32, 8),
+    (torch.float32, 64, 16, 2, 64, 2),
+    (torch.float32, 128, 64, 4, 128, 2),
+    (torch.float32, 128, 1, 5, 32, 2),
 ])
-def test_decode_edge_lengths(dtype, D, P, group, chunk):
-    hkv = 2
+def test_decode_edge_lengths(dtype, D, P, group, chunk, hkv):
     c = workloads.make_decode_case(40 + D + P + group, seq_lens=EDGE_LENS, num_q_heads=hkv * group,
                                    num_kv_heads=hkv, head_dim=D, page_size=P,
                                    num_pages=-(-sum(EDGE_LENS) // P) + len(EDGE_LENS) + 3,
                                    dtype=dtype, kv_chunk=chunk)
     c = to_device(c, DEV)
     fp32 = dtype == torch.float32
-    say(f"edge dtype={dtype} D={D} P={P} G={group} chunk={chunk} S={c.num_splits}")
+    say(f"edge dtype={dtype} D={D} P={P} G={group} Hkv={hkv} chunk={chunk} S={c.num_splits}")
     check_case(c, chunk, c.num_splits, fp32=fp32)
-    say(f"edge single split dtype={dtype} D={D} P={P}")
+    say(f"edge single split dtype={dtype} D={D} P={P} Hkv={hkv}")
     check_case(c, 0, 1, fp32=fp32)
 
 
