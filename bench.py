@@ -208,13 +208,18 @@ def run_prefill(torch, pkv, workloads, args):
     kl = torch.empty((B,), dtype=torch.int32, device=dev)
     out = torch.empty_like(c.q)
     lse = torch.empty(c.q.shape[:2], dtype=torch.float32, device=dev)
+    max_k = int(c.seq_lens.max())
+    ws_bytes = pkv.paged_attn_varlen_prefill_workspace_size(
+        B, c.q.shape[0], c.max_seqlen_q, max_k, c.q.shape[1], c.k_cache.shape[2], c.q.shape[2])
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)   # counters stay zero
 
     def step(timer):
         pkv.build_page_table(r2t, rpi, sl, c.page_size, c.table_width, page_table=pt,
                              kv_lens=kl, with_cu_seqlens=False)
         e0 = timer.mark() if timer else None
         pkv.paged_attn_varlen_prefill(c.q, c.k_cache, c.v_cache, pt, cu, kl, c.max_seqlen_q,
-                                      c.scale, causal=True, out=out, lse=lse)
+                                      c.scale, max_seqlen_k=max_k, causal=True, workspace=ws,
+                                      out=out, lse=lse)
         if timer:
             timer.pairs.append((e0, timer.mark()))
 

@@ -107,19 +107,34 @@ pkv_status_t build_page_table(const int32_t* req_to_token, int64_t req_to_token_
  * k_cache, v_cache [num_pages, page_size, num_kv_heads, head_dim] dtype
  * page_table [batch, pt_stride] int32 page ids; cu_seqlens_q [batch + 1];
  * kv_lens [batch] int32 (requires M_b <= L_b <= pt_stride * page_size)
+ * max_seqlen_q >= every M_b and max_seqlen_k >= every L_b: launch bounds, as
+ *          in flash_attn_varlen_func; they size the grid and the key splits.
+ *          (A max_seqlen_k below some L_b is still correct, only slower.)
+ * workspace caller-owned device memory of at least
+ *          paged_attn_varlen_prefill_workspace_size(...) bytes (0 when no q
+ *          tile is split: NULL allowed). Its first bytes are counters that
+ *          must be zero before the first call; every call leaves them zero.
+ *          Calls sharing a workspace must not overlap in time.
  * out      [total_q, num_q_heads, head_dim] dtype (out); lse [total_q, num_q_heads]
  *          fp32 (out) or NULL.
  * Supported: dtype PKV_BF16, head_dim 64 or 128, Hq % Hkv == 0,
- * Hq / Hkv <= 16, causal 0 or 1. max_seqlen_q >= every M_b (a launch bound).
+ * Hq / Hkv <= 16, causal 0 or 1.
+ * Errors: PKV_EINVAL for bad sizes, NULL pointers or a short workspace.
  */
+size_t paged_attn_varlen_prefill_workspace_size(int32_t batch, int32_t total_q,
+                                                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim);
 pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void* k_cache,
                                        const void* v_cache, int64_t num_pages,
                                        const int32_t* page_table, int32_t pt_stride,
                                        const int32_t* cu_seqlens_q, const int32_t* kv_lens,
                                        int32_t batch, int32_t total_q, int32_t max_seqlen_q,
-                                       int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t page_size, float softmax_scale,
-                                       int32_t causal, void* out, float* lse, void* stream);
+                                       int32_t max_seqlen_k, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                       float softmax_scale, int32_t causal, void* workspace,
+                                       size_t workspace_bytes, void* out, float* lse,
+                                       void* stream);
 
 /*
  * paged_attn_decode_splitkv -- one query token per request, key axis split.

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "PkvError", "PkvLibraryMissing", "load_library", "library_path", "declared_symbols",
-    "build_page_table", "paged_attn_varlen_prefill", "paged_attn_decode_splitkv",
+    "build_page_table", "paged_attn_varlen_prefill", "paged_attn_varlen_prefill_workspace_size",
+    "paged_attn_decode_splitkv",
     "merge_state", "sparse_topk_decode", "sparse_topk_decode_workspace_size",
     "PKV_F32", "PKV_BF16",
 ]
@@ -62,9 +63,11 @@ _SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "build_page_table": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _I32, _I32, _I32, _I32,
                                         _P, _P, _P, _P]),
+    "paged_attn_varlen_prefill_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32,
+                                                        _I32]),
     "paged_attn_varlen_prefill": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _P,
-                                                 _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F,
-                                                 _I32, _P, _P, _P]),
+                                                 _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                 _F, _I32, _P, _SZ, _P, _P, _P]),
     "paged_attn_decode_splitkv": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _I32,
                                                  _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _P,
                                                  _P, _P, _P]),
@@ -229,10 +232,21 @@ def merge_state(o_parts, lse_parts, *, out_dtype=torch.bfloat16, out=None, lse_o
     return out, lse_out
 
 
+def paged_attn_varlen_prefill_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k,
+                                             num_q_heads, num_kv_heads, head_dim):
+    return int(load_library().paged_attn_varlen_prefill_workspace_size(
+        batch, total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim))
+
+
 def paged_attn_varlen_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens,
-                              max_seqlen_q, softmax_scale, *, causal=True, out=None, lse=None,
-                              return_lse=True):
-    """Causal varlen extend over a paged cache. Returns (out, lse or None)."""
+                              max_seqlen_q, softmax_scale, *, max_seqlen_k=None, causal=True,
+                              workspace=None, out=None, lse=None, return_lse=True):
+    """Causal varlen extend over a paged cache. Returns (out, lse or None).
+
+    max_seqlen_k defaults to the page table's capacity (width * page_size).
+    workspace: a uint8 device tensor of at least
+    paged_attn_varlen_prefill_workspace_size(...) bytes whose counters are
+    zero (a fresh zeroed one is made when None; the call leaves them zero)."""
     lib = load_library()
     dev = q.device
     _need(q, "q", torch.bfloat16, dev, 3)
@@ -243,14 +257,23 @@ def paged_attn_varlen_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_
     kl = _i32(kv_lens, "kv_lens", dev)
     total_q, hq, d = q.shape
     num_pages, page_size, hkv, _ = k_cache.shape
+    batch = kl.numel()
+    if max_seqlen_k is None:
+        max_seqlen_k = pt.shape[1] * page_size
+    need = paged_attn_varlen_prefill_workspace_size(batch, total_q, int(max_seqlen_q),
+                                                    int(max_seqlen_k), hq, hkv, d)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev)
     st = lib.paged_attn_varlen_prefill(
         _ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(pt),
-        pt.shape[1], _ptr(cu), _ptr(kl), kl.numel(), total_q, int(max_seqlen_q), hq, hkv, d,
-        page_size, float(softmax_scale), int(bool(causal)), _ptr(out), _ptr(lse), _stream(dev))
+        pt.shape[1], _ptr(cu), _ptr(kl), batch, total_q, int(max_seqlen_q), int(max_seqlen_k),
+        hq, hkv, d, page_size, float(softmax_scale), int(bool(causal)), _ptr(workspace),
+        ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
     _check("paged_attn_varlen_prefill", st)
     return out, lse
 

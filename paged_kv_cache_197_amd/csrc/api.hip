@@ -1,6 +1,8 @@
 // C ABI of libpkv.so (declared in include/pkv.h): host-side argument checks,
 // then one launcher call per entry point. No allocation, no synchronisation.
 #include <math.h>
+
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -40,6 +42,48 @@ static int32_t log2_if_pow2(int32_t v) {
 
 static float scale_log2(float softmax_scale) {
   return static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+}
+
+// Key-split plan of paged_attn_varlen_prefill. A workgroup (8 waves) handles
+// one (q tile, kv head); when there are fewer such units than half the CUs,
+// the 32-key tiles a q tile sees are cut into splits of split_tiles tiles so
+// that about kPrefillWorkgroups workgroups run, never below kMinSplitTiles
+// tiles per split. The workspace holds the split counters (zero between
+// calls), then the partial LSEs and outputs.
+constexpr int64_t kPrefillWorkgroups = 256;
+constexpr int64_t kMinSplitTiles = 4;
+
+struct PrefillPlan {
+  int32_t split_tiles, max_splits, max_qtiles;
+  size_t counter_bytes, lse_bytes, o_bytes, bytes;
+};
+
+static size_t round_up256(size_t v) { return (v + 255) / 256 * 256; }
+
+static PrefillPlan prefill_plan(int64_t batch, int64_t total_q, int64_t max_seqlen_q,
+                                int64_t max_seqlen_k, int64_t hq, int64_t hkv, int64_t head_dim) {
+  PrefillPlan p;
+  const int64_t n_kt = max_seqlen_k > 0 ? (max_seqlen_k + 31) / 32 : 1;
+  p.max_qtiles = static_cast<int32_t>((max_seqlen_q + 31) / 32);
+  const int64_t qtiles = std::min<int64_t>((total_q + 31) / 32 + batch, batch * p.max_qtiles);
+  const int64_t units = std::max<int64_t>(1, qtiles * hkv);
+  const int64_t want = (2 * units >= kPrefillWorkgroups)
+                           ? 1
+                           : std::min<int64_t>(16, kPrefillWorkgroups / units);
+  const int64_t tiles = std::max<int64_t>(kMinSplitTiles, (n_kt + want - 1) / want);
+  p.split_tiles = static_cast<int32_t>(std::min<int64_t>(tiles, 1 << 30));
+  p.max_splits = static_cast<int32_t>((n_kt + p.split_tiles - 1) / p.split_tiles);
+  p.counter_bytes = p.lse_bytes = p.o_bytes = p.bytes = 0;
+  if (p.max_splits <= 1) {
+    p.max_splits = 1;
+    return p;
+  }
+  const int64_t n_hb = (hq / hkv + 3) / 4;
+  p.counter_bytes = round_up256(static_cast<size_t>(batch * p.max_qtiles * hkv * n_hb) * 4);
+  p.lse_bytes = round_up256(static_cast<size_t>(p.max_splits) * total_q * hq * 4);
+  p.o_bytes = static_cast<size_t>(p.max_splits) * total_q * hq * head_dim * 4;
+  p.bytes = p.counter_bytes + p.lse_bytes + p.o_bytes;
+  return p;
 }
 
 }  // namespace pkv_host
@@ -195,20 +239,34 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
       "decode launch");
 }
 
+size_t paged_attn_varlen_prefill_workspace_size(int32_t batch, int32_t total_q,
+                                                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim) {
+  if (batch <= 0 || total_q <= 0 || max_seqlen_q <= 0 || max_seqlen_k < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0)
+    return 0;
+  return pkv_host::prefill_plan(batch, total_q, max_seqlen_q, max_seqlen_k, num_q_heads,
+                                num_kv_heads, head_dim)
+      .bytes;
+}
+
 pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void* k_cache,
                                        const void* v_cache, int64_t num_pages,
                                        const int32_t* page_table, int32_t pt_stride,
                                        const int32_t* cu_seqlens_q, const int32_t* kv_lens,
                                        int32_t batch, int32_t total_q, int32_t max_seqlen_q,
-                                       int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t page_size, float softmax_scale,
-                                       int32_t causal, void* out, float* lse, void* stream) {
+                                       int32_t max_seqlen_k, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                       float softmax_scale, int32_t causal, void* workspace,
+                                       size_t workspace_bytes, void* out, float* lse,
+                                       void* stream) {
   PKV_REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "prefill: dtype %d not supported (bf16)",
               dtype);
   PKV_REQUIRE(head_dim == 64 || head_dim == 128, PKV_EUNSUPPORTED,
               "prefill: head_dim %d not supported (64, 128)", head_dim);
-  PKV_REQUIRE(batch >= 0 && total_q >= 0 && max_seqlen_q >= 0 && num_q_heads >= 1 &&
-                  num_kv_heads >= 1,
+  PKV_REQUIRE(batch >= 0 && total_q >= 0 && max_seqlen_q >= 0 && max_seqlen_k >= 0 &&
+                  num_q_heads >= 1 && num_kv_heads >= 1,
               PKV_EINVAL, "prefill: bad sizes");
   PKV_REQUIRE(num_q_heads % num_kv_heads == 0, PKV_EINVAL,
               "prefill: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
@@ -224,6 +282,11 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return pkv_host::ok();
   PKV_REQUIRE(q && k_cache && v_cache && page_table && cu_seqlens_q && kv_lens && out,
               PKV_EINVAL, "prefill: NULL required pointer");
+  const pkv_host::PrefillPlan plan = pkv_host::prefill_plan(
+      batch, total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim);
+  PKV_REQUIRE(plan.bytes == 0 || (workspace != nullptr && workspace_bytes >= plan.bytes),
+              PKV_EINVAL, "prefill: workspace of %zu bytes, need %zu", workspace_bytes,
+              plan.bytes);
   pkv::PrefillArgs a;
   a.q = q;
   a.k = k_cache;
@@ -242,6 +305,14 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
   a.num_pages = num_pages;
   a.scale_log2 = pkv_host::scale_log2(softmax_scale);
   a.causal = causal;
+  a.split_tiles = plan.split_tiles;
+  a.max_splits = plan.max_splits;
+  a.max_qtiles = plan.max_qtiles;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = plan.bytes ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  a.ws_lse = plan.bytes ? reinterpret_cast<float*>(ws + plan.counter_bytes) : nullptr;
+  a.ws_o = plan.bytes ? reinterpret_cast<float*>(ws + plan.counter_bytes + plan.lse_bytes)
+                      : nullptr;
   a.out = out;
   a.lse = lse;
   return pkv_host::from_hip(pkv_launch::prefill(a, head_dim, static_cast<hipStream_t>(stream)),

@@ -75,6 +75,44 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 // instead of inside it.
 __device__ __forceinline__ void retire(uint32_t v) { asm volatile("" ::"v"(v)); }
 
+// Data handed from one workgroup to another within a launch (split partials,
+// then a counter): stores and loads at device scope (cache-policy bit sc1), so
+// they are written through, and read past, the per-XCD L2 caches and need no
+// cache writeback or invalidate around the hand-off. The producer waits for
+// its stores (vmcnt(0)) before bumping the counter; the consumer reads after.
+// Buffer resources need a wave-uniform base; the byte offsets are per lane.
+constexpr int kScopeDevice = 16;   // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kScopeDevice);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, kScopeDevice);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kScopeDevice);
+}
+__device__ __forceinline__ float load_coherent1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kScopeDevice));
+}
+__device__ __forceinline__ f32x2_t load_coherent2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kScopeDevice));
+}
+__device__ __forceinline__ f32x4 load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kScopeDevice));
+}
+// all of this wave's memory operations have completed
+__device__ __forceinline__ void wait_all_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// device-scope counter, relaxed: ordering comes from wait_all_vmem and barriers
+__device__ __forceinline__ int counter_add(int* c, int v) {
+  return __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void counter_reset(int* c) {
+  __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Clamp an index read from device memory into [0, n): a violated precondition
 // turns into a wrong (but in-bounds) access instead of a fault.
 __device__ __forceinline__ int64_t clamp_index(int64_t i, int64_t n) {

@@ -3,13 +3,19 @@
 // new, cu_seqlens_q over the new tokens, causal=True). New row j of request b
 // sits at position L_b - M_b + j and sees keys [0, L_b - M_b + j].
 //
-// Work decomposition: one workgroup of 8 waves per (32-row q tile, kv head,
-// request), dispatched last-q-tile first (those see the most keys). The 8
-// waves form two groups of 4; the tile's keys are cut in two halves, one per
-// group, and the two online-softmax states are merged through LDS at the end,
-// so the longest workgroup walks half the keys. Within a group, wave w owns
-// q heads w, w+4, ... of the GQA group and all four share the group's key
-// tiles: 32 keys gathered through the page table into double-buffered LDS.
+// Work decomposition. One workgroup of 8 waves per (32-row q tile, kv head,
+// request, key split). A q tile's visible 32-key tiles are cut into splits of
+// `split_tiles` tiles when the tiles are long enough to leave CUs idle
+// otherwise; each split writes its normalised partial output and LSE to the
+// workspace at device scope, and the last split of the tile to finish (device-
+// scope counter) merges them. A q tile with one split writes the output
+// directly. Inside a workgroup the split's key tiles are halved between two
+// groups of four waves, whose softmax states are merged through LDS at the end;
+// the two waves sharing a SIMD (one per group) hide each other's latencies.
+// Within a group wave w owns q heads w, w+4, ... of the GQA group and all four
+// share 32-key K/V tiles, copied into the group's three-stage LDS ring by
+// direct global-to-LDS loads two tiles ahead of their use. The page-table
+// entries of the 8 keys a wave copies per tile are scalar loads.
 //
 // Per wave and key tile (32x32x16 bf16 MFMA):
 //   S^T [32 keys x 32 rows] = K [32 x D] . Q^T [D x 32]        (D/16 MFMAs)
@@ -19,240 +25,316 @@
 // operand needs for the two 16-key k-steps, and its O^T accumulator rows are
 // dims of row q. Row max / sum / rescale stay in the lane (the max is reduced
 // with the other lane half by one xor-shuffle).
-// V^T operand: block n, row m is dim NB*m + n (NB = D/32), so a lane reads the
-// NB contiguous dims [NB*m, NB*m + NB) of each of its 8 keys per k-step from
-// LDS and transposes them in registers (byte permutes).
-// Pipeline: the page-table entries of a tile are fetched two tiles ahead and
-// its K/V rows one tile ahead, issued before the current tile's MFMAs.
+// V^T operand: block n, row m is dim 32n + m, read from the row-major LDS tile
+// with gfx950's transposing LDS read (ds_read_b64_tr_b16), so no register
+// shuffles are needed.
+// LDS rows are D*2 bytes with their 16-byte chunks XOR-swizzled by the row
+// index, so that the K operand reads (16 rows, one chunk) hit distinct banks.
 #include "args.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace pkv {
 
-template <int D, bool POW2>
+// 16 bytes per lane from global memory straight into LDS (gfx950): lane l's
+// bytes land at lds_base + 16 l. Counted by vmcnt only; waits are explicit
+// (wait_vmem, then a barrier before any wave reads the stage).
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base));
+}
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 4 bytes per lane into LDS: lane l's word lands at lds_base + 4 l.
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(gptr), "{m0}"(lds_base));
+}
+
+// page-table arithmetic
+enum PageMode : int {
+  kPageToken = 0,   // page_size 1: one entry per key
+  kPagePow2 = 1,    // page_size a power of two: shifts
+  kPageAny = 2,     // anything else: division
+};
+
+template <int D, int PM>
 struct PrefillKernel {
   static constexpr int KT = 32;               // keys per tile
   static constexpr int QT = 32;               // q rows per tile
   static constexpr int NKS = D / 16;          // 16-wide k-steps of S^T
   static constexpr int NB = D / 32;           // 32-dim blocks of O^T
-  static constexpr int ROW_BYTES = D * 2;
-  static constexpr int LDS_STRIDE = ROW_BYTES + 16;   // pad: rows start 4 banks apart
-  static constexpr int TILE_BYTES = KT * LDS_STRIDE;
-  static constexpr int CHUNKS_PER_ROW = ROW_BYTES / 16;          // 16-byte pieces
-  static constexpr int PIECES = KT * CHUNKS_PER_ROW;              // per tile per tensor
-  static constexpr int PPT = PIECES / 256;                        // per thread of a group
-  static constexpr int GROUP_LDS = 4 * TILE_BYTES;                // K, V x double buffer
-  static constexpr int LDS_BYTES = 2 * GROUP_LDS;
-  static constexpr int MERGE_FLOATS = 16 * NB + 2;                // acc + m + l per lane
-  static_assert(4 * 64 * MERGE_FLOATS * 4 <= LDS_BYTES, "merge buffer fits the tile buffers");
+  static constexpr int ROW = D * 2;           // bytes per key row (one kv head)
+  static constexpr int CH = ROW / 16;         // 16-byte chunks per row
+  static constexpr int TILE = KT * ROW;       // one tensor's tile
+  static constexpr int STAGE = 2 * TILE;      // K and V
+  static constexpr int NSTAGE = 3;
+  static constexpr int GROUP_LDS = NSTAGE * STAGE;
+  static constexpr int ENTRY_BYTES = 8 * 2 * 256;     // 8 waves x 2 segments x 64 words
+  static constexpr int LDS_BYTES = 2 * GROUP_LDS + ENTRY_BYTES;
+  static constexpr int RPB = 1024 / ROW;      // key rows per 1 KB copy block
+  static constexpr int IPW = TILE / 1024 / 4; // copy blocks per wave and tensor
+  static constexpr int KPW = IPW * RPB;       // keys per wave per tile
+  static constexpr int SWZ = 256 / ROW;       // rows sharing one 64-bank span
+  static constexpr int MERGE_FLOATS = 16 * NB + 2;   // acc, m, l of a lane
+  static constexpr float kRescaleLog2 = 8.f;          // see compute_tile
+  static_assert(KPW == 8, "a wave copies 8 keys of each tile");
+  static_assert(4 * 64 * MERGE_FLOATS * 4 <= LDS_BYTES, "merge buffer fits the rings");
 
   // key of S^T accumulator register r for lane half h
   static __device__ __forceinline__ int rho(int h, int r) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+  // LDS chunk position of global chunk c of key row k (an involution in c).
+  // u = row index within a 256-byte bank span, rotated left by one bit: the
+  // 16 rows of a K operand read get distinct chunk positions, and so do the
+  // chunk pairs of 4 consecutive rows read by a transposed V read.
+  static __device__ __forceinline__ int swz(int k, int c) {
+    const int u = (k / SWZ) % CH;
+    return c ^ (((2 * u) % CH) | ((2 * u) / CH));
+  }
 
-  struct Stage {
-    u32x4 k[PPT];
-    u32x4 v[PPT];
-  };
-
-  // token t -> (page-table column, offset in page); shifts when P = 2^k
   static __device__ __forceinline__ int page_col(const PrefillArgs& a, int t) {
-    if constexpr (POW2) return t >> a.page_shift;
+    if constexpr (PM == kPageToken) return t;
+    else if constexpr (PM == kPagePow2) return t >> a.page_shift;
     else return t / a.page_size;
   }
   static __device__ __forceinline__ int page_off(const PrefillArgs& a, int t) {
-    if constexpr (POW2) return t & (a.page_size - 1);
+    if constexpr (PM == kPageToken) return 0;
+    else if constexpr (PM == kPagePow2) return t & (a.page_size - 1);
     else return t % a.page_size;
   }
 
-  // page-table entries of the keys this thread copies for `tile`
-  static __device__ __forceinline__ void fetch_raw(const PrefillArgs& a, const int32_t* pt_row,
-                                                   int kv_len, int tile, int gt, int32_t (&raw)[PPT]) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int key = (gt + 256 * i) / CHUNKS_PER_ROW;
-      const int t = min(tile * KT + key, kv_len - 1);   // tail keys: any valid row (masked)
-      raw[i] = pt_row[page_col(a, t)];
-    }
+  // Page-table entries. Each wave copies 8 keys [kt*32 + 8w, +8) of every
+  // tile; the entries of those keys for a segment of SEG consecutive tiles are
+  // fetched by one direct-to-LDS load (lane l: tile l/8, key l%8, clamped to
+  // the last key) into the wave's double-buffered entry slots, a segment ahead.
+  static constexpr int SEG = 8;
+  static __device__ __forceinline__ void fetch_entries(const PrefillArgs& a, const int32_t* pt_row,
+                                                       int L, int seg_tile, int w, int lane,
+                                                       uint32_t slot_base) {
+    const int t = min((seg_tile + lane / 8) * KT + KPW * w + lane % 8, L - 1);
+    lds_dma4(pt_row + page_col(a, t), slot_base);
   }
 
-  // row_bytes = Hkv * D * 2; col_off[i] = kvh * D * 2 + chunk * 16 of piece i
-  static __device__ __forceinline__ void load_tile(const PrefillArgs& a, int kv_len, int tile,
-                                                   int gt, int64_t row_bytes,
-                                                   const int32_t (&col_off)[PPT],
-                                                   const int32_t (&raw)[PPT], Stage& st) {
-    const char* kb = static_cast<const char*>(a.k);
-    const char* vb = static_cast<const char*>(a.v);
+  // Issue the direct-to-LDS copies of key tile kt into the LDS stage at
+  // stage_base. Copy block blk (1 KB of a tensor tile) holds key rows
+  // [blk*RPB, +RPB); lane l fills row blk*RPB + l/CH at LDS chunk l%CH, i.e.
+  // it reads global chunk swz(row, l%CH), at byte chunk_off[i] of the row.
+  // entries: this wave's entry slots of the segment holding kt (tile tt in it).
+  static __device__ __forceinline__ void copy_tile(const PrefillArgs& a, int L, int kt, int tt,
+                                                   int w, int lane, const int32_t* entries,
+                                                   int64_t row_bytes, const char* kb,
+                                                   const char* vb, const int (&chunk_off)[IPW],
+                                                   uint32_t stage_base) {
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int key = (gt + 256 * i) / CHUNKS_PER_ROW;
-      const int t = min(tile * KT + key, kv_len - 1);
-      const int64_t page = clamp_index(raw[i], a.num_pages);
+    for (int i = 0; i < IPW; ++i) {
+      const int j = i * RPB + lane / CH;   // key 8w + j of the tile
+      const int t = min(kt * KT + KPW * w + j, L - 1);
+      const int64_t page = clamp_index(entries[tt * 8 + j], a.num_pages);
       int64_t slot;
-      if constexpr (POW2) slot = (page << a.page_shift) | page_off(a, t);
+      if constexpr (PM == kPageToken) slot = page;
+      else if constexpr (PM == kPagePow2) slot = (page << a.page_shift) | page_off(a, t);
       else slot = page * a.page_size + page_off(a, t);
-      const int64_t off = slot * row_bytes + col_off[i];
-      st.k[i] = *reinterpret_cast<const u32x4*>(kb + off);
-      st.v[i] = *reinterpret_cast<const u32x4*>(vb + off);
-    }
-  }
-
-  static __device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, int gt,
-                                                    const Stage& st) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int piece = gt + 256 * i;
-      const int key = piece / CHUNKS_PER_ROW;
-      const int chunk = piece % CHUNKS_PER_ROW;
-      *reinterpret_cast<u32x4*>(lds_k + key * LDS_STRIDE + chunk * 16) = st.k[i];
-      *reinterpret_cast<u32x4*>(lds_v + key * LDS_STRIDE + chunk * 16) = st.v[i];
+      const int64_t off = slot * row_bytes + chunk_off[i];
+      const int blk = w * IPW + i;
+      lds_dma16(kb + off, stage_base + blk * 1024);
+      lds_dma16(vb + off, stage_base + TILE + blk * 1024);
     }
   }
 
   // One key tile for this wave's row block: S^T, online softmax, O^T update.
+  // kbase / vbase: per-lane LDS offsets of the K and V operand rows (group
+  // ring included) from the stage's base.
   // m_run is kept in raw score units; scale_log2 > 0 is applied inside the
   // exponent (exp2(s * c - m * c)). Masked tiles apply the per-row key limit.
-  static __device__ __forceinline__ void compute_tile(const char* lk, const char* lv, int kt,
-                                                      bool masked, int limit, int q, int h,
-                                                      float scale_log2,
+  static __device__ __forceinline__ void compute_tile(const char* stage, int kbase, int q,
+                                                      const int (&vofs)[2][NB], bool masked,
+                                                      int rel, int h, float scale_log2,
                                                       const u32x4 (&qop)[NKS], f32x16 (&acc)[NB],
                                                       float& m_run, float& l_run) {
+    constexpr int SK = 0;
+    constexpr int SV = TILE;
+    const char* smem = stage;
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    const char* kl = lk + q * LDS_STRIDE;   // A row = key q of the tile
+    u32x4 kw[NKS];   // all K operand reads in flight before the first MFMA
 #pragma unroll
-    for (int j = 0; j < NKS; ++j) {
-      const u32x4 kw = *reinterpret_cast<const u32x4*>(kl + (16 * j + 8 * h) * 2);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), as_bf16x8(qop[j]), s, 0, 0, 0);
-    }
+    for (int j = 0; j < NKS; ++j)
+      kw[j] = *reinterpret_cast<const u32x4*>(smem + kbase + swz(q, 2 * j + h) * 16 + SK);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NKS; ++j)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[j]), as_bf16x8(qop[j]), s, 0, 0, 0);
 
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = s[r];
     if (masked) {   // wave-uniform: only tiles that reach past some row's limit
+      // key kt*32 + rho(h, r) is visible iff rho(h, r) - 4h < rel
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kt * KT + rho(h, r) >= limit) x[r] = neg_inf();
+        if (8 * (r >> 2) + (r & 3) >= rel) x[r] = neg_inf();
     }
     float mt = fmaxf(x[0], x[1]);
 #pragma unroll
     for (int r = 2; r < 16; ++r) mt = fmaxf(mt, x[r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * scale_log2);
+    // m_run is a reference max: it moves only when a row's tile max exceeds it
+    // by more than kRescaleLog2 (log2 units of the scaled score). In between,
+    // the exponentials stay below 2^kRescaleLog2 and the sum and the output
+    // share the reference, so the result is unchanged while the rescale of
+    // the accumulators (64 multiplies) is skipped on almost every tile.
+    // (-inf - -inf is NaN: a row with no visible key yet does not move.)
+    const bool grow = (mt - m_run) * scale_log2 > kRescaleLog2;
+    const float m_ref = grow ? mt : m_run;
+    const float m_use = (m_ref == neg_inf()) ? 0.f : m_ref;
+    const float alpha = grow ? fast_exp2((m_run - m_use) * scale_log2) : 1.f;
     const float neg_mc = -m_use * scale_log2;
-    m_run = m_new;
+    m_run = m_ref;
     float p[16];
-    float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = fast_exp2(__builtin_fmaf(x[r], scale_log2, neg_mc));
-      psum += p[r];
-    }
-    l_run = l_run * alpha + psum;
-    // rescale only when some row's running max moved (rare after the first tiles)
-    if (__any(alpha != 1.f)) {
+    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(x[r], scale_log2, neg_mc));
+    float ps[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ps[i] = (p[4 * i] + p[4 * i + 1]) + (p[4 * i + 2] + p[4 * i + 3]);
+    l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    if (__any(grow)) {
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[n] *= alpha;
     }
 
+    // O^T block n row m = dim 32n + m. Its A operand for the 16-key step t is
+    // V^T[32n + m][keys 16t + 8(e/4) + 4h + e%4], e = 0..7: two transposed
+    // 8-byte LDS reads (ds_read_b64_tr_b16), each turning 16 lanes' row-major
+    // 4-dim pieces of 4 keys into one dim's 4 keys per lane (vofs).
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((address_space(3))) char lds_char;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       u32x4 pw = {pack_bf16x2(p[8 * t + 0], p[8 * t + 1]), pack_bf16x2(p[8 * t + 2], p[8 * t + 3]),
                   pack_bf16x2(p[8 * t + 4], p[8 * t + 5]), pack_bf16x2(p[8 * t + 6], p[8 * t + 7])};
-      // V rows of the 8 keys 16t + 8(e/4) + 4h + e%4, dims [NB*q, NB*q + NB)
-      uint32_t vr[8][NB / 2];
+      s16x4 vt[NB][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = 16 * t + 8 * (e >> 2) + 4 * h + (e & 3);
-        const char* src = lv + key * LDS_STRIDE + NB * q * 2;
-        if constexpr (NB == 4) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(src);
-          vr[e][0] = w.x;
-          vr[e][1] = w.y;
-        } else {
-          vr[e][0] = *reinterpret_cast<const uint32_t*>(src);
-        }
-      }
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          vt[n][s2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
+              (lds_char*)smem + vofs[s2][n] + SV + 16 * t * ROW));
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        u32x4 vw;
-        if ((n & 1) == 0) {
-          vw.x = pair_lo(vr[0][n >> 1], vr[1][n >> 1]);
-          vw.y = pair_lo(vr[2][n >> 1], vr[3][n >> 1]);
-          vw.z = pair_lo(vr[4][n >> 1], vr[5][n >> 1]);
-          vw.w = pair_lo(vr[6][n >> 1], vr[7][n >> 1]);
-        } else {
-          vw.x = pair_hi(vr[0][n >> 1], vr[1][n >> 1]);
-          vw.y = pair_hi(vr[2][n >> 1], vr[3][n >> 1]);
-          vw.z = pair_hi(vr[4][n >> 1], vr[5][n >> 1]);
-          vw.w = pair_hi(vr[6][n >> 1], vr[7][n >> 1]);
-        }
+        const u32x2 lo = __builtin_bit_cast(u32x2, vt[n][0]);
+        const u32x2 hi = __builtin_bit_cast(u32x2, vt[n][1]);
+        const u32x4 vw = {lo.x, lo.y, hi.x, hi.y};
         acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), as_bf16x8(pw), acc[n], 0,
                                                          0, 0);
       }
     }
   }
 
+  // bf16 output of lane row q: acc block n, register r is dim 32n + rho(h, r);
+  // registers 4a..4a+3 are the 4 consecutive dims 32n + 8a + 4h + [0, 4)
+  static __device__ __forceinline__ int out_dim(int h, int n, int a) { return 32 * n + 8 * a + 4 * h; }
+  static __device__ __forceinline__ void store_out_row(bf16_t* dst, int h, const float (&o)[16][NB],
+                                                       float scale) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        u32x2 w;
+        w.x = pack_bf16x2(o[4 * a4][n] * scale, o[4 * a4 + 1][n] * scale);
+        w.y = pack_bf16x2(o[4 * a4 + 2][n] * scale, o[4 * a4 + 3][n] * scale);
+        *reinterpret_cast<u32x2*>(dst + out_dim(h, n, a4)) = w;
+      }
+  }
+
   static __device__ void run(const PrefillArgs& a) {
     extern __shared__ __align__(16) char smem[];
+    __shared__ int sh_last;
 
     const int G = a.hq / a.hkv;
-    // flat grid: kv head fastest, then request, then q tile counted from the end
+    const int n_hb = (G + 3) / 4;
+    // flat grid: kv head fastest, then request, then split, then q tile from the end
     const int kvh = blockIdx.x % a.hkv;
-    const int b = (blockIdx.x / a.hkv) % a.batch;
-    const int qrev = blockIdx.x / (a.hkv * a.batch);
+    const int rest = blockIdx.x / a.hkv;
+    const int b = rest % a.batch;
+    const int rest2 = rest / a.batch;
+    const int split = rest2 % a.max_splits;
+    const int qrev = rest2 / a.max_splits;
     const int q0 = a.cu_q[b];
     const int M = a.cu_q[b + 1] - q0;
     const int n_qtiles = (M + QT - 1) / QT;
     const int qtile = n_qtiles - 1 - qrev;
-    if (qtile < 0) return;
+    if (qtile < 0 || qtile >= a.max_qtiles) return;   // (the latter only if M > max_seqlen_q)
     const int64_t cap = static_cast<int64_t>(a.pt_stride) * a.page_size;
     const int L = static_cast<int>(min<int64_t>(max(a.kv_lens[b], 0), cap));
     const int j0 = qtile * QT;
     const int rows = min(QT, M - j0);
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int grp = wave >> 2;            // key-half group
-    const int gw = wave & 3;              // wave within the group
-    const int gt = threadIdx.x & 255;     // thread within the group
-    const int q = lane & 31;
-    const int h = lane >> 5;
-
     // keys this q tile can see: up to position L - M + j0 + rows - 1
     const int key_end = a.causal ? min(L, L - M + j0 + rows) : L;
     const int n_ktiles = key_end > 0 ? (key_end + KT - 1) / KT : 0;
-    const int half = (n_ktiles + 1) / 2;
-    const int t_begin = grp == 0 ? 0 : half;
-    const int n_my = grp == 0 ? half : n_ktiles - half;
-    const int n_iter = half;              // both groups step through the same barriers
-    const int row_ok = q < rows;
+    const int n_split = max(1, min((n_ktiles + a.split_tiles - 1) / a.split_tiles, a.max_splits));
+    if (split >= n_split) return;
+    const int t_begin = split * a.split_tiles;
+    const int t_end = (split == n_split - 1) ? n_ktiles : t_begin + a.split_tiles;
+    const int n_all = max(t_end - t_begin, 0);
+    const int n_iter = (n_all + 1) / 2;           // group 0 takes the first half
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave >> 2;
+    const int gw = wave & 3;
+    const int gb = t_begin + grp * n_iter;          // this group's first tile
+    const int n_g = grp == 0 ? n_iter : n_all - n_iter;
+    const int q = lane & 31;
+    const int h = lane >> 5;
+    const bool row_ok = q < rows && q0 + j0 + q < a.total_q;
     // keys visible to row q (rows past the tile's end compute discarded values)
     const int limit = a.causal ? min(L, L - M + j0 + q + 1) : L;
     // tiles entirely below every row's limit need no mask
     const int full_tiles = max(a.causal ? min(L, L - M + j0 + 1) : L, 0) / KT;
-    const int64_t row_bytes = static_cast<int64_t>(a.hkv) * D * 2;
-    int32_t col_off[PPT];
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) col_off[i] = kvh * D * 2 + ((gt + 256 * i) % CHUNKS_PER_ROW) * 16;
-
+    const int64_t row_bytes = static_cast<int64_t>(a.hkv) * ROW;
+    const char* kb = static_cast<const char*>(a.k) + static_cast<int64_t>(kvh) * ROW;
+    const char* vb = static_cast<const char*>(a.v) + static_cast<int64_t>(kvh) * ROW;
     const int32_t* pt_row = a.pt + static_cast<int64_t>(b) * a.pt_stride;
-    char* gbase = smem + grp * GROUP_LDS;
-    auto lds_k = [&](int i) { return gbase + 2 * i * TILE_BYTES; };
-    auto lds_v = [&](int i) { return gbase + (2 * i + 1) * TILE_BYTES; };
+    typedef __attribute__((address_space(3))) char lds_char;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)smem));
+    const uint32_t ring0 = lds0 + static_cast<uint32_t>(grp * GROUP_LDS);
 
-    for (int hb = 0; hb < (G + 3) / 4; ++hb) {
-      const int hg = 4 * hb + gw;           // this wave's head within the group
+    // per-lane offsets: copy source chunks, K and V operand reads (stage 0, t = 0)
+    int chunk_off[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int key = (gw * IPW + i) * RPB + lane / CH;
+      chunk_off[i] = swz(key, lane % CH) * 16;
+    }
+    // K operand read of k-step j: row q, chunk swz(q, 2j + h).
+    const int kbase = grp * GROUP_LDS + q * ROW;
+    // Transposed V read (s, n) of lane (G = lane/16, j = lane%16): key row
+    // 8s + 4(G/2) + j/4 (+16t), dims 32n + 16(G%2) + 4(j%4) + [0, 4).
+    int vofs[2][NB];
+    {
+      const int G = lane >> 4, j = lane & 15;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          const int row = 8 * s2 + 4 * (G >> 1) + (j >> 2);
+          const int byte = 2 * (32 * n + 16 * (G & 1) + 4 * (j & 3));
+          vofs[s2][n] = grp * GROUP_LDS + row * ROW + swz(row, byte / 16) * 16 + byte % 16;
+        }
+    }
+    for (int hb = 0; hb < n_hb; ++hb) {
+      const int hg = 4 * hb + gw;           // this wave's head within the GQA group
       const bool head_ok = hg < G;
       const int head = kvh * G + min(hg, G - 1);
 
       // Q^T operand: row q, dims 16j + 8h + [0, 8)
       u32x4 qop[NKS];
       {
-        const int row = q0 + j0 + min(q, rows - 1);
+        const int row = min(q0 + j0 + min(q, rows - 1), a.total_q - 1);
         const char* qrow = static_cast<const char*>(a.q) +
                            ((static_cast<int64_t>(row) * a.hq + head) * D) * 2;
 #pragma unroll
@@ -274,39 +356,42 @@ struct PrefillKernel {
       float m_run = neg_inf();
       float l_run = 0.f;
 
-      // ---- prologue: tile t_begin in LDS, entries of the next one in hand ----
-      Stage st;
-      int32_t raw_n[PPT];
-      if (n_my > 0) {
-        int32_t raw0[PPT];
-        fetch_raw(a, pt_row, L, t_begin, gt, raw0);
-        load_tile(a, L, t_begin, gt, row_bytes, col_off, raw0, st);
-        fetch_raw(a, pt_row, L, min(t_begin + 1, t_begin + n_my - 1), gt, raw_n);
-        store_tile(lds_k(0), lds_v(0), gt, st);
+      // ---- pipeline: tile i+2 is copied while tile i is consumed ----
+      // Before tile i is read, every copy issued before tile i+1's must have
+      // landed: at most the 2*IPW copies of tile i+1 stay in flight.
+      // entry slots of segment m: entry_lds + (m % 2) * 256 (LDS address / pointer)
+      const uint32_t entry_lds = lds0 + 2 * GROUP_LDS + wave * 512;
+      const int32_t* entry_ptr = reinterpret_cast<const int32_t*>(smem + 2 * GROUP_LDS + wave * 512);
+      auto entries_of = [&](int it) { return entry_ptr + ((it / SEG) & 1) * 64; };
+      if (n_g > 0) {
+        fetch_entries(a, pt_row, L, gb, gw, lane, entry_lds);
+        wait_vmem<0>();
+        copy_tile(a, L, gb, 0, gw, lane, entries_of(0), row_bytes, kb, vb, chunk_off, ring0);
+        if (n_g > 1)
+          copy_tile(a, L, gb + 1, 1, gw, lane, entries_of(1), row_bytes, kb, vb, chunk_off,
+                    ring0 + STAGE);
       }
-      __syncthreads();
-
       for (int it = 0; it < n_iter; ++it) {
-        const int kt = t_begin + it;
-        const bool more = it + 1 < n_my;
-        int32_t raw_nn[PPT];
-        if (more) {
-          load_tile(a, L, kt + 1, gt, row_bytes, col_off, raw_n, st);
-          fetch_raw(a, pt_row, L, min(kt + 2, t_begin + n_my - 1), gt, raw_nn);
+        if (it < n_g) {
+          if (it + 1 < n_g) wait_vmem<2 * IPW>();
+          else wait_vmem<0>();
         }
-        __builtin_amdgcn_sched_barrier(0);   // loads go out before the MFMAs
-        if (it < n_my) {
-          compute_tile(lds_k(it & 1), lds_v(it & 1), kt, kt >= full_tiles, limit, q, h,
-                       a.scale_log2, qop, acc, m_run, l_run);
+        __syncthreads();   // tile it is in LDS; stage (it + 2) % 3 is free
+        // the next segment's entries land before the wait that precedes its
+        // first copy (issued ahead of this iteration's copy)
+        if ((it + 3) % SEG == 0 && it + 3 < n_g)
+          fetch_entries(a, pt_row, L, gb + it + 3, gw, lane,
+                        entry_lds + (((it + 3) / SEG) & 1) * 256);
+        if (it + 2 < n_g)
+          copy_tile(a, L, gb + it + 2, (it + 2) % SEG, gw, lane, entries_of(it + 2), row_bytes,
+                    kb, vb, chunk_off, ring0 + ((it + 2) % NSTAGE) * STAGE);
+        if (it < n_g) {
+          const int kt = gb + it;
+          compute_tile(smem + (it % NSTAGE) * STAGE, kbase, q, vofs, kt >= full_tiles,
+                       limit - kt * KT - 4 * h, h, a.scale_log2, qop, acc, m_run, l_run);
         }
-        if (more) {
-          // buffer (it + 1) & 1 was last read before the previous barrier
-          store_tile(lds_k((it + 1) & 1), lds_v((it + 1) & 1), gt, st);
-#pragma unroll
-          for (int i = 0; i < PPT; ++i) raw_n[i] = raw_nn[i];
-        }
-        __syncthreads();
       }
+      __syncthreads();   // every wave is done with the rings
 
       // ---- merge the two key halves (group 1 -> group 0) through LDS ----
       float* mbuf = reinterpret_cast<float*>(smem) + (gw * 64 + lane) * MERGE_FLOATS;
@@ -319,76 +404,139 @@ struct PrefillKernel {
         mbuf[16 * NB + 1] = l_run;
       }
       __syncthreads();
+      float lse_val = 0.f, inv = 0.f;
       if (grp == 0) {
         const float m1 = mbuf[16 * NB];
         const float l1 = mbuf[16 * NB + 1];
-        const float M2 = fmaxf(m_run, m1);
-        const float f0 = (m_run == neg_inf()) ? 0.f : fast_exp2((m_run - M2) * a.scale_log2);
-        const float f1 = (m1 == neg_inf()) ? 0.f : fast_exp2((m1 - M2) * a.scale_log2);
-        float l_m = f0 * l_run + f1 * l1;
+        const float mm = fmaxf(m_run, m1);
+        const float f0 = (m_run == neg_inf()) ? 0.f : fast_exp2((m_run - mm) * a.scale_log2);
+        const float f1 = (m1 == neg_inf()) ? 0.f : fast_exp2((m1 - mm) * a.scale_log2);
 #pragma unroll
         for (int n = 0; n < NB; ++n)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[n][r] = f0 * acc[n][r] + f1 * mbuf[16 * n + r];
+        const float l_m = f0 * l_run + f1 * l1;
         const float l_tot = l_m + __shfl_xor(l_m, 32);
-        if (head_ok && row_ok) {
-          const int64_t row = q0 + j0 + q;
-          const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-          bf16_t* dst = static_cast<bf16_t*>(a.out) + (row * a.hq + head) * D;
+        inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        lse_val = l_tot > 0.f ? (mm * a.scale_log2 + fast_log2(l_tot)) * kLn2 : neg_inf();
+      }
+      const int64_t row = q0 + j0 + q;
+      if (n_split == 1) {
+        if (grp == 0 && head_ok && row_ok) {
+          float o[16][NB];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int dim = NB * rho(h, r);
-            if constexpr (NB == 4) {
-              u32x2 w;
-              w.x = pack_bf16x2(acc[0][r] * inv, acc[1][r] * inv);
-              w.y = pack_bf16x2(acc[2][r] * inv, acc[3][r] * inv);
-              *reinterpret_cast<u32x2*>(dst + dim) = w;
-            } else {
-              *reinterpret_cast<uint32_t*>(dst + dim) =
-                  pack_bf16x2(acc[0][r] * inv, acc[1][r] * inv);
-            }
-          }
-          if (a.lse != nullptr && h == 0) {
-            a.lse[row * a.hq + head] =
-                l_tot > 0.f ? (M2 * a.scale_log2 + fast_log2(l_tot)) * kLn2 : neg_inf();
+          for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int n = 0; n < NB; ++n) o[r][n] = acc[n][r];
+          store_out_row(static_cast<bf16_t*>(a.out) + (row * a.hq + head) * D, h, o, inv);
+          if (a.lse != nullptr && h == 0) a.lse[row * a.hq + head] = lse_val;
+        }
+        __syncthreads();   // the merge buffer is reused by the next head block
+        continue;
+      }
+
+      // partial of this split: o [split][row][head][D], lse [split][row][head],
+      // stored at device scope (see coherent_rsrc); a wave's rows of one head
+      // are a uniform base plus per-lane offsets
+      const int64_t part = static_cast<int64_t>(a.total_q) * a.hq;
+      const int64_t tile_row0 = static_cast<int64_t>(q0 + j0) * a.hq + head;
+      const uint32_t o_bytes = static_cast<uint32_t>(QT * a.hq * D * 4);
+      const uint32_t l_bytes = static_cast<uint32_t>(QT * a.hq * 4);
+      const uint32_t o_lane = static_cast<uint32_t>(q * a.hq * D * 4);
+      const uint32_t l_lane = static_cast<uint32_t>(q * a.hq * 4);
+      if (grp == 0 && head_ok && row_ok) {
+        const auto ro = coherent_rsrc(a.ws_o + (split * part + tile_row0) * D, o_bytes);
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+            store_coherent(ro, o_lane + out_dim(h, n, a4) * 4,
+                           f32x4{acc[n][4 * a4] * inv, acc[n][4 * a4 + 1] * inv,
+                                 acc[n][4 * a4 + 2] * inv, acc[n][4 * a4 + 3] * inv});
+        if (h == 0) store_coherent(coherent_rsrc(a.ws_lse + split * part + tile_row0, l_bytes),
+                                   l_lane, lse_val);
+      }
+      wait_all_vmem();
+      __syncthreads();   // every wave's partial has been written through
+      int* counter = a.counters +
+                     ((static_cast<int64_t>(b) * a.max_qtiles + qtile) * a.hkv + kvh) * n_hb + hb;
+      if (threadIdx.x == 0) sh_last = (counter_add(counter, 1) == n_split - 1);
+      __syncthreads();
+      if (!sh_last) continue;
+      // the last split of this (q tile, kv head, head block) merges all of them
+      if (grp == 0 && head_ok && row_ok) {
+        float ls[16];
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2)
+          ls[s2] = s2 < n_split ? load_coherent1(
+                                      coherent_rsrc(a.ws_lse + s2 * part + tile_row0, l_bytes),
+                                      l_lane)
+                                : neg_inf();
+        float mx = ls[0];
+#pragma unroll
+        for (int s2 = 1; s2 < 16; ++s2) mx = fmaxf(mx, ls[s2]);
+        float o[16][NB];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+          for (int n = 0; n < NB; ++n) o[r][n] = 0.f;
+        float wsum = 0.f;
+        if (mx != neg_inf()) {
+          for (int s2 = 0; s2 < n_split; ++s2) {
+            const float wgt = fast_exp2((ls[s2] - mx) * kLog2e);
+            wsum += wgt;
+            const auto ro = coherent_rsrc(a.ws_o + (s2 * part + tile_row0) * D, o_bytes);
+            f32x4 v[NB][4];   // all loads in flight before the first use
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+#pragma unroll
+              for (int a4 = 0; a4 < 4; ++a4) v[n][a4] = load_coherent4(ro, o_lane + out_dim(h, n, a4) * 4);
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+#pragma unroll
+              for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o[4 * a4 + c][n] += wgt * v[n][a4][c];
           }
         }
+        store_out_row(static_cast<bf16_t*>(a.out) + (row * a.hq + head) * D, h, o,
+                      wsum > 0.f ? 1.f / wsum : 0.f);
+        if (a.lse != nullptr && h == 0)
+          a.lse[row * a.hq + head] = (mx == neg_inf()) ? neg_inf() : mx + fast_log2(wsum) * kLn2;
       }
-      __syncthreads();   // merge buffer and tile buffers are reused by the next head slice
+      if (threadIdx.x == 0) counter_reset(counter);   // ready for the next call
     }
   }
 };
 
-template <int D, bool POW2>
+template <int D, int PM>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
-  PrefillKernel<D, POW2>::run(a);
+  PrefillKernel<D, PM>::run(a);
 }
 
 }  // namespace pkv
 
 namespace pkv_launch {
 
+template <int D, int PM>
+static void launch_prefill_t(const pkv::PrefillArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((pkv::prefill_kernel<D, PM>), grid, dim3(512),
+                     (pkv::PrefillKernel<D, PM>::LDS_BYTES), stream, a);
+}
+
+template <int D>
+static void launch_prefill_d(const pkv::PrefillArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.page_size == 1) launch_prefill_t<D, pkv::kPageToken>(a, grid, stream);
+  else if (a.page_shift >= 0) launch_prefill_t<D, pkv::kPagePow2>(a, grid, stream);
+  else launch_prefill_t<D, pkv::kPageAny>(a, grid, stream);
+}
+
 hipError_t prefill(const pkv::PrefillArgs& a, int head_dim, hipStream_t stream) {
-  const int64_t max_qtiles = (a.max_seqlen_q + 31) / 32;
-  const int64_t blocks = max_qtiles * a.hkv * a.batch;
+  const int64_t blocks = static_cast<int64_t>(a.max_qtiles) * a.max_splits * a.hkv * a.batch;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
-  const bool pow2 = a.page_shift >= 0;
-  if (head_dim == 128) {
-    if (pow2)
-      hipLaunchKernelGGL((pkv::prefill_kernel<128, true>), grid, dim3(512),
-                         (pkv::PrefillKernel<128, true>::LDS_BYTES), stream, a);
-    else
-      hipLaunchKernelGGL((pkv::prefill_kernel<128, false>), grid, dim3(512),
-                         (pkv::PrefillKernel<128, false>::LDS_BYTES), stream, a);
-  } else {
-    if (pow2)
-      hipLaunchKernelGGL((pkv::prefill_kernel<64, true>), grid, dim3(512),
-                         (pkv::PrefillKernel<64, true>::LDS_BYTES), stream, a);
-    else
-      hipLaunchKernelGGL((pkv::prefill_kernel<64, false>), grid, dim3(512),
-                         (pkv::PrefillKernel<64, false>::LDS_BYTES), stream, a);
-  }
+  if (head_dim == 128) launch_prefill_d<128>(a, grid, stream);
+  else launch_prefill_d<64>(a, grid, stream);
   return hipGetLastError();
 }
 

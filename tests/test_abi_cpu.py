@@ -18,7 +18,8 @@ EINVAL, EUNSUP = 1, 2
 def test_header_declares_the_five_entry_points():
     names = pkv.declared_symbols()
     for fn in ["build_page_table", "paged_attn_varlen_prefill", "paged_attn_decode_splitkv",
-               "merge_state", "sparse_topk_decode"]:
+               "merge_state", "sparse_topk_decode", "paged_attn_varlen_prefill_workspace_size",
+               "sparse_topk_decode_workspace_size"]:
         assert fn in names
 
 
@@ -88,12 +89,36 @@ def test_merge_and_sparse_and_prefill_argument_errors():
     assert sp(None, None, 10, None, 2, 10, None, None, 4, 1, 128, 576, 512, 0.1, None, 0, None,
               None, None) == EINVAL
     pf = lib.paged_attn_varlen_prefill
-    assert pf(None, 0, None, None, 8, None, 4, None, None, 2, 10, 5, 8, 2, 128, 1, 0.1, 1, None,
-              None, None) == EUNSUP                       # fp32 prefill not instantiated
-    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, 8, 3, 128, 1, 0.1, 1, None,
-              None, None) == EINVAL
-    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, 8, 2, 128, 1, 0.1, 2, None,
-              None, None) == EINVAL
+    # q dtype k v pages pt stride cu kl  B  Tq Mq Mk  Hq Hkv D   P  scale causal ws  bytes out lse st
+    assert pf(None, 0, None, None, 8, None, 4, None, None, 2, 10, 5, 40, 8, 2, 128, 1, 0.1, 1, None,
+              0, None, None, None) == EUNSUP                # fp32 prefill not instantiated
+    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, 40, 8, 3, 128, 1, 0.1, 1, None,
+              0, None, None, None) == EINVAL
+    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, 40, 8, 2, 128, 1, 0.1, 2, None,
+              0, None, None, None) == EINVAL
+    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, -1, 8, 2, 128, 1, 0.1, 1, None,
+              0, None, None, None) == EINVAL              # negative max_seqlen_k
+
+
+def test_prefill_workspace_plan():
+    lib = pkv.load_library()
+    size = lib.paged_attn_varlen_prefill_workspace_size
+    # enough (q tile, kv head) units to fill the GPU: no key split, no workspace
+    assert size(4, 849, 512, 1024, 32, 8, 128) == 0
+    assert size(4, 849, 512, 96, 32, 8, 128) == 0
+    # two q tiles against 8192 cached keys: split, workspace scales with total_q
+    small = size(1, 64, 64, 8192, 32, 8, 128)
+    assert small > 0
+    assert size(1, 128, 64, 8192, 32, 8, 128) > small
+    # a call that needs a workspace rejects a missing or short one before any
+    # launch (fake non-NULL pointers: validation never touches them)
+    fake = ctypes.c_void_p(256)
+    pf = lib.paged_attn_varlen_prefill
+    args = [fake, 1, fake, fake, 8192, fake, 8192, fake, fake, 1, 64, 64, 8192, 32, 8, 128, 1,
+            0.088, 1]
+    assert pf(*args, None, 0, fake, None, None) == EINVAL
+    assert pf(*args, fake, small - 1, fake, None, None) == EINVAL
+    assert b"workspace" in lib.pkv_last_error()
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

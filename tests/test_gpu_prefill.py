@@ -13,15 +13,21 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def run_case(c, causal=True):
-    """GPU page table + prefill vs the oracle, every row and head."""
+def gpu_prefill(c, causal=True, workspace=None):
     pt, kl, _ = pkv.build_page_table(c.req_to_token, c.req_pool_indices, c.seq_lens, c.page_size,
                                      c.table_width)
     out = torch.full_like(c.q, float("nan"))
     lse = torch.full(c.q.shape[:2], float("nan"), device=DEV)
     pkv.paged_attn_varlen_prefill(c.q, c.k_cache, c.v_cache, pt, c.cu_seqlens_q, kl,
-                                  c.max_seqlen_q, c.scale, causal=causal, out=out, lse=lse)
+                                  c.max_seqlen_q, c.scale, causal=causal, workspace=workspace,
+                                  out=out, lse=lse)
     torch.cuda.synchronize()
+    return out, lse, pt, kl
+
+
+def run_case(c, causal=True, workspace=None):
+    """GPU page table + prefill vs the oracle, every row and head."""
+    out, lse, pt, kl = gpu_prefill(c, causal, workspace)
     pt_np, kl_np = np_i(pt), np_i(kl)
     rows = list(range(len(kl_np)))
     k_small, pt_small = compact_pages(c.k_cache, pt_np, kl_np, c.page_size, rows)
@@ -54,6 +60,32 @@ def test_prefill_edge_shapes(D, P, group, causal):
     c = to_device(c, DEV)
     say(f"prefill D={D} P={P} G={group} causal={causal}")
     run_case(c, causal)
+
+
+# Long cached prefixes: q tiles see many key tiles and are cut into several key
+# splits merged through the workspace (G = 8 also runs two head blocks).
+@pytest.mark.parametrize("D,P,group,causal,hkv", [
+    (128, 1, 4, True, 2), (128, 16, 8, True, 2), (64, 1, 2, True, 4), (128, 64, 4, False, 2),
+    (64, 3, 16, True, 1),
+])
+def test_prefill_key_splits(D, P, group, causal, hkv):
+    prefix = [2000, 0, 777, 3100]
+    extend = [300, 1, 129, 45]
+    total = sum(p + e for p, e in zip(prefix, extend))
+    c = workloads.make_prefill_case(90 + D + P + group, prefix_lens=prefix, extend_lens=extend,
+                                    num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=D,
+                                    page_size=P, num_pages=total // P + len(prefix) + 4)
+    c = to_device(c, DEV)
+    need = pkv.paged_attn_varlen_prefill_workspace_size(
+        len(prefix), c.q.shape[0], c.max_seqlen_q, c.table_width * P, c.q.shape[1], hkv, D)
+    assert need > 0, "this shape is meant to split"
+    say(f"prefill splits D={D} P={P} G={group} Hkv={hkv} causal={causal} ws={need}")
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    a = run_case(c, causal, ws)
+    b = gpu_prefill(c, causal, ws)   # the first call left the split counters at zero
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    n_counters = len(prefix) * -(-c.max_seqlen_q // 32) * hkv * -(-group // 4)
+    assert not torch.any(ws[:4 * n_counters].view(torch.int32) != 0)
 
 
 def test_prefill_deterministic_and_page_permutation_invariant():
