@@ -118,8 +118,9 @@ pkv_status_t build_page_table(const int32_t* req_to_token, int64_t req_to_token_
  * out      [total_q, num_q_heads, head_dim] dtype (out); lse [total_q, num_q_heads]
  *          fp32 (out) or NULL.
  * Supported: dtype PKV_BF16, head_dim 64 or 128, Hq % Hkv == 0,
- * Hq / Hkv <= 16, causal 0 or 1.
- * Errors: PKV_EINVAL for bad sizes, NULL pointers or a short workspace.
+ * Hq / Hkv <= 16, causal 0 or 1, num_pages * page_size < 2^31.
+ * Errors: PKV_EINVAL for bad sizes, NULL pointers or a short workspace;
+ * PKV_EUNSUPPORTED outside the supported set.
  */
 size_t paged_attn_varlen_prefill_workspace_size(int32_t batch, int32_t total_q,
                                                 int32_t max_seqlen_q, int32_t max_seqlen_k,

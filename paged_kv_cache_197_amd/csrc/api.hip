@@ -54,7 +54,7 @@ constexpr int64_t kPrefillWorkgroups = 256;
 constexpr int64_t kMinSplitTiles = 4;
 
 struct PrefillPlan {
-  int32_t split_tiles, max_splits, max_qtiles;
+  int32_t split_tiles, max_splits, qtile_slots;
   size_t counter_bytes, lse_bytes, o_bytes, bytes;
 };
 
@@ -64,8 +64,11 @@ static PrefillPlan prefill_plan(int64_t batch, int64_t total_q, int64_t max_seql
                                 int64_t max_seqlen_k, int64_t hq, int64_t hkv, int64_t head_dim) {
   PrefillPlan p;
   const int64_t n_kt = max_seqlen_k > 0 ? (max_seqlen_k + 31) / 32 : 1;
-  p.max_qtiles = static_cast<int32_t>((max_seqlen_q + 31) / 32);
-  const int64_t qtiles = std::min<int64_t>((total_q + 31) / 32 + batch, batch * p.max_qtiles);
+  // q tiles of all requests: at most ceil(total_q / 32) + batch (and at most
+  // batch * ceil(max_seqlen_q / 32) when max_seqlen_q bounds every request)
+  const int64_t qtiles =
+      std::min<int64_t>((total_q + 31) / 32 + batch, batch * ((max_seqlen_q + 31) / 32));
+  p.qtile_slots = static_cast<int32_t>(std::min<int64_t>((total_q + 31) / 32 + batch, 1 << 30));
   const int64_t units = std::max<int64_t>(1, qtiles * hkv);
   const int64_t want = (2 * units >= kPrefillWorkgroups)
                            ? 1
@@ -79,7 +82,7 @@ static PrefillPlan prefill_plan(int64_t batch, int64_t total_q, int64_t max_seql
     return p;
   }
   const int64_t n_hb = (hq / hkv + 3) / 4;
-  p.counter_bytes = round_up256(static_cast<size_t>(batch * p.max_qtiles * hkv * n_hb) * 4);
+  p.counter_bytes = round_up256(static_cast<size_t>(p.qtile_slots * hkv * n_hb) * 4);
   p.lse_bytes = round_up256(static_cast<size_t>(p.max_splits) * total_q * hq * 4);
   p.o_bytes = static_cast<size_t>(p.max_splits) * total_q * hq * head_dim * 4;
   p.bytes = p.counter_bytes + p.lse_bytes + p.o_bytes;
@@ -276,6 +279,9 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
   PKV_REQUIRE(page_size >= 1 && pt_stride >= 1 && num_pages >= 1, PKV_EINVAL,
               "prefill: page_size %d pt_stride %d num_pages %lld", page_size, pt_stride,
               (long long)num_pages);
+  PKV_REQUIRE(num_pages * page_size <= 0x7fffffffLL, PKV_EUNSUPPORTED,
+              "prefill: a cache of %lld slots (more than 2^31)",
+              (long long)(num_pages * page_size));
   PKV_REQUIRE(causal == 0 || causal == 1, PKV_EINVAL, "prefill: causal %d", causal);
   PKV_REQUIRE(max_seqlen_q <= total_q, PKV_EINVAL, "prefill: max_seqlen_q %d > total_q %d",
               max_seqlen_q, total_q);
@@ -307,7 +313,7 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
   a.causal = causal;
   a.split_tiles = plan.split_tiles;
   a.max_splits = plan.max_splits;
-  a.max_qtiles = plan.max_qtiles;
+  a.qtile_slots = plan.qtile_slots;
   char* ws = static_cast<char*>(workspace);
   a.counters = plan.bytes ? reinterpret_cast<int32_t*>(ws) : nullptr;
   a.ws_lse = plan.bytes ? reinterpret_cast<float*>(ws + plan.counter_bytes) : nullptr;

@@ -51,10 +51,10 @@ struct PrefillArgs {
   int32_t causal;
   int32_t split_tiles;  // 32-key tiles per key split
   int32_t max_splits;   // splits per q tile (grid extent)
-  int32_t max_qtiles;   // ceil(max_seqlen_q / 32)
+  int32_t qtile_slots;  // >= the q tiles of all requests: ceil(total_q / 32) + batch, capped
   float* ws_o;          // [max_splits, total_q, Hq, D] partial outputs (max_splits > 1)
   float* ws_lse;        // [max_splits, total_q, Hq]
-  int32_t* counters;    // [batch, max_qtiles, Hkv, ceil(G / 4)], zero between calls
+  int32_t* counters;    // [qtile_slots, Hkv, ceil(G / 4)], zero between calls
   void* out;
   float* lse;
 };

@@ -68,6 +68,14 @@ __device__ __forceinline__ float sum_over_groups16(float v) {
   return v;
 }
 
+// max(v, v of lane l ^ 32) without an LDS round trip: v_permlane32_swap hands
+// each half of the wave the other half's values.
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // Make the load that produced `v` complete here: an empty asm statement that

@@ -13,8 +13,8 @@
 // groups of four waves, whose softmax states are merged through LDS at the end;
 // the two waves sharing a SIMD (one per group) hide each other's latencies.
 // Within a group wave w owns q heads w, w+4, ... of the GQA group and all four
-// share 32-key K/V tiles, copied into the group's three-stage LDS ring by
-// direct global-to-LDS loads two tiles ahead of their use. The page-table
+// share 32-key K/V tiles, copied into the group's four-stage LDS ring by
+// direct global-to-LDS loads three tiles ahead of their use. The page-table
 // entries of the 8 keys a wave copies per tile are scalar loads.
 //
 // Per wave and key tile (32x32x16 bf16 MFMA):
@@ -69,7 +69,7 @@ struct PrefillKernel {
   static constexpr int CH = ROW / 16;         // 16-byte chunks per row
   static constexpr int TILE = KT * ROW;       // one tensor's tile
   static constexpr int STAGE = 2 * TILE;      // K and V
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = 4;
   static constexpr int GROUP_LDS = NSTAGE * STAGE;
   static constexpr int ENTRY_BYTES = 8 * 2 * 256;     // 8 waves x 2 segments x 64 words
   static constexpr int LDS_BYTES = 2 * GROUP_LDS + ENTRY_BYTES;
@@ -78,7 +78,7 @@ struct PrefillKernel {
   static constexpr int KPW = IPW * RPB;       // keys per wave per tile
   static constexpr int SWZ = 256 / ROW;       // rows sharing one 64-bank span
   static constexpr int MERGE_FLOATS = 16 * NB + 2;   // acc, m, l of a lane
-  static constexpr float kRescaleLog2 = 8.f;          // see compute_tile
+  static constexpr float kRescaleLog2 = 8.f;          // see softmax_pv
   static_assert(KPW == 8, "a wave copies 8 keys of each tile");
   static_assert(4 * 64 * MERGE_FLOATS * 4 <= LDS_BYTES, "merge buffer fits the rings");
 
@@ -126,52 +126,54 @@ struct PrefillKernel {
                                                    int64_t row_bytes, const char* kb,
                                                    const char* vb, const int (&chunk_off)[IPW],
                                                    uint32_t stage_base) {
+    int32_t raws[IPW];   // both entry reads in flight together
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) raws[i] = entries[tt * 8 + i * RPB + lane / CH];
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int j = i * RPB + lane / CH;   // key 8w + j of the tile
       const int t = min(kt * KT + KPW * w + j, L - 1);
-      const int64_t page = clamp_index(entries[tt * 8 + j], a.num_pages);
-      int64_t slot;
+      const int32_t raw = raws[i];
+      // page in [0, num_pages) (num_pages * page_size < 2^31: slots fit 32 bits)
+      const uint32_t page = static_cast<uint32_t>(raw) < static_cast<uint32_t>(a.num_pages)
+                                ? static_cast<uint32_t>(raw) : 0u;
+      uint32_t slot;
       if constexpr (PM == kPageToken) slot = page;
       else if constexpr (PM == kPagePow2) slot = (page << a.page_shift) | page_off(a, t);
       else slot = page * a.page_size + page_off(a, t);
-      const int64_t off = slot * row_bytes + chunk_off[i];
+      const uint64_t off = static_cast<uint64_t>(slot) * static_cast<uint32_t>(row_bytes) +
+                           static_cast<uint32_t>(chunk_off[i]);
       const int blk = w * IPW + i;
       lds_dma16(kb + off, stage_base + blk * 1024);
       lds_dma16(vb + off, stage_base + TILE + blk * 1024);
     }
   }
 
-  // One key tile for this wave's row block: S^T, online softmax, O^T update.
-  // kbase / vbase: per-lane LDS offsets of the K and V operand rows (group
-  // ring included) from the stage's base.
-  // m_run is kept in raw score units; scale_log2 > 0 is applied inside the
-  // exponent (exp2(s * c - m * c)). Masked tiles apply the per-row key limit.
-  static __device__ __forceinline__ void compute_tile(const char* stage, int kbase, int q,
+  // K operand reads of one key tile (row q, chunk swz(q, 2j + h) for k-step j)
+  static __device__ __forceinline__ void read_k(const char* stage, int kbase, int q, int h,
+                                                u32x4 (&kw)[NKS]) {
+#pragma unroll
+    for (int j = 0; j < NKS; ++j)
+      kw[j] = *reinterpret_cast<const u32x4*>(stage + kbase + swz(q, 2 * j + h) * 16);
+  }
+
+  // Softmax of S^T for this wave's row block and the O^T update with the
+  // tile's V, software-pipelined with S^T of the next tile: its K operands
+  // (kw, already read) go through the MFMAs while the exponentials of this
+  // tile run on the VALU. Returns the next tile's S^T.
+  // m_run is a reference max in raw score units; scale_log2 > 0 is applied
+  // inside the exponent (exp2(s * c - m * c)). Masked tiles apply the per-row
+  // key limit (key kt*32 + rho(h, r) is visible iff rho(h, r) - 4h < rel).
+  static __device__ __forceinline__ f32x16 softmax_pv(f32x16 s, const char* stage_v,
                                                       const int (&vofs)[2][NB], bool masked,
                                                       int rel, int h, float scale_log2,
+                                                      const u32x4 (&kw)[NKS],
                                                       const u32x4 (&qop)[NKS], f32x16 (&acc)[NB],
                                                       float& m_run, float& l_run) {
-    constexpr int SK = 0;
-    constexpr int SV = TILE;
-    const char* smem = stage;
-    f32x16 s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    u32x4 kw[NKS];   // all K operand reads in flight before the first MFMA
-#pragma unroll
-    for (int j = 0; j < NKS; ++j)
-      kw[j] = *reinterpret_cast<const u32x4*>(smem + kbase + swz(q, 2 * j + h) * 16 + SK);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < NKS; ++j)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[j]), as_bf16x8(qop[j]), s, 0, 0, 0);
-
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = s[r];
     if (masked) {   // wave-uniform: only tiles that reach past some row's limit
-      // key kt*32 + rho(h, r) is visible iff rho(h, r) - 4h < rel
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (8 * (r >> 2) + (r & 3) >= rel) x[r] = neg_inf();
@@ -179,12 +181,12 @@ struct PrefillKernel {
     float mt = fmaxf(x[0], x[1]);
 #pragma unroll
     for (int r = 2; r < 16; ++r) mt = fmaxf(mt, x[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // m_run is a reference max: it moves only when a row's tile max exceeds it
-    // by more than kRescaleLog2 (log2 units of the scaled score). In between,
-    // the exponentials stay below 2^kRescaleLog2 and the sum and the output
-    // share the reference, so the result is unchanged while the rescale of
-    // the accumulators (64 multiplies) is skipped on almost every tile.
+    mt = max_xor32(mt);
+    // m_run moves only when a row's tile max exceeds it by more than
+    // kRescaleLog2 (log2 units of the scaled score). In between, the
+    // exponentials stay below 2^kRescaleLog2 and the sum and the output share
+    // the reference, so the result is unchanged while the rescale of the
+    // accumulators is skipped on almost every tile.
     // (-inf - -inf is NaN: a row with no visible key yet does not move.)
     const bool grow = (mt - m_run) * scale_log2 > kRescaleLog2;
     const float m_ref = grow ? mt : m_run;
@@ -192,45 +194,72 @@ struct PrefillKernel {
     const float alpha = grow ? fast_exp2((m_run - m_use) * scale_log2) : 1.f;
     const float neg_mc = -m_use * scale_log2;
     m_run = m_ref;
-    float p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(x[r], scale_log2, neg_mc));
-    float ps[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ps[i] = (p[4 * i] + p[4 * i + 1]) + (p[4 * i + 2] + p[4 * i + 3]);
-    l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     if (__any(grow)) {
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[n] *= alpha;
     }
 
+    // V^T operands (see below) of the first 16-key step, early
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((address_space(3))) char lds_char;
+    s16x4 vt[2][NB][2];
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        vt[0][n][s2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_s16x4*>((lds_char*)stage_v + vofs[s2][n]));
+
+    // next tile's S^T on the MFMA pipe, this tile's exponentials on the VALU:
+    // a few exponentials between consecutive (dependent) MFMAs, order pinned.
+    // (after the last tile the K operands are stale LDS; the result is unused)
+    f32x16 sn;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sn[r] = 0.f;
+    float p[16];
+    constexpr int PER = 16 / NKS;
+#pragma unroll
+    for (int j = 0; j < NKS; ++j) {
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[j]), as_bf16x8(qop[j]), sn, 0, 0,
+                                                    0);
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        p[PER * j + e] = fast_exp2(__builtin_fmaf(x[PER * j + e], scale_log2, neg_mc));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // second step's V^T operands
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        vt[1][n][s2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_s16x4*>((lds_char*)stage_v + vofs[s2][n] + 16 * ROW));
+    float ps[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ps[i] = (p[4 * i] + p[4 * i + 1]) + (p[4 * i + 2] + p[4 * i + 3]);
+    l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+
     // O^T block n row m = dim 32n + m. Its A operand for the 16-key step t is
     // V^T[32n + m][keys 16t + 8(e/4) + 4h + e%4], e = 0..7: two transposed
     // 8-byte LDS reads (ds_read_b64_tr_b16), each turning 16 lanes' row-major
     // 4-dim pieces of 4 keys into one dim's 4 keys per lane (vofs).
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    typedef __attribute__((address_space(3))) char lds_char;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      u32x4 pw = {pack_bf16x2(p[8 * t + 0], p[8 * t + 1]), pack_bf16x2(p[8 * t + 2], p[8 * t + 3]),
-                  pack_bf16x2(p[8 * t + 4], p[8 * t + 5]), pack_bf16x2(p[8 * t + 6], p[8 * t + 7])};
-      s16x4 vt[NB][2];
-#pragma unroll
-      for (int n = 0; n < NB; ++n)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          vt[n][s2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
-              (lds_char*)smem + vofs[s2][n] + SV + 16 * t * ROW));
+      const u32x4 pw = {pack_bf16x2(p[8 * t + 0], p[8 * t + 1]),
+                        pack_bf16x2(p[8 * t + 2], p[8 * t + 3]),
+                        pack_bf16x2(p[8 * t + 4], p[8 * t + 5]),
+                        pack_bf16x2(p[8 * t + 6], p[8 * t + 7])};
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const u32x2 lo = __builtin_bit_cast(u32x2, vt[n][0]);
-        const u32x2 hi = __builtin_bit_cast(u32x2, vt[n][1]);
+        const u32x2 lo = __builtin_bit_cast(u32x2, vt[t][n][0]);
+        const u32x2 hi = __builtin_bit_cast(u32x2, vt[t][n][1]);
         const u32x4 vw = {lo.x, lo.y, hi.x, hi.y};
         acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), as_bf16x8(pw), acc[n], 0,
                                                          0, 0);
       }
     }
+    return sn;
   }
 
   // bf16 output of lane row q: acc block n, register r is dim 32n + rho(h, r);
@@ -255,18 +284,47 @@ struct PrefillKernel {
 
     const int G = a.hq / a.hkv;
     const int n_hb = (G + 3) / 4;
-    // flat grid: kv head fastest, then request, then split, then q tile from the end
+    const int lane = threadIdx.x & 63;
+    // flat grid: kv head fastest, then split, then q-tile slot. Slots number
+    // the q tiles request by request (each request's from its last, longest
+    // one); a request with M rows has ceil(M / 32) of them, so
+    // ceil(total_q / 32) + batch slots cover all and few stay empty.
     const int kvh = blockIdx.x % a.hkv;
     const int rest = blockIdx.x / a.hkv;
-    const int b = rest % a.batch;
-    const int rest2 = rest / a.batch;
-    const int split = rest2 % a.max_splits;
-    const int qrev = rest2 / a.max_splits;
+    const int split = rest % a.max_splits;
+    const int slot = rest / a.max_splits;
+    int b = -1, qrev = 0;
+    {
+      int base = 0;   // q tiles of the requests before this chunk of 64
+      for (int c0 = 0; c0 < a.batch; c0 += 64) {
+        const int bi = c0 + lane;
+        const int nt = bi < a.batch ? max(a.cu_q[bi + 1] - a.cu_q[bi] + QT - 1, 0) / QT : 0;
+        int incl = nt;   // inclusive prefix sum over the wave
+#pragma unroll
+        for (int d = 1; d < 64; d *= 2) {
+          const int v = __shfl_up(incl, d);
+          if (lane >= d) incl += v;
+        }
+        const int first = base + incl - nt;   // slot of request bi's last q tile
+        const unsigned long long hit = __ballot(nt > 0 && slot >= first && slot < first + nt);
+        if (hit) {
+          const int l = __builtin_ctzll(hit);
+          b = c0 + l;
+          qrev = slot - __shfl(first, l);
+          break;
+        }
+        base += __shfl(incl, 63);
+      }
+    }
+    // (wave-uniform; made explicit so that everything derived stays scalar)
+    b = __builtin_amdgcn_readfirstlane(b);
+    qrev = __builtin_amdgcn_readfirstlane(qrev);
+    if (b < 0) return;   // an empty slot
     const int q0 = a.cu_q[b];
     const int M = a.cu_q[b + 1] - q0;
     const int n_qtiles = (M + QT - 1) / QT;
     const int qtile = n_qtiles - 1 - qrev;
-    if (qtile < 0 || qtile >= a.max_qtiles) return;   // (the latter only if M > max_seqlen_q)
+    if (qtile < 0) return;
     const int64_t cap = static_cast<int64_t>(a.pt_stride) * a.page_size;
     const int L = static_cast<int>(min<int64_t>(max(a.kv_lens[b], 0), cap));
     const int j0 = qtile * QT;
@@ -282,7 +340,6 @@ struct PrefillKernel {
     const int n_all = max(t_end - t_begin, 0);
     const int n_iter = (n_all + 1) / 2;           // group 0 takes the first half
 
-    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int grp = wave >> 2;
     const int gw = wave & 3;
@@ -363,32 +420,54 @@ struct PrefillKernel {
       const uint32_t entry_lds = lds0 + 2 * GROUP_LDS + wave * 512;
       const int32_t* entry_ptr = reinterpret_cast<const int32_t*>(smem + 2 * GROUP_LDS + wave * 512);
       auto entries_of = [&](int it) { return entry_ptr + ((it / SEG) & 1) * 64; };
+      // Tile i's K and V land in stage i % 4, copied three tiles ahead; tile
+      // i's softmax and O^T update run together with tile i+1's S^T, so at the
+      // top of iteration i tile i+1 must have landed: at most the 2*IPW copies
+      // of tile i+2 stay in flight.
+      f32x16 s_cur;
       if (n_g > 0) {
         fetch_entries(a, pt_row, L, gb, gw, lane, entry_lds);
         wait_vmem<0>();
-        copy_tile(a, L, gb, 0, gw, lane, entries_of(0), row_bytes, kb, vb, chunk_off, ring0);
-        if (n_g > 1)
-          copy_tile(a, L, gb + 1, 1, gw, lane, entries_of(1), row_bytes, kb, vb, chunk_off,
-                    ring0 + STAGE);
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          if (i < n_g)
+            copy_tile(a, L, gb + i, i, gw, lane, entries_of(i), row_bytes, kb, vb, chunk_off,
+                      ring0 + i * STAGE);
+        if (n_g > 2) wait_vmem<4 * IPW>();
+        else if (n_g > 1) wait_vmem<2 * IPW>();
+        else wait_vmem<0>();
+      }
+      __syncthreads();   // tile 0 is in LDS
+      if (n_g > 0) {
+        u32x4 kw[NKS];
+        read_k(smem, kbase, q, h, kw);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_cur[r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NKS; ++j)
+          s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[j]), as_bf16x8(qop[j]),
+                                                          s_cur, 0, 0, 0);
       }
       for (int it = 0; it < n_iter; ++it) {
-        if (it < n_g) {
-          if (it + 1 < n_g) wait_vmem<2 * IPW>();
+        if (it + 1 < n_g) {
+          if (it + 2 < n_g) wait_vmem<2 * IPW>();
           else wait_vmem<0>();
         }
-        __syncthreads();   // tile it is in LDS; stage (it + 2) % 3 is free
+        __syncthreads();   // tile it+1 is in LDS; stage (it + 3) % 4 is free
         // the next segment's entries land before the wait that precedes its
         // first copy (issued ahead of this iteration's copy)
-        if ((it + 3) % SEG == 0 && it + 3 < n_g)
-          fetch_entries(a, pt_row, L, gb + it + 3, gw, lane,
-                        entry_lds + (((it + 3) / SEG) & 1) * 256);
-        if (it + 2 < n_g)
-          copy_tile(a, L, gb + it + 2, (it + 2) % SEG, gw, lane, entries_of(it + 2), row_bytes,
-                    kb, vb, chunk_off, ring0 + ((it + 2) % NSTAGE) * STAGE);
+        if ((it + 4) % SEG == 0 && it + 4 < n_g)
+          fetch_entries(a, pt_row, L, gb + it + 4, gw, lane,
+                        entry_lds + (((it + 4) / SEG) & 1) * 256);
+        if (it + 3 < n_g)
+          copy_tile(a, L, gb + it + 3, (it + 3) % SEG, gw, lane, entries_of(it + 3), row_bytes,
+                    kb, vb, chunk_off, ring0 + ((it + 3) % NSTAGE) * STAGE);
         if (it < n_g) {
           const int kt = gb + it;
-          compute_tile(smem + (it % NSTAGE) * STAGE, kbase, q, vofs, kt >= full_tiles,
-                       limit - kt * KT - 4 * h, h, a.scale_log2, qop, acc, m_run, l_run);
+          u32x4 kw[NKS];
+          read_k(smem + ((it + 1) % NSTAGE) * STAGE, kbase, q, h, kw);
+          s_cur = softmax_pv(s_cur, smem + (it % NSTAGE) * STAGE + TILE, vofs, kt >= full_tiles,
+                             limit - kt * KT - 4 * h, h, a.scale_log2, kw, qop, acc, m_run, l_run);
         }
       }
       __syncthreads();   // every wave is done with the rings
@@ -459,7 +538,7 @@ struct PrefillKernel {
       wait_all_vmem();
       __syncthreads();   // every wave's partial has been written through
       int* counter = a.counters +
-                     ((static_cast<int64_t>(b) * a.max_qtiles + qtile) * a.hkv + kvh) * n_hb + hb;
+                     ((static_cast<int64_t>(slot) * a.hkv + kvh) * n_hb + hb);
       if (threadIdx.x == 0) sh_last = (counter_add(counter, 1) == n_split - 1);
       __syncthreads();
       if (!sh_last) continue;
@@ -532,7 +611,7 @@ static void launch_prefill_d(const pkv::PrefillArgs& a, dim3 grid, hipStream_t s
 }
 
 hipError_t prefill(const pkv::PrefillArgs& a, int head_dim, hipStream_t stream) {
-  const int64_t blocks = static_cast<int64_t>(a.max_qtiles) * a.max_splits * a.hkv * a.batch;
+  const int64_t blocks = static_cast<int64_t>(a.qtile_slots) * a.max_splits * a.hkv;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (head_dim == 128) launch_prefill_d<128>(a, grid, stream);

@@ -84,7 +84,8 @@ def test_prefill_key_splits(D, P, group, causal, hkv):
     a = run_case(c, causal, ws)
     b = gpu_prefill(c, causal, ws)   # the first call left the split counters at zero
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
-    n_counters = len(prefix) * -(-c.max_seqlen_q // 32) * hkv * -(-group // 4)
+    # counters: one per (q-tile slot, kv head, head block); ceil(total_q / 32) + batch slots
+    n_counters = (-(-c.q.shape[0] // 32) + len(prefix)) * hkv * -(-group // 4)
     assert not torch.any(ws[:4 * n_counters].view(torch.int32) != 0)
 
 
