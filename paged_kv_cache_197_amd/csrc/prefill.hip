@@ -293,12 +293,16 @@ struct PrefillKernel {
     const int rest = blockIdx.x / a.hkv;
     const int split = rest % a.max_splits;
     const int slot = rest / a.max_splits;
-    int b = -1, qrev = 0;
+    int b = -1, qrev = 0, q0 = 0, M = 0, Lraw = 0;
     {
       int base = 0;   // q tiles of the requests before this chunk of 64
       for (int c0 = 0; c0 < a.batch; c0 += 64) {
         const int bi = c0 + lane;
-        const int nt = bi < a.batch ? max(a.cu_q[bi + 1] - a.cu_q[bi] + QT - 1, 0) / QT : 0;
+        const bool in = bi < a.batch;
+        const int qs = in ? a.cu_q[bi] : 0;       // one round trip for all three
+        const int qe = in ? a.cu_q[bi + 1] : 0;
+        const int kl = in ? a.kv_lens[bi] : 0;
+        const int nt = in ? max(qe - qs + QT - 1, 0) / QT : 0;
         int incl = nt;   // inclusive prefix sum over the wave
 #pragma unroll
         for (int d = 1; d < 64; d *= 2) {
@@ -311,6 +315,9 @@ struct PrefillKernel {
           const int l = __builtin_ctzll(hit);
           b = c0 + l;
           qrev = slot - __shfl(first, l);
+          q0 = __shfl(qs, l);
+          M = __shfl(qe, l) - q0;
+          Lraw = __shfl(kl, l);
           break;
         }
         base += __shfl(incl, 63);
@@ -319,14 +326,15 @@ struct PrefillKernel {
     // (wave-uniform; made explicit so that everything derived stays scalar)
     b = __builtin_amdgcn_readfirstlane(b);
     qrev = __builtin_amdgcn_readfirstlane(qrev);
+    q0 = __builtin_amdgcn_readfirstlane(q0);
+    M = __builtin_amdgcn_readfirstlane(M);
+    Lraw = __builtin_amdgcn_readfirstlane(Lraw);
     if (b < 0) return;   // an empty slot
-    const int q0 = a.cu_q[b];
-    const int M = a.cu_q[b + 1] - q0;
     const int n_qtiles = (M + QT - 1) / QT;
     const int qtile = n_qtiles - 1 - qrev;
     if (qtile < 0) return;
     const int64_t cap = static_cast<int64_t>(a.pt_stride) * a.page_size;
-    const int L = static_cast<int>(min<int64_t>(max(a.kv_lens[b], 0), cap));
+    const int L = static_cast<int>(min<int64_t>(max(Lraw, 0), cap));
     const int j0 = qtile * QT;
     const int rows = min(QT, M - j0);
 
@@ -388,7 +396,10 @@ struct PrefillKernel {
       const bool head_ok = hg < G;
       const int head = kvh * G + min(hg, G - 1);
 
-      // Q^T operand: row q, dims 16j + 8h + [0, 8)
+      // the first segment's page entries and the Q^T operand (row q, dims
+      // 16j + 8h + [0, 8)) in one round trip: the wait for Q covers the entries
+      const uint32_t entry_lds = lds0 + 2 * GROUP_LDS + wave * 512;
+      if (n_g > 0) fetch_entries(a, pt_row, L, gb, gw, lane, entry_lds);
       u32x4 qop[NKS];
       {
         const int row = min(q0 + j0 + min(q, rows - 1), a.total_q - 1);
@@ -405,6 +416,7 @@ struct PrefillKernel {
           retire(qop[j].w);
         }
       }
+      wait_vmem<0>();
       f32x16 acc[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n)
@@ -417,7 +429,6 @@ struct PrefillKernel {
       // Before tile i is read, every copy issued before tile i+1's must have
       // landed: at most the 2*IPW copies of tile i+1 stay in flight.
       // entry slots of segment m: entry_lds + (m % 2) * 256 (LDS address / pointer)
-      const uint32_t entry_lds = lds0 + 2 * GROUP_LDS + wave * 512;
       const int32_t* entry_ptr = reinterpret_cast<const int32_t*>(smem + 2 * GROUP_LDS + wave * 512);
       auto entries_of = [&](int it) { return entry_ptr + ((it / SEG) & 1) * 64; };
       // Tile i's K and V land in stage i % 4, copied three tiles ahead; tile
@@ -426,8 +437,6 @@ struct PrefillKernel {
       // of tile i+2 stay in flight.
       f32x16 s_cur;
       if (n_g > 0) {
-        fetch_entries(a, pt_row, L, gb, gw, lane, entry_lds);
-        wait_vmem<0>();
 #pragma unroll
         for (int i = 0; i < 3; ++i)
           if (i < n_g)
