@@ -24,7 +24,7 @@ import time
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dense bf16
 ROOT = os.path.dirname(os.path.abspath(__file__))
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_splitkv_config3_counters.json")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_group_config3_counters.json")
 
 
 def parse_args(argv=None):
@@ -389,7 +389,7 @@ def main(argv=None):
                 "algorithmic_bytes_per_step": r["bytes"],
             },
             "roofline": {
-                "kernel": "decode_splitkv_kernel<bf16,128,uniform-page>",
+                "kernel": "decode_group_kernel<128, uniform page> (bf16)",
                 "bound": "hbm",
                 "achieved": round(achieved, 2),
                 "peak": HBM_PEAK_GBS,
