@@ -15,7 +15,8 @@
 // Within a group wave w owns q heads w, w+4, ... of the GQA group and all four
 // share 32-key K/V tiles, copied into the group's four-stage LDS ring by
 // direct global-to-LDS loads three tiles ahead of their use. The page-table
-// entries of the 8 keys a wave copies per tile are scalar loads.
+// entries of the 8 keys a wave copies per tile are themselves fetched into LDS
+// by direct loads, eight tiles at a time, well before the copies need them.
 //
 // Per wave and key tile (32x32x16 bf16 MFMA):
 //   S^T [32 keys x 32 rows] = K [32 x D] . Q^T [D x 32]        (D/16 MFMAs)
