@@ -239,7 +239,7 @@ def run_sparse(torch, pkv, workloads, args):
     out = torch.empty((B, hq, dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
     need = pkv.sparse_topk_decode_workspace_size(B, K, hq, dv)
-    ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    ws = torch.zeros((max(need, 1),), dtype=torch.uint8, device=dev)   # counters start at zero
     # a buffer larger than the 256 MB last-level cache, rewritten before each
     # timed step so the 85 MB working set is read from HBM
     flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)

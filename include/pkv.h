@@ -205,13 +205,15 @@ pkv_status_t merge_state(const float* o_parts, const float* lse_parts, int32_t n
  * topk_idx [batch, topk] int32 logical indices in [0, stride) or -1
  * workspace: device scratch of at least sparse_topk_decode_workspace_size(...)
  *          bytes (may be NULL when that size is 0). It holds per-split partial
- *          results and one completion counter per (request, 32-head block): it
+ *          results and one completion counter per (request, head block; a head
+ *          block is 64 heads when num_q_heads is a multiple of 64, else 32): it
  *          must be zero-filled before its first use, and every call that
  *          returns PKV_OK leaves the counters zero again. Calls sharing one
  *          workspace must not overlap in time (same stream, or synchronised).
  * out      [batch, num_q_heads, head_dim_v] bf16 (out); lse [batch, num_q_heads]
  *          fp32 (out) or NULL.
- * Supported: head_dim_qk 576, head_dim_v 512, num_q_heads a multiple of 32.
+ * Supported: head_dim_qk 576, head_dim_v 512, num_q_heads a multiple of 32,
+ * topk <= 131072 (PKV_EUNSUPPORTED above).
  */
 size_t sparse_topk_decode_workspace_size(int32_t batch, int32_t topk, int32_t num_q_heads,
                                          int32_t head_dim_v);

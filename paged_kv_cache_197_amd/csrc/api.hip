@@ -345,6 +345,8 @@ pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num
               "sparse_topk_decode: bad sizes batch %d topk %d heads %d", batch, topk, num_q_heads);
   PKV_REQUIRE(num_q_heads % 32 == 0, PKV_EUNSUPPORTED,
               "sparse_topk_decode: num_q_heads %d not a multiple of 32", num_q_heads);
+  PKV_REQUIRE(topk <= 131072, PKV_EUNSUPPORTED,
+              "sparse_topk_decode: topk %d above 131072 (64 key splits of 2048)", topk);
   if (batch == 0) return pkv_host::ok();
   PKV_REQUIRE(q && kv_cache && req_to_token && req_pool_indices && out, PKV_EINVAL,
               "sparse_topk_decode: NULL required pointer");

@@ -4,95 +4,123 @@
 // skipped; [NSA] _forward_fa3: score over the whole 576-wide row
 // ([c_kv 512 | k_rope 64] against [q_nope | q_rope]), value = c_kv.
 //
-// Work decomposition: one workgroup (4 waves) per (32-head block, request,
-// key split). The workgroup first translates its whole slice of the top-k
-// list into cache slots (kept in LDS), then walks it in 32-key tiles: each
-// tile's 32 rows (1152 B each) are gathered into double-buffered LDS and
-// shared by the four waves. Per tile:
-//   * QK: wave w computes a partial S^T [32 keys x 32 heads] over score dims
-//     [144w, 144w + 144) (nine 32x32x16 MFMAs) and publishes it in LDS.
+// Work decomposition: one workgroup per (head block, request, key split). A
+// head block is 64 heads (eight waves: two quads of four) when the head count
+// is a multiple of 64, else 32 heads (one quad). The workgroup translates its
+// slice of the top-k list into cache slots once (kept in LDS), then walks it
+// in 32-key tiles. A tile's 32 rows (1152 B each) are copied by direct
+// global-to-LDS loads into a three-stage ring two tiles ahead of their use,
+// and both quads work on the same tile. Per tile and quad:
+//   * QK: wave w of the quad computes a partial S^T [32 keys x 32 heads] over
+//     score dims [144w, 144w + 144) (nine 32x32x16 MFMAs, Q^T in registers)
+//     and publishes it in LDS;
 //   * softmax: wave w sums the four partials for heads [8w, 8w + 8) only, runs
 //     the online softmax for them and publishes P^T (bf16) and each head's
-//     rescale factor, so the softmax work is not repeated across waves.
+//     rescale factor, so the softmax work is not repeated across waves;
 //   * PV: wave w accumulates O^T for value dims [128w, 128w + 128) (four
 //     32x32x16 blocks x two 16-key k-steps); the value rows are the first 512
 //     dims of the same LDS tile.
+// Two workgroup barriers per tile: after QK (partials visible, every wave done
+// with the previous tile, whose stage then takes the copy of tile t + 2) and
+// after the softmax (P^T visible, tile t + 1 landed).
 // MFMA C-layout used throughout: lane (col = lane % 32, h = lane / 32) holds
 // column col (a head) and rows rho(h, r) = 8*(r/4) + 4h + r%4, r < 16 (keys
 // of S^T, dims of O^T).
+// LDS rows are unpadded; within each group of eight 16-byte chunks, chunk c of
+// row r is stored at position c ^ ((r / 2) % 8), so that the K operand reads
+// (sixteen rows, one chunk) and the V reads (one row, 256 bytes) each touch
+// every bank once.
 // Key splits (needed to fill the chip when batch x head blocks is small) are
 // merged inside the kernel: every split writes its normalised partial and LSE
-// to the workspace, and the last split to finish (device-scope counter) merges
-// them and writes the output; the counter is reset for the next call.
+// to the workspace with device-coherent stores, and the last split to finish
+// (device-scope counter) reads them back the same way, merges them and writes
+// the output; the counter is reset for the next call.
 #include "args.hpp"
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_dma.hpp"
 
 namespace pkv {
 
-struct SparseCfg {
+struct SparseGeom {
   static constexpr int DQK = 576;
   static constexpr int DV = 512;
-  static constexpr int HB = 32;                 // heads per workgroup
-  static constexpr int KT = 32;                 // keys per tile
-  static constexpr int ROW_BYTES = DQK * 2;     // 1152
-  static constexpr int LDS_STRIDE = ROW_BYTES + 16;
-  static constexpr int TILE_BYTES = KT * LDS_STRIDE;
-  static constexpr int PIECES = KT * ROW_BYTES / 16;      // 2304 16-byte pieces
-  static constexpr int PPT = PIECES / 256;                // 9 per thread
-  static constexpr int QK_SLICE = DQK / 4;      // 144 score dims per wave
-  static constexpr int QK_STEPS = QK_SLICE / 16;  // 9
-  static constexpr int DV_SLICE = DV / 4;       // 128 value dims per wave
-  static constexpr int NBLK = DV_SLICE / 32;    // 4
+  static constexpr int KT = 32;                  // keys per tile
+  static constexpr int ROW = DQK * 2;            // 1152 bytes per cache row
+  static constexpr int CH = ROW / 16;            // 72 chunks of 16 bytes
+  static constexpr int TILE = KT * ROW;          // 36864
+  static constexpr int NS = 3;                   // ring stages
+  static constexpr int DMAS = TILE / 1024;       // 1 KB copies per tile
+  static constexpr int QK_SLICE = DQK / 4;       // 144 score dims per wave
+  static constexpr int QK_STEPS = QK_SLICE / 16; // 9
+  static constexpr int DV_SLICE = DV / 4;        // 128 value dims per wave
+  static constexpr int NBLK = DV_SLICE / 32;     // 4
   static constexpr int MAX_KEYS_PER_SPLIT = 2048;   // slot list capacity in LDS
-  static constexpr int SP_BYTES = 4 * 4 * 64 * 16;  // partial S^T: [wave][quad][lane] float4
-  static constexpr int PB_BYTES = 4 * 64 * 8;       // P^T bf16: [quad][lane] 4 x bf16
+  static constexpr int MAX_SPLITS = 64;             // merge weight table capacity
+  static constexpr int MAX_TOPK = MAX_KEYS_PER_SPLIT * MAX_SPLITS;
+  static constexpr int SP_BYTES = 4 * 4 * 64 * 16;  // partial S^T: [wave][reg quad][lane] float4
+  static constexpr int PB_BYTES = 4 * 64 * 8;       // P^T bf16: [reg quad][lane] 4 x bf16
   static constexpr int AUX_BYTES = 32 * 4 * 3;      // per head: rescale factor, final m, l
-  static constexpr int LDS_BYTES =
-      2 * TILE_BYTES + SP_BYTES + PB_BYTES + AUX_BYTES + MAX_KEYS_PER_SPLIT * 4;
+  static constexpr int QUAD_BYTES = SP_BYTES + PB_BYTES + AUX_BYTES;
 };
 
-// splits per (request, head block) so the grid has about 256 workgroups, each
-// split keeping at least 128 keys; the last split may be shorter
+template <int QUADS>
+struct SparseCfg : SparseGeom {
+  static constexpr int W = 4 * QUADS;            // waves
+  static constexpr int THREADS = 64 * W;
+  static constexpr int HB = 32 * QUADS;          // heads per workgroup
+  static constexpr int DMA_PER_WAVE = (DMAS + W - 1) / W;
+  static constexpr int LDS_BYTES = NS * TILE + QUADS * QUAD_BYTES + MAX_KEYS_PER_SPLIT * 4;
+  static_assert(LDS_BYTES <= 160 * 1024, "fits the CU's LDS");
+};
+
+__host__ __device__ inline int sparse_quads(int hq) { return hq % 64 == 0 ? 2 : 1; }
+__host__ __device__ inline int sparse_head_block(int hq) { return 32 * sparse_quads(hq); }
+
+// splits per (request, head block) so the grid has about 256 workgroups (one
+// per CU), each split keeping at least 256 keys; the last split may be shorter
 __host__ __device__ inline int sparse_num_splits(int batch, int topk, int hq) {
-  const int units = batch * (hq / SparseCfg::HB);
+  const int units = batch * (hq / sparse_head_block(hq));
   if (units <= 0 || topk <= 0) return 1;
   int s = (256 + units - 1) / units;
-  const int by_keys = (topk + 127) / 128;
+  const int by_keys = (topk + 255) / 256;
   s = s < by_keys ? s : by_keys;
-  const int min_for_lds = (topk + SparseCfg::MAX_KEYS_PER_SPLIT - 1) / SparseCfg::MAX_KEYS_PER_SPLIT;
-  if (s < min_for_lds) s = min_for_lds;
+  s = s < SparseGeom::MAX_SPLITS ? s : SparseGeom::MAX_SPLITS;
+  const int min_for_lds = (topk + SparseGeom::MAX_KEYS_PER_SPLIT - 1) / SparseGeom::MAX_KEYS_PER_SPLIT;
+  if (s < min_for_lds) s = min_for_lds;   // only above MAX_TOPK, which the entry point rejects
   return s < 1 ? 1 : s;
 }
 
 __host__ __device__ inline int sparse_keys_per_split(int topk, int splits) {
   const int k = (topk + splits - 1) / splits;
-  return (k + SparseCfg::KT - 1) / SparseCfg::KT * SparseCfg::KT;
+  return (k + SparseGeom::KT - 1) / SparseGeom::KT * SparseGeom::KT;
 }
 
-struct SparseWorkspace {
-  float* o;        // [units][S][HB][DV]
-  float* lse;      // [units][S][HB]
-  int* counter;    // [units]
-};
-
-__host__ __device__ inline size_t sparse_ws_bytes(int units, int splits) {
+// workspace: o [units][S][HB][DV] fp32, lse [units][S][HB], counter [units]
+__host__ __device__ inline size_t sparse_ws_bytes(int units, int splits, int hb) {
   if (splits <= 1) return 0;
-  size_t o = static_cast<size_t>(units) * splits * SparseCfg::HB * SparseCfg::DV * 4;
-  size_t l = static_cast<size_t>(units) * splits * SparseCfg::HB * 4;
-  size_t c = static_cast<size_t>(units) * 4;
+  const size_t o = static_cast<size_t>(units) * splits * hb * SparseGeom::DV * 4;
+  const size_t l = static_cast<size_t>(units) * splits * hb * 4;
+  const size_t c = static_cast<size_t>(units) * 4;
   return o + l + c;
 }
 
 __device__ __forceinline__ int rho32(int h, int r) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+// chunk permutation of tile row r (within groups of eight chunks)
+__device__ __forceinline__ int row_swz(int r) { return (r >> 1) & 7; }
+// slot of lane L's float4 in a published partial: lanes 32..63 are moved by
+// eight slots so that the softmax reads (lane s together with lane s + 32)
+// fall in distinct banks
+__device__ __forceinline__ int sp_pos(int L) { return L ^ ((L & 32) >> 2); }
 
-__global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int splits, int kps) {
-  using C = SparseCfg;
+template <int QUADS>
+__global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a, int splits,
+                                                                     int kps) {
+  using C = SparseCfg<QUADS>;
+  typedef __attribute__((address_space(3))) char lds_char;
   extern __shared__ __align__(16) char smem[];
-  auto lds_tile = [&](int i) { return smem + i * C::TILE_BYTES; };
-  float* sp = reinterpret_cast<float*>(smem + 2 * C::TILE_BYTES);
-  int32_t* slots = reinterpret_cast<int32_t*>(smem + 2 * C::TILE_BYTES + C::SP_BYTES +
-                                              C::PB_BYTES + C::AUX_BYTES);
+  __shared__ int is_last;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)smem));
 
   const int hblocks = a.hq / C::HB;
   const int units = a.batch * hblocks;
@@ -110,85 +138,123 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
   const int unit = b * hblocks + hb;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 31;     // head within the block (B / C column)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int quad = wave >> 2;
+  const int w4 = wave & 3;
+  const int col = lane & 31;     // head within the quad (B / C column)
   const int h = lane >> 5;
+
+  char* quad_lds = smem + C::NS * C::TILE + quad * C::QUAD_BYTES;
+  float* sp = reinterpret_cast<float*>(quad_lds);
+  char* pb = quad_lds + C::SP_BYTES;
+  float* aux = reinterpret_cast<float*>(quad_lds + C::SP_BYTES + C::PB_BYTES);
+  float* alpha_buf = aux;            // [32] per-head rescale of the current tile
+  float* m_buf = aux + 32;           // [32] final running max per head (raw units)
+  float* l_buf = aux + 64;           // [32] final denominator per head
+  int32_t* slots = reinterpret_cast<int32_t*>(smem + C::NS * C::TILE + QUADS * C::QUAD_BYTES);
 
   const int k_begin = ks * kps;
   const int k_end = min(a.topk, k_begin + kps);
   const int nkeys = max(k_end - k_begin, 0);
   const int n_tiles = (nkeys + C::KT - 1) / C::KT;
 
-  // ---- translate this split's top-k entries to cache slots (-1: skip) ----
-  const int64_t r = a.rpi[b];
-  const bool row_ok = r >= 0 && r < a.r2t_rows;
-  for (int i = threadIdx.x; i < n_tiles * C::KT; i += 256) {
-    int32_t slot = -1;
-    if (i < nkeys && row_ok) {
-      const int32_t idx = a.topk_idx[static_cast<int64_t>(b) * a.topk + k_begin + i];
-      if (idx >= 0 && idx < a.r2t_stride) {
-        const int32_t s = a.r2t[r * a.r2t_stride + idx];
-        slot = (s >= 0 && s < a.num_slots) ? s : -1;
-      }
-    }
-    slots[i] = slot;
-  }
-  __syncthreads();
-
-  const char* kvb = static_cast<const char*>(a.kv);
-  u32x4 stage[C::PPT];
-  // unconditional loads (skipped keys read row 0; their LDS rows are zeroed)
-  auto load_tile = [&](int tile) {
-#pragma unroll
-    for (int i = 0; i < C::PPT; ++i) {
-      const int piece = threadIdx.x + 256 * i;
-      const int key = piece / (C::ROW_BYTES / 16);
-      const int chunk = piece % (C::ROW_BYTES / 16);
-      const int32_t sl = max(slots[tile * C::KT + key], 0);
-      stage[i] = *reinterpret_cast<const u32x4*>(kvb + static_cast<int64_t>(sl) * C::ROW_BYTES +
-                                                 chunk * 16);
-    }
-  };
-  auto store_tile = [&](char* dst, uint32_t valid) {
-    const bool all_valid = (valid == 0xffffffffu);
-#pragma unroll
-    for (int i = 0; i < C::PPT; ++i) {
-      const int piece = threadIdx.x + 256 * i;
-      const int key = piece / (C::ROW_BYTES / 16);
-      const int chunk = piece % (C::ROW_BYTES / 16);
-      u32x4 v = stage[i];
-      if (!all_valid && !((valid >> key) & 1u)) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(dst + key * C::LDS_STRIDE + chunk * 16) = v;
-    }
-  };
-  // bit k set: key k of the tile has a slot (the same mask in every wave)
-  auto tile_valid = [&](int tile) -> uint32_t {
-    const bool ok = slots[tile * C::KT + (lane & 31)] >= 0;
-    return static_cast<uint32_t>(__ballot(ok) & 0xffffffffull);
-  };
-
-  float* aux = reinterpret_cast<float*>(smem + 2 * C::TILE_BYTES + C::SP_BYTES + C::PB_BYTES);
-  float* alpha_buf = aux;            // [32] per-head rescale of the current tile
-  float* m_buf = aux + 32;           // [32] final running max per head (raw units)
-  float* l_buf = aux + 64;           // [32] final denominator per head
-  char* pb = smem + 2 * C::TILE_BYTES + C::SP_BYTES;
-
-  // Q^T operand for this wave's score slice: head col, dims 144w + 16j + 8h + [0, 8)
-  const int head = hb * C::HB + col;
+  // Q^T operand for this wave's score slice: head col of the quad, dims
+  // 144 w4 + 16j + 8h + [0, 8); in flight while the slots are translated
+  const int head = hb * C::HB + 32 * quad + col;
   u32x4 qop[C::QK_STEPS];
   {
     const char* qrow = static_cast<const char*>(a.q) +
                        (static_cast<int64_t>(b) * a.hq + head) * C::DQK * 2;
 #pragma unroll
     for (int j = 0; j < C::QK_STEPS; ++j)
-      qop[j] = *reinterpret_cast<const u32x4*>(qrow + (C::QK_SLICE * wave + 16 * j + 8 * h) * 2);
-#pragma unroll
-    for (int j = 0; j < C::QK_STEPS; ++j) {
-      retire(qop[j].x);
-      retire(qop[j].y);
-      retire(qop[j].z);
-      retire(qop[j].w);
+      qop[j] = *reinterpret_cast<const u32x4*>(qrow + (C::QK_SLICE * w4 + 16 * j + 8 * h) * 2);
+  }
+
+  // ---- translate this split's top-k entries to cache slots (-1: skip) ----
+  {
+    const int64_t r = a.rpi[b];
+    const bool row_ok = r >= 0 && r < a.r2t_rows;
+    for (int i = threadIdx.x; i < n_tiles * C::KT; i += C::THREADS) {
+      int32_t slot = -1;
+      if (i < nkeys && row_ok) {
+        const int32_t idx = a.topk_idx[static_cast<int64_t>(b) * a.topk + k_begin + i];
+        if (idx >= 0 && idx < a.r2t_stride) {
+          const int32_t s = a.r2t[r * a.r2t_stride + idx];
+          slot = (s >= 0 && s < a.num_slots) ? s : -1;
+        }
+      }
+      slots[i] = slot;
     }
+  }
+#pragma unroll
+  for (int j = 0; j < C::QK_STEPS; ++j) {
+    retire(qop[j].x);
+    retire(qop[j].y);
+    retire(qop[j].z);
+    retire(qop[j].w);
+  }
+  __syncthreads();   // slots visible
+
+  // ---- tile copies: copy i of a tile fills LDS bytes [1024 i, +1024), lane l
+  // the 16 bytes of piece p = 64 i + l: row p / 72 at position p % 72, which
+  // holds chunk (p % 72) ^ row_swz(row) of the cache row. Copy i belongs to
+  // wave i % W. Skipped keys copy row 0 and are masked in the softmax / PV.
+  const char* kvb = static_cast<const char*>(a.kv);
+  int dma_row[C::DMA_PER_WAVE];
+  uint32_t dma_off[C::DMA_PER_WAVE];
+#pragma unroll
+  for (int k = 0; k < C::DMA_PER_WAVE; ++k) {
+    const int i = min(wave + C::W * k, C::DMAS - 1);
+    const int p = 64 * i + lane;
+    const int row = p / C::CH;
+    dma_row[k] = row;
+    dma_off[k] = static_cast<uint32_t>(((p % C::CH) ^ row_swz(row)) * 16);
+  }
+  auto issue_tile = [&](int t) {
+    const uint32_t stage = lds0 + static_cast<uint32_t>((t % C::NS) * C::TILE);
+    int32_t sl[C::DMA_PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < C::DMA_PER_WAVE; ++k) sl[k] = slots[t * C::KT + dma_row[k]];
+#pragma unroll
+    for (int k = 0; k < C::DMA_PER_WAVE; ++k) {
+      const int i = wave + C::W * k;
+      if (i < C::DMAS) {
+        const uint32_t s = static_cast<uint32_t>(max(sl[k], 0));
+        lds_dma16(kvb + static_cast<uint64_t>(s) * C::ROW + dma_off[k], stage + i * 1024);
+      }
+    }
+  };
+  // wait until only the newest tile's copies of this wave are in flight
+  auto wait_older_tiles = [&]() {
+    if constexpr (C::W == 4) {
+      wait_vmem<9>();
+    } else {
+      static_assert(C::W == 8, "two quads");
+      if (wave < 4) wait_vmem<5>();
+      else wait_vmem<4>();
+    }
+  };
+  // bit k set: key k of tile t has a slot (the same mask in every wave)
+  auto tile_valid = [&](int t) -> uint32_t {
+    const bool ok = slots[t * C::KT + col] >= 0;
+    return static_cast<uint32_t>(__ballot(ok) & 0xffffffffull);
+  };
+
+  // per-lane byte offsets inside a tile
+  // K operand of k-step j: row col, chunk 18 w4 + 2j + h
+  uint32_t koff[C::QK_STEPS];
+#pragma unroll
+  for (int j = 0; j < C::QK_STEPS; ++j)
+    koff[j] = static_cast<uint32_t>(col * C::ROW + (((18 * w4 + 2 * j + h) ^ row_swz(col)) * 16));
+  // V element e of k-step 0: row 8 (e / 4) + 4h + e % 4, value dims 128 w4 +
+  // 4 col + [0, 4) (chunk 16 w4 + col / 2, byte 8 (col % 2)); k-step 1 is 16
+  // rows further (same permutation)
+  uint32_t voff[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int key = 8 * (e >> 2) + 4 * h + (e & 3);
+    voff[e] = static_cast<uint32_t>(key * C::ROW + (((16 * w4 + (col >> 1)) ^ row_swz(key)) * 16) +
+                                    8 * (col & 1));
   }
 
   f32x16 acc[C::NBLK];
@@ -197,73 +263,70 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[n][i] = 0.f;
 
-  // softmax ownership: lane L of wave w handles head sc = 8w + (L & 7), the
+  // softmax ownership: lane L of wave w4 handles head sc = 8 w4 + (L & 7), the
   // four S^T values of lane sl = sc + 32 * sh, register quad sq
-  const int sc = 8 * wave + (lane & 7);
+  const int sc = 8 * w4 + (lane & 7);
   const int sh = (lane >> 3) & 1;
   const int sq = lane >> 4;
   const int src_lane = sc + 32 * sh;
   float m_run = neg_inf();   // raw score units, for head sc
   float l_run = 0.f;         // partial denominator over this lane's keys
 
-  uint32_t valid_cur = 0xffffffffu;
-  if (n_tiles > 0) {
-    valid_cur = tile_valid(0);
-    load_tile(0);
-    store_tile(lds_tile(0), valid_cur);
+  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 1) {
+    issue_tile(1);
+    wait_older_tiles();
+  } else {
+    wait_vmem<0>();
   }
-  __syncthreads();
+  __syncthreads();   // tile 0 landed
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < n_tiles;
-    if (more) load_tile(kt + 1);
-    __builtin_amdgcn_sched_barrier(0);   // the next tile's loads go out before the MFMAs
-    const char* tile = lds_tile(buf);
+  for (int t = 0; t < n_tiles; ++t) {
+    const char* tile = smem + (t % C::NS) * C::TILE;
 
     // ---- partial S^T over this wave's 144 score dims -> LDS ----
     {
+      u32x4 kw[C::QK_STEPS];
+#pragma unroll
+      for (int j = 0; j < C::QK_STEPS; ++j) kw[j] = *reinterpret_cast<const u32x4*>(tile + koff[j]);
       f32x16 s;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = 0.f;
-      const char* krow = tile + col * C::LDS_STRIDE;     // A row: key col of the tile
 #pragma unroll
-      for (int j = 0; j < C::QK_STEPS; ++j) {
-        const u32x4 kw =
-            *reinterpret_cast<const u32x4*>(krow + (C::QK_SLICE * wave + 16 * j + 8 * h) * 2);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), as_bf16x8(qop[j]), s, 0, 0, 0);
-      }
+      for (int j = 0; j < C::QK_STEPS; ++j)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[j]), as_bf16x8(qop[j]), s, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        reinterpret_cast<float4*>(sp)[(wave * 4 + i) * 64 + lane] =
+        reinterpret_cast<float4*>(sp)[(w4 * 4 + i) * 64 + sp_pos(lane)] =
             make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
     }
-    const uint32_t valid_next = more ? tile_valid(kt + 1) : 0xffffffffu;
-    __syncthreads();   // A: partial scores visible; every wave is done with tile buf ^ 1
-    if (more) store_tile(lds_tile(buf ^ 1), valid_next);
+    const uint32_t valid = tile_valid(t);
+    __syncthreads();   // A: partials visible; every wave is done with tile t - 1
+    const bool more = t + 2 < n_tiles;
+    if (more) issue_tile(t + 2);   // into the stage of tile t - 1
 
-    // ---- softmax for heads [8w, 8w + 8): 4 keys per lane ----
+    // ---- softmax for heads [8 w4, 8 w4 + 8): 4 keys per lane ----
     {
       float x[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float4 v = reinterpret_cast<const float4*>(sp)[(w * 4 + sq) * 64 + src_lane];
+        const float4 v = reinterpret_cast<const float4*>(sp)[(w * 4 + sq) * 64 + sp_pos(src_lane)];
         x[0] += v.x;
         x[1] += v.y;
         x[2] += v.z;
         x[3] += v.w;
       }
-      if (valid_cur != 0xffffffffu) {
+      if (valid != 0xffffffffu) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {   // key of register 4*sq + j of lane half sh
           const int key = 8 * sq + 4 * sh + j;
-          if (!((valid_cur >> key) & 1u)) x[j] = neg_inf();
+          if (!((valid >> key) & 1u)) x[j] = neg_inf();
         }
       }
       float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mt = fmaxf(mt, __shfl_xor(mt, 8));
       mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_xor32(mt);
       const float m_new = fmaxf(m_run, mt);
       const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
       const float alpha = fast_exp2((m_run - m_use) * a.scale_log2);
@@ -279,7 +342,9 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
       reinterpret_cast<u32x2*>(pb)[sq * 64 + src_lane] = pw;
       if (lane < 8) alpha_buf[sc] = alpha;
     }
-    __syncthreads();   // B: P^T and rescale factors visible
+    if (more) wait_older_tiles();
+    else wait_vmem<0>();
+    __syncthreads();   // B: P^T and rescale factors visible; tile t + 1 landed
 
     // ---- O^T (this wave's 128 value dims) += V^T . P^T ----
     {
@@ -289,18 +354,26 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
         for (int n = 0; n < C::NBLK; ++n) acc[n] *= alpha_c;
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x2 p0 = reinterpret_cast<const u32x2*>(pb)[(2 * t) * 64 + lane];
-        const u32x2 p1 = reinterpret_cast<const u32x2*>(pb)[(2 * t + 1) * 64 + lane];
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const u32x2 p0 = reinterpret_cast<const u32x2*>(pb)[(2 * t2) * 64 + lane];
+        const u32x2 p1 = reinterpret_cast<const u32x2*>(pb)[(2 * t2 + 1) * 64 + lane];
         const u32x4 pw = {p0.x, p0.y, p1.x, p1.y};
         uint32_t vr[8][2];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int key = 16 * t + 8 * (e >> 2) + 4 * h + (e & 3);
-          const u32x2 w2 = *reinterpret_cast<const u32x2*>(tile + key * C::LDS_STRIDE +
-                                                            (C::DV_SLICE * wave + 4 * col) * 2);
+          const u32x2 w2 = *reinterpret_cast<const u32x2*>(tile + t2 * 16 * C::ROW + voff[e]);
           vr[e][0] = w2.x;
           vr[e][1] = w2.y;
+        }
+        if (valid != 0xffffffffu) {   // skipped keys: whatever row 0 holds must not reach O
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = 16 * t2 + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (!((valid >> key) & 1u)) {
+              vr[e][0] = 0u;
+              vr[e][1] = 0u;
+            }
+          }
         }
 #pragma unroll
         for (int n = 0; n < C::NBLK; ++n) {
@@ -321,8 +394,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
         }
       }
     }
-    valid_cur = valid_next;
-    // the next iteration's barrier A orders these reads before buf / pb / sp are rewritten
+    // the next iteration's barrier A orders these reads before sp / pb / the
+    // stage are rewritten
   }
 
   // ---- per-head totals: owners reduce their lanes' partial sums, publish ----
@@ -340,14 +413,14 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
   const float m_head = m_buf[col];
   const float l_tot = l_buf[col];
 
-  // ---- this split's result for head col, value dims 128w + 4*rho(h, i) + n ----
+  // ---- this split's result for head col, value dims 128 w4 + 4*rho(h, i) + n ----
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_val =
       l_tot > 0.f ? (m_head * a.scale_log2 + fast_log2(l_tot)) * kLn2 : neg_inf();
 
   if (splits == 1) {
     bf16_t* dst = static_cast<bf16_t*>(a.out) + (static_cast<int64_t>(b) * a.hq + head) * C::DV +
-                  C::DV_SLICE * wave;
+                  C::DV_SLICE * w4;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       u32x2 w2;
@@ -355,73 +428,117 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(SparseArgs a, int sp
       w2.y = pack_bf16x2(acc[2][i] * inv, acc[3][i] * inv);
       *reinterpret_cast<u32x2*>(dst + 4 * rho32(h, i)) = w2;
     }
-    if (a.lse != nullptr && wave == 0 && h == 0) a.lse[static_cast<int64_t>(b) * a.hq + head] = lse_val;
+    if (a.lse != nullptr && w4 == 0 && h == 0) a.lse[static_cast<int64_t>(b) * a.hq + head] = lse_val;
     return;
   }
 
-  SparseWorkspace ws;
+  // ---- hand-off through the workspace ----
+  // The normalised partial is staged in LDS as [HB][DV + 4] fp32 (the ring and
+  // exchange buffers are free now), so that it is written, and read back, in
+  // contiguous 1 KB runs: device-coherent stores go through to memory as they
+  // are issued, and scattered 16-byte pieces would each cost a memory write.
   char* wsb = static_cast<char*>(a.workspace);
-  ws.o = reinterpret_cast<float*>(wsb);
-  ws.lse = reinterpret_cast<float*>(wsb + static_cast<size_t>(units) * splits * C::HB * C::DV * 4);
-  ws.counter = reinterpret_cast<int*>(wsb + static_cast<size_t>(units) * splits * C::HB * C::DV * 4 +
-                                      static_cast<size_t>(units) * splits * C::HB * 4);
+  const int64_t n_parts = static_cast<int64_t>(units) * splits;
+  float* ws_o = reinterpret_cast<float*>(wsb);
+  float* ws_lse = reinterpret_cast<float*>(wsb + n_parts * C::HB * C::DV * 4);
+  int* counter = reinterpret_cast<int*>(wsb + n_parts * C::HB * C::DV * 4 + n_parts * C::HB * 4);
+  const int64_t part0 = static_cast<int64_t>(unit) * splits;   // this unit's first partial
+  constexpr uint32_t kPartBytes = C::HB * C::DV * 4;
+  constexpr int SROW = C::DV + 4;                  // staging row, padded (floats)
+  constexpr int F4_ROW = C::DV / 4;                // float4s per head row
+  constexpr int PASSES = C::HB * F4_ROW / C::THREADS;
+  static_assert(PASSES * C::THREADS == C::HB * F4_ROW, "whole rows per pass");
+  static_assert((C::HB * SROW + C::HB + 64 * C::HB) * 4 <= C::LDS_BYTES, "staging fits");
+  float* st_o = reinterpret_cast<float*>(smem);    // [HB][SROW]
+  float* st_lse = st_o + C::HB * SROW;             // [HB]
+  float* st_w = st_lse + C::HB;                    // [splits][HB], splits <= 64
+  __syncthreads();   // m_buf / l_buf lie in the staging area
   {
-    float* dst = ws.o + ((static_cast<int64_t>(unit) * splits + ks) * C::HB + col) * C::DV +
-                 C::DV_SLICE * wave;
+    float* row = st_o + (32 * quad + col) * SROW + C::DV_SLICE * w4;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      *reinterpret_cast<float4*>(dst + 4 * rho32(h, i)) =
-          make_float4(acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv);
-    if (wave == 0 && h == 0) ws.lse[(static_cast<int64_t>(unit) * splits + ks) * C::HB + col] = lse_val;
+      *reinterpret_cast<f32x4*>(row + 4 * rho32(h, i)) =
+          f32x4{acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
+    if (w4 == 0 && h == 0) st_lse[32 * quad + col] = lse_val;
   }
-  __threadfence();
   __syncthreads();
-  __shared__ int is_last;
-  if (threadIdx.x == 0) is_last = (atomicAdd(&ws.counter[unit], 1) == splits - 1);
+  {
+    const auto ro = coherent_rsrc(ws_o + (part0 + ks) * C::HB * C::DV, kPartBytes);
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      const int e = k * C::THREADS + static_cast<int>(threadIdx.x);   // float4 index in [HB][DV]
+      store_coherent(ro, static_cast<uint32_t>(e * 16),
+                     *reinterpret_cast<const f32x4*>(st_o + (e / F4_ROW) * SROW + 4 * (e % F4_ROW)));
+    }
+    if (threadIdx.x < C::HB)
+      store_coherent(coherent_rsrc(ws_lse + (part0 + ks) * C::HB, C::HB * 4), threadIdx.x * 4,
+                     st_lse[threadIdx.x]);
+  }
+  wait_all_vmem();
+  __syncthreads();   // every wave's part has been written through
+  if (threadIdx.x == 0) is_last = (counter_add(&counter[unit], 1) == splits - 1);
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
 
   // ---- last split: merge all splits of this (request, head block) ----
-  // thread -> (head, 64-dim segment): 32 heads x 8 segments = 256 threads
-  const int mh = threadIdx.x >> 3;
-  const int seg = (threadIdx.x & 7) * 64;
-  const float* lse_src = ws.lse + static_cast<int64_t>(unit) * splits * C::HB;
-  float m = neg_inf();
-  for (int s2 = 0; s2 < splits; ++s2) m = fmaxf(m, __builtin_nontemporal_load(lse_src + s2 * C::HB + mh));
-  float wsum = 0.f;
-  float o[64];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) o[i] = 0.f;
-  if (m != neg_inf()) {
+  // weights w_s(head) = exp(lse_s - max_s lse_s), kept in LDS; this split's
+  // own partial is read from the staging area
+  {
+    const auto rl = coherent_rsrc(ws_lse + part0 * C::HB, static_cast<uint32_t>(splits * C::HB * 4));
+    for (int i = threadIdx.x; i < splits * C::HB; i += C::THREADS)
+      st_w[i] = (i / C::HB == ks) ? st_lse[i % C::HB] : load_coherent1(rl, static_cast<uint32_t>(i * 4));
+  }
+  __syncthreads();
+  if (threadIdx.x < C::HB) {
+    const int hd = threadIdx.x;
+    float m = neg_inf();
+    for (int s2 = 0; s2 < splits; ++s2) m = fmaxf(m, st_w[s2 * C::HB + hd]);
+    float wsum = 0.f;
     for (int s2 = 0; s2 < splits; ++s2) {
-      const float w = fast_exp2((__builtin_nontemporal_load(lse_src + s2 * C::HB + mh) - m) * kLog2e);
-      if (w == 0.f) continue;
+      const float w = (m == neg_inf()) ? 0.f : fast_exp2((st_w[s2 * C::HB + hd] - m) * kLog2e);
+      st_w[s2 * C::HB + hd] = w;
       wsum += w;
-      const float* src = ws.o + ((static_cast<int64_t>(unit) * splits + s2) * C::HB + mh) * C::DV + seg;
+    }
+    if (a.lse != nullptr)
+      a.lse[static_cast<int64_t>(b) * a.hq + hb * C::HB + hd] =
+          (m == neg_inf()) ? neg_inf() : m + fast_log2(wsum) * kLn2;
+    st_lse[hd] = wsum > 0.f ? 1.f / wsum : 0.f;   // now the normaliser
+  }
+  __syncthreads();
+  f32x4 o[PASSES];
 #pragma unroll
-      for (int i = 0; i < 64; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + i);
-        o[i] += w * v.x;
-        o[i + 1] += w * v.y;
-        o[i + 2] += w * v.z;
-        o[i + 3] += w * v.w;
+  for (int k = 0; k < PASSES; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s2 = 0; s2 < splits; ++s2) {
+    f32x4 v[PASSES];   // all loads in flight before the first use
+    if (s2 == ks) {
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) {
+        const int e = k * C::THREADS + static_cast<int>(threadIdx.x);
+        v[k] = *reinterpret_cast<const f32x4*>(st_o + (e / F4_ROW) * SROW + 4 * (e % F4_ROW));
       }
+    } else {
+      const auto ro = coherent_rsrc(ws_o + (part0 + s2) * C::HB * C::DV, kPartBytes);
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k)
+        v[k] = load_coherent4(ro, static_cast<uint32_t>((k * C::THREADS + threadIdx.x) * 16));
+    }
+#pragma unroll
+    for (int k = 0; k < PASSES; ++k) {
+      const int e = k * C::THREADS + static_cast<int>(threadIdx.x);
+      o[k] += st_w[s2 * C::HB + e / F4_ROW] * v[k];
     }
   }
-  const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int ohead = hb * C::HB + mh;
-  bf16_t* dst = static_cast<bf16_t*>(a.out) + (static_cast<int64_t>(b) * a.hq + ohead) * C::DV + seg;
+  bf16_t* dst = static_cast<bf16_t*>(a.out) + (static_cast<int64_t>(b) * a.hq + hb * C::HB) * C::DV;
 #pragma unroll
-  for (int i = 0; i < 64; i += 4) {
+  for (int k = 0; k < PASSES; ++k) {
+    const int e = k * C::THREADS + static_cast<int>(threadIdx.x);
+    const float nrm = st_lse[e / F4_ROW];
     u32x2 w2;
-    w2.x = pack_bf16x2(o[i] * winv, o[i + 1] * winv);
-    w2.y = pack_bf16x2(o[i + 2] * winv, o[i + 3] * winv);
-    *reinterpret_cast<u32x2*>(dst + i) = w2;
+    w2.x = pack_bf16x2(o[k][0] * nrm, o[k][1] * nrm);
+    w2.y = pack_bf16x2(o[k][2] * nrm, o[k][3] * nrm);
+    *reinterpret_cast<u32x2*>(dst + 4 * e) = w2;
   }
-  if (a.lse != nullptr && seg == 0)
-    a.lse[static_cast<int64_t>(b) * a.hq + ohead] = (m == neg_inf()) ? neg_inf() : m + fast_log2(wsum) * kLn2;
-  if (threadIdx.x == 0) atomicExch(&ws.counter[unit], 0);   // ready for the next call
+  if (threadIdx.x == 0) counter_reset(&counter[unit]);   // ready for the next call
 }
 
 }  // namespace pkv
@@ -431,22 +548,29 @@ namespace pkv_launch {
 size_t sparse_workspace_bytes(int batch, int topk, int num_q_heads, int head_dim_v) {
   (void)head_dim_v;
   const int splits = pkv::sparse_num_splits(batch, topk, num_q_heads);
-  const int units = batch * (num_q_heads / pkv::SparseCfg::HB);
-  return pkv::sparse_ws_bytes(units, splits);
+  const int hb = pkv::sparse_head_block(num_q_heads);
+  const int units = batch * (num_q_heads / hb);
+  return pkv::sparse_ws_bytes(units, splits, hb);
 }
 
-hipError_t sparse_topk(const pkv::SparseArgs& a, hipStream_t stream) {
-  using C = pkv::SparseCfg;
+template <int QUADS>
+static hipError_t launch_sparse(const pkv::SparseArgs& a, hipStream_t stream) {
+  using C = pkv::SparseCfg<QUADS>;
   const int splits = pkv::sparse_num_splits(a.batch, a.topk, a.hq);
   const int kps = pkv::sparse_keys_per_split(a.topk, splits);
-  if (kps > C::MAX_KEYS_PER_SPLIT) return hipErrorInvalidValue;
+  if (kps > C::MAX_KEYS_PER_SPLIT || splits > C::MAX_SPLITS) return hipErrorInvalidValue;
   const int hblocks = a.hq / C::HB;
   // grid: requests rounded up to a multiple of 8 (one per XCD) x head blocks x splits
   const int64_t blocks = static_cast<int64_t>((a.batch + 7) / 8) * 8 * hblocks * splits;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(pkv::sparse_mla_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
-                     C::LDS_BYTES, stream, a, splits, kps);
+  hipLaunchKernelGGL(pkv::sparse_mla_kernel<QUADS>, dim3(static_cast<unsigned>(blocks)),
+                     dim3(C::THREADS), C::LDS_BYTES, stream, a, splits, kps);
   return hipGetLastError();
+}
+
+hipError_t sparse_topk(const pkv::SparseArgs& a, hipStream_t stream) {
+  if (pkv::sparse_quads(a.hq) == 2) return launch_sparse<2>(a, stream);
+  return launch_sparse<1>(a, stream);
 }
 
 }  // namespace pkv_launch

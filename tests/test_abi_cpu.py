@@ -88,6 +88,20 @@ def test_merge_and_sparse_and_prefill_argument_errors():
               None, None) == EUNSUP
     assert sp(None, None, 10, None, 2, 10, None, None, 4, 1, 128, 576, 512, 0.1, None, 0, None,
               None, None) == EINVAL
+    assert sp(None, None, 10, None, 2, 10, None, None, 131073, 1, 128, 576, 512, 0.1, None, 0,
+              None, None, None) == EUNSUP                 # above 64 splits x 2048 keys
+
+
+def test_sparse_workspace_plan():
+    lib = pkv.load_library()
+    size = lib.sparse_topk_decode_workspace_size
+    # 32 requests x 128 heads: 64-head blocks, 64 units, 4 key splits of 512
+    units, splits, hb = 64, 4, 64
+    assert size(32, 2048, 128, 512) == units * splits * hb * (512 + 1) * 4 + units * 4
+    # one request, 32 heads: one 32-head block, 8 splits of 256 keys
+    assert size(1, 2048, 32, 512) == 8 * 32 * (512 + 1) * 4 + 4
+    # 96 heads are three 32-head blocks; enough units for one split: no workspace
+    assert size(96, 2048, 96, 512) == 0
     pf = lib.paged_attn_varlen_prefill
     # q dtype k v pages pt stride cu kl  B  Tq Mq Mk  Hq Hkv D   P  scale causal ws  bytes out lse st
     assert pf(None, 0, None, None, 8, None, 4, None, None, 2, 10, 5, 40, 8, 2, 128, 1, 0.1, 1, None,
