@@ -26,10 +26,9 @@
 // MFMA C-layout used throughout: lane (col = lane % 32, h = lane / 32) holds
 // column col (a head) and rows rho(h, r) = 8*(r/4) + 4h + r%4, r < 16 (keys
 // of S^T, dims of O^T).
-// LDS rows are unpadded; within each group of eight 16-byte chunks, chunk c of
-// row r is stored at position c ^ ((r / 2) % 8), so that the K operand reads
-// (sixteen rows, one chunk) and the V reads (one row, 256 bytes) each touch
-// every bank once.
+// LDS rows are 1168 bytes apart (the row plus 16 bytes), which puts the
+// sixteen rows of a K operand read in distinct banks; a V read is 256
+// consecutive bytes of one row.
 // Key splits (needed to fill the chip when batch x head blocks is small) are
 // merged inside the kernel: every split writes its normalised partial and LSE
 // to the workspace with device-coherent stores, and the last split to finish
@@ -38,6 +37,7 @@
 #include "args.hpp"
 #include "common.hpp"
 #include "launch.hpp"
+#include "lanes.hpp"
 #include "lds_dma.hpp"
 
 namespace pkv {
@@ -47,10 +47,10 @@ struct SparseGeom {
   static constexpr int DV = 512;
   static constexpr int KT = 32;                  // keys per tile
   static constexpr int ROW = DQK * 2;            // 1152 bytes per cache row
-  static constexpr int CH = ROW / 16;            // 72 chunks of 16 bytes
-  static constexpr int TILE = KT * ROW;          // 36864
+  static constexpr int LROW = ROW + 16;          // LDS row stride (292 words: rows 36 banks apart)
+  static constexpr int DMAS = (KT * LROW + 1023) / 1024;   // 1 KB copies per tile (37)
+  static constexpr int TILE = DMAS * 1024;       // LDS bytes per ring stage
   static constexpr int NS = 3;                   // ring stages
-  static constexpr int DMAS = TILE / 1024;       // 1 KB copies per tile
   static constexpr int QK_SLICE = DQK / 4;       // 144 score dims per wave
   static constexpr int QK_STEPS = QK_SLICE / 16; // 9
   static constexpr int DV_SLICE = DV / 4;        // 128 value dims per wave
@@ -58,6 +58,7 @@ struct SparseGeom {
   static constexpr int MAX_KEYS_PER_SPLIT = 2048;   // slot list capacity in LDS
   static constexpr int MAX_SPLITS = 64;             // merge weight table capacity
   static constexpr int MAX_TOPK = MAX_KEYS_PER_SPLIT * MAX_SPLITS;
+  static constexpr float kRescaleLog2 = 8.f;     // lazy rescale bound (log2 units)
   static constexpr int SP_BYTES = 4 * 4 * 64 * 16;  // partial S^T: [wave][reg quad][lane] float4
   static constexpr int PB_BYTES = 4 * 64 * 8;       // P^T bf16: [reg quad][lane] 4 x bf16
   static constexpr int AUX_BYTES = 32 * 4 * 3;      // per head: rescale factor, final m, l
@@ -69,7 +70,7 @@ struct SparseCfg : SparseGeom {
   static constexpr int W = 4 * QUADS;            // waves
   static constexpr int THREADS = 64 * W;
   static constexpr int HB = 32 * QUADS;          // heads per workgroup
-  static constexpr int DMA_PER_WAVE = (DMAS + W - 1) / W;
+  static constexpr int COPIES = (DMAS + 3) / 4;   // copies per tile of each copying wave
   static constexpr int LDS_BYTES = NS * TILE + QUADS * QUAD_BYTES + MAX_KEYS_PER_SPLIT * 4;
   static_assert(LDS_BYTES <= 160 * 1024, "fits the CU's LDS");
 };
@@ -96,18 +97,16 @@ __host__ __device__ inline int sparse_keys_per_split(int topk, int splits) {
   return (k + SparseGeom::KT - 1) / SparseGeom::KT * SparseGeom::KT;
 }
 
-// workspace: o [units][S][HB][DV] fp32, lse [units][S][HB], counter [units]
+// workspace: o [units][S][HB][DV] bf16, lse [units][S][HB] fp32, counter [units]
 __host__ __device__ inline size_t sparse_ws_bytes(int units, int splits, int hb) {
   if (splits <= 1) return 0;
-  const size_t o = static_cast<size_t>(units) * splits * hb * SparseGeom::DV * 4;
+  const size_t o = static_cast<size_t>(units) * splits * hb * SparseGeom::DV * 2;
   const size_t l = static_cast<size_t>(units) * splits * hb * 4;
   const size_t c = static_cast<size_t>(units) * 4;
   return o + l + c;
 }
 
 __device__ __forceinline__ int rho32(int h, int r) { return 8 * (r >> 2) + 4 * h + (r & 3); }
-// chunk permutation of tile row r (within groups of eight chunks)
-__device__ __forceinline__ int row_swz(int r) { return (r >> 1) & 7; }
 // slot of lane L's float4 in a published partial: lanes 32..63 are moved by
 // eight slots so that the softmax reads (lane s together with lane s + 32)
 // fall in distinct banks
@@ -195,44 +194,46 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
   }
   __syncthreads();   // slots visible
 
-  // ---- tile copies: copy i of a tile fills LDS bytes [1024 i, +1024), lane l
-  // the 16 bytes of piece p = 64 i + l: row p / 72 at position p % 72, which
-  // holds chunk (p % 72) ^ row_swz(row) of the cache row. Copy i belongs to
-  // wave i % W. Skipped keys copy row 0 and are masked in the softmax / PV.
+  // ---- tile copies: copy i of a tile fills LDS bytes [1024 i, +1024) of the
+  // stage, lane l the 16 bytes at o = 1024 i + 16 l: row o / 1168, chunk
+  // (o % 1168) / 16 of the cache row. Lanes that land in a row's 16-byte pad
+  // or past the last row copy chunk 0 of row 31, which nothing reads. The
+  // copies are issued by the waves of the last quad (copy i by its wave i % 4),
+  // which spend the interval in which they are issued on the softmax. Skipped
+  // keys copy row 0 and are masked in the softmax / PV.
   const char* kvb = static_cast<const char*>(a.kv);
-  int dma_row[C::DMA_PER_WAVE];
-  uint32_t dma_off[C::DMA_PER_WAVE];
-#pragma unroll
-  for (int k = 0; k < C::DMA_PER_WAVE; ++k) {
-    const int i = min(wave + C::W * k, C::DMAS - 1);
-    const int p = 64 * i + lane;
-    const int row = p / C::CH;
-    dma_row[k] = row;
-    dma_off[k] = static_cast<uint32_t>(((p % C::CH) ^ row_swz(row)) * 16);
-  }
+  const bool copier = (quad == QUADS - 1);
   auto issue_tile = [&](int t) {
     const uint32_t stage = lds0 + static_cast<uint32_t>((t % C::NS) * C::TILE);
-    int32_t sl[C::DMA_PER_WAVE];
+    // the addresses are cheap to recompute; an opaque lane offset keeps the
+    // compiler from hoisting all of them out of the loop into registers
+    int l16 = 16 * lane;
+    asm volatile("" : "+v"(l16));
+    int32_t sl[C::COPIES];
+    uint32_t off[C::COPIES];
 #pragma unroll
-    for (int k = 0; k < C::DMA_PER_WAVE; ++k) sl[k] = slots[t * C::KT + dma_row[k]];
+    for (int k = 0; k < C::COPIES; ++k) {
+      const int i = min(w4 + 4 * k, C::DMAS - 1);
+      const int o = 1024 * i + l16;
+      const int row = min(o / C::LROW, C::KT - 1);
+      const int cb = o - row * C::LROW;
+      off[k] = static_cast<uint32_t>(cb < C::ROW ? cb : 0);
+      sl[k] = slots[t * C::KT + row];
+    }
 #pragma unroll
-    for (int k = 0; k < C::DMA_PER_WAVE; ++k) {
-      const int i = wave + C::W * k;
+    for (int k = 0; k < C::COPIES; ++k) {
+      const int i = w4 + 4 * k;
       if (i < C::DMAS) {
         const uint32_t s = static_cast<uint32_t>(max(sl[k], 0));
-        lds_dma16(kvb + static_cast<uint64_t>(s) * C::ROW + dma_off[k], stage + i * 1024);
+        lds_dma16(kvb + static_cast<uint64_t>(s) * C::ROW + off[k], stage + i * 1024);
       }
     }
   };
-  // wait until only the newest tile's copies of this wave are in flight
-  auto wait_older_tiles = [&]() {
-    if constexpr (C::W == 4) {
-      wait_vmem<9>();
-    } else {
-      static_assert(C::W == 8, "two quads");
-      if (wave < 4) wait_vmem<5>();
-      else wait_vmem<4>();
-    }
+  // copier waves: wait until only the newest tile's copies are in flight
+  auto wait_newest_tile = [&]() {
+    static_assert(C::COPIES == 10 && C::DMAS == 37, "copy counts below");
+    if (w4 == 0) wait_vmem<10>();
+    else wait_vmem<9>();
   };
   // bit k set: key k of tile t has a slot (the same mask in every wave)
   auto tile_valid = [&](int t) -> uint32_t {
@@ -241,21 +242,11 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
   };
 
   // per-lane byte offsets inside a tile
-  // K operand of k-step j: row col, chunk 18 w4 + 2j + h
-  uint32_t koff[C::QK_STEPS];
-#pragma unroll
-  for (int j = 0; j < C::QK_STEPS; ++j)
-    koff[j] = static_cast<uint32_t>(col * C::ROW + (((18 * w4 + 2 * j + h) ^ row_swz(col)) * 16));
-  // V element e of k-step 0: row 8 (e / 4) + 4h + e % 4, value dims 128 w4 +
-  // 4 col + [0, 4) (chunk 16 w4 + col / 2, byte 8 (col % 2)); k-step 1 is 16
-  // rows further (same permutation)
-  uint32_t voff[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int key = 8 * (e >> 2) + 4 * h + (e & 3);
-    voff[e] = static_cast<uint32_t>(key * C::ROW + (((16 * w4 + (col >> 1)) ^ row_swz(key)) * 16) +
-                                    8 * (col & 1));
-  }
+  // K operand of k-step j: row col, dims 144 w4 + 16 j + 8h + [0, 8)
+  const uint32_t kbase = static_cast<uint32_t>(col * C::LROW + (C::QK_SLICE * w4 + 8 * h) * 2);
+  // V element e of k-step t2: row 16 t2 + 8 (e / 4) + 4h + e % 4, value dims
+  // 128 w4 + 4 col + [0, 4)
+  const uint32_t vbase = static_cast<uint32_t>(4 * h * C::LROW + (C::DV_SLICE * w4 + 4 * col) * 2);
 
   f32x16 acc[C::NBLK];
 #pragma unroll
@@ -272,130 +263,160 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
   float m_run = neg_inf();   // raw score units, for head sc
   float l_run = 0.f;         // partial denominator over this lane's keys
 
-  if (n_tiles > 0) issue_tile(0);
-  if (n_tiles > 1) {
-    issue_tile(1);
-    wait_older_tiles();
-  } else {
-    wait_vmem<0>();
+  // Schedule per tile t (two workgroup barriers):
+  //   QK(t) -> partials;  A;  copy of tile t + 2 (into the stage of t - 1);
+  //   softmax(t) -> P^T;  B (tile t + 1 has landed);  PV(t), with the K
+  //   operands of tile t + 1 read alongside its V reads.
+  u32x4 kw[C::QK_STEPS];
+  auto read_k = [&](int t) {
+    const char* tile = smem + (t % C::NS) * C::TILE;
+#pragma unroll
+    for (int j = 0; j < C::QK_STEPS; ++j)
+      kw[j] = *reinterpret_cast<const u32x4*>(tile + kbase + 32 * j);
+  };
+
+  // partial S^T over this wave's 144 score dims (K operands in kw) -> LDS
+  auto qk = [&]() {
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < C::QK_STEPS; ++j)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[j]), as_bf16x8(qop[j]), s, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      reinterpret_cast<float4*>(sp)[(w4 * 4 + i) * 64 + sp_pos(lane)] =
+          make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
+  };
+
+  // softmax for heads [8 w4, 8 w4 + 8): 4 keys per lane; publishes P^T and
+  // each head's rescale factor
+  auto softmax = [&](uint32_t valid) {
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 v = reinterpret_cast<const float4*>(sp)[(w * 4 + sq) * 64 + sp_pos(src_lane)];
+      x[0] += v.x;
+      x[1] += v.y;
+      x[2] += v.z;
+      x[3] += v.w;
+    }
+    if (valid != 0xffffffffu) {
+      // register 4*sq + j of lane half sh holds key 8 sq + 4 sh + j
+      const uint32_t vb = valid >> (8 * sq + 4 * sh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (!(vb & (1u << j))) x[j] = neg_inf();
+    }
+    // the eight lanes of head sc differ in lane bits 3..5
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mt = max_xor8(mt);
+    mt = max_xor16(mt);
+    mt = max_xor32(mt);
+    // the reference max moves only when the tile max exceeds it by more than
+    // 2^kRescaleLog2 in exponential units; in between the exponentials stay
+    // below that bound and the sum and the output share the stale reference,
+    // which the final normalisation cancels
+    const bool grow = (mt - m_run) * a.scale_log2 > C::kRescaleLog2;
+    const float m_ref = grow ? mt : m_run;
+    const float m_use = (m_ref == neg_inf()) ? 0.f : m_ref;
+    const float alpha = grow ? fast_exp2((m_run - m_use) * a.scale_log2) : 1.f;
+    const float neg_mc = -m_use * a.scale_log2;
+    m_run = m_ref;
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = fast_exp2(__builtin_fmaf(x[j], a.scale_log2, neg_mc));
+    l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+    u32x2 pw;
+    pw.x = pack_bf16x2(p[0], p[1]);
+    pw.y = pack_bf16x2(p[2], p[3]);
+    reinterpret_cast<u32x2*>(pb)[sq * 64 + src_lane] = pw;
+    if (lane < 8) alpha_buf[sc] = alpha;
+  };
+
+  // O^T (this wave's 128 value dims) += V^T . P^T for tile t; with `next`,
+  // the K operands of tile t + 1 are read together with this tile's V
+  auto pv = [&](int t, uint32_t valid, bool next) {
+    const char* tile = smem + (t % C::NS) * C::TILE;
+    const float alpha_c = alpha_buf[col];
+    u32x2 pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = reinterpret_cast<const u32x2*>(pb)[i * 64 + lane];
+    u32x2 vr[2][8];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vr[t2][e] = *reinterpret_cast<const u32x2*>(
+            tile + vbase + (16 * t2 + 8 * (e >> 2) + (e & 3)) * C::LROW);
+    if (next) read_k(t + 1);
+    if (__any(alpha_c != 1.f)) {   // some head's reference max moved
+#pragma unroll
+      for (int n = 0; n < C::NBLK; ++n) acc[n] *= alpha_c;
+    }
+    if (valid != 0xffffffffu) {   // skipped keys: whatever row 0 holds must not reach O
+      const uint32_t vb = valid >> (4 * h);   // element e of k-step t2: key 16 t2 + 8 (e/4) + 4h + e%4
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!(vb & (1u << (16 * t2 + 8 * (e >> 2) + (e & 3))))) vr[t2][e] = u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const u32x4 pw = {pr[2 * t2].x, pr[2 * t2].y, pr[2 * t2 + 1].x, pr[2 * t2 + 1].y};
+#pragma unroll
+      for (int n = 0; n < C::NBLK; ++n) {
+        const int hw = n >> 1;
+        u32x4 vw;
+        if ((n & 1) == 0) {
+          vw.x = pair_lo(vr[t2][0][hw], vr[t2][1][hw]);
+          vw.y = pair_lo(vr[t2][2][hw], vr[t2][3][hw]);
+          vw.z = pair_lo(vr[t2][4][hw], vr[t2][5][hw]);
+          vw.w = pair_lo(vr[t2][6][hw], vr[t2][7][hw]);
+        } else {
+          vw.x = pair_hi(vr[t2][0][hw], vr[t2][1][hw]);
+          vw.y = pair_hi(vr[t2][2][hw], vr[t2][3][hw]);
+          vw.z = pair_hi(vr[t2][4][hw], vr[t2][5][hw]);
+          vw.w = pair_hi(vr[t2][6][hw], vr[t2][7][hw]);
+        }
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), as_bf16x8(pw), acc[n], 0,
+                                                         0, 0);
+      }
+    }
+  };
+
+  if (copier) {
+    if (n_tiles > 0) issue_tile(0);
+    if (n_tiles > 1) {
+      issue_tile(1);
+      wait_newest_tile();
+    } else {
+      wait_vmem<0>();
+    }
   }
   __syncthreads();   // tile 0 landed
+  uint32_t valid_cur = 0xffffffffu;   // key mask of tile t
+  if (n_tiles > 0) {
+    read_k(0);
+    valid_cur = tile_valid(0);
+  }
 
   for (int t = 0; t < n_tiles; ++t) {
-    const char* tile = smem + (t % C::NS) * C::TILE;
-
-    // ---- partial S^T over this wave's 144 score dims -> LDS ----
-    {
-      u32x4 kw[C::QK_STEPS];
-#pragma unroll
-      for (int j = 0; j < C::QK_STEPS; ++j) kw[j] = *reinterpret_cast<const u32x4*>(tile + koff[j]);
-      f32x16 s;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = 0.f;
-#pragma unroll
-      for (int j = 0; j < C::QK_STEPS; ++j)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[j]), as_bf16x8(qop[j]), s, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        reinterpret_cast<float4*>(sp)[(w4 * 4 + i) * 64 + sp_pos(lane)] =
-            make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
-    }
-    const uint32_t valid = tile_valid(t);
+    qk();
     __syncthreads();   // A: partials visible; every wave is done with tile t - 1
     const bool more = t + 2 < n_tiles;
-    if (more) issue_tile(t + 2);   // into the stage of tile t - 1
-
-    // ---- softmax for heads [8 w4, 8 w4 + 8): 4 keys per lane ----
-    {
-      float x[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float4 v = reinterpret_cast<const float4*>(sp)[(w * 4 + sq) * 64 + sp_pos(src_lane)];
-        x[0] += v.x;
-        x[1] += v.y;
-        x[2] += v.z;
-        x[3] += v.w;
-      }
-      if (valid != 0xffffffffu) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {   // key of register 4*sq + j of lane half sh
-          const int key = 8 * sq + 4 * sh + j;
-          if (!((valid >> key) & 1u)) x[j] = neg_inf();
-        }
-      }
-      float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mt = fmaxf(mt, __shfl_xor(mt, 8));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = max_xor32(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * a.scale_log2);
-      const float neg_mc = -m_use * a.scale_log2;
-      m_run = m_new;
-      float p[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = fast_exp2(__builtin_fmaf(x[j], a.scale_log2, neg_mc));
-      l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-      u32x2 pw;
-      pw.x = pack_bf16x2(p[0], p[1]);
-      pw.y = pack_bf16x2(p[2], p[3]);
-      reinterpret_cast<u32x2*>(pb)[sq * 64 + src_lane] = pw;
-      if (lane < 8) alpha_buf[sc] = alpha;
+    if (copier && more) issue_tile(t + 2);
+    softmax(valid_cur);
+    if (copier) {
+      if (more) wait_newest_tile();
+      else wait_vmem<0>();
     }
-    if (more) wait_older_tiles();
-    else wait_vmem<0>();
     __syncthreads();   // B: P^T and rescale factors visible; tile t + 1 landed
-
-    // ---- O^T (this wave's 128 value dims) += V^T . P^T ----
-    {
-      const float alpha_c = alpha_buf[col];
-      if (__any(alpha_c != 1.f)) {   // rescale only when some head's running max moved
-#pragma unroll
-        for (int n = 0; n < C::NBLK; ++n) acc[n] *= alpha_c;
-      }
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const u32x2 p0 = reinterpret_cast<const u32x2*>(pb)[(2 * t2) * 64 + lane];
-        const u32x2 p1 = reinterpret_cast<const u32x2*>(pb)[(2 * t2 + 1) * 64 + lane];
-        const u32x4 pw = {p0.x, p0.y, p1.x, p1.y};
-        uint32_t vr[8][2];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const u32x2 w2 = *reinterpret_cast<const u32x2*>(tile + t2 * 16 * C::ROW + voff[e]);
-          vr[e][0] = w2.x;
-          vr[e][1] = w2.y;
-        }
-        if (valid != 0xffffffffu) {   // skipped keys: whatever row 0 holds must not reach O
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = 16 * t2 + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (!((valid >> key) & 1u)) {
-              vr[e][0] = 0u;
-              vr[e][1] = 0u;
-            }
-          }
-        }
-#pragma unroll
-        for (int n = 0; n < C::NBLK; ++n) {
-          u32x4 vw;
-          if ((n & 1) == 0) {
-            vw.x = pair_lo(vr[0][n >> 1], vr[1][n >> 1]);
-            vw.y = pair_lo(vr[2][n >> 1], vr[3][n >> 1]);
-            vw.z = pair_lo(vr[4][n >> 1], vr[5][n >> 1]);
-            vw.w = pair_lo(vr[6][n >> 1], vr[7][n >> 1]);
-          } else {
-            vw.x = pair_hi(vr[0][n >> 1], vr[1][n >> 1]);
-            vw.y = pair_hi(vr[2][n >> 1], vr[3][n >> 1]);
-            vw.z = pair_hi(vr[4][n >> 1], vr[5][n >> 1]);
-            vw.w = pair_hi(vr[6][n >> 1], vr[7][n >> 1]);
-          }
-          acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), as_bf16x8(pw), acc[n], 0,
-                                                           0, 0);
-        }
-      }
-    }
-    // the next iteration's barrier A orders these reads before sp / pb / the
-    // stage are rewritten
+    const uint32_t valid_pv = valid_cur;
+    pv(t, valid_pv, t + 1 < n_tiles);
+    if (t + 1 < n_tiles) valid_cur = tile_valid(t + 1);
+    // the next barrier A orders these reads before sp / pb / the stage are rewritten
   }
 
   // ---- per-head totals: owners reduce their lanes' partial sums, publish ----
@@ -435,15 +456,17 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
   // ---- hand-off through the workspace ----
   // The normalised partial is staged in LDS as [HB][DV + 4] fp32 (the ring and
   // exchange buffers are free now), so that it is written, and read back, in
-  // contiguous 1 KB runs: device-coherent stores go through to memory as they
-  // are issued, and scattered 16-byte pieces would each cost a memory write.
+  // contiguous runs: device-coherent stores go through to memory as they are
+  // issued, and scattered pieces would each cost a memory write. Other splits'
+  // partials travel as bf16 (the output precision); the merging split keeps
+  // its own in fp32.
   char* wsb = static_cast<char*>(a.workspace);
   const int64_t n_parts = static_cast<int64_t>(units) * splits;
-  float* ws_o = reinterpret_cast<float*>(wsb);
-  float* ws_lse = reinterpret_cast<float*>(wsb + n_parts * C::HB * C::DV * 4);
-  int* counter = reinterpret_cast<int*>(wsb + n_parts * C::HB * C::DV * 4 + n_parts * C::HB * 4);
+  bf16_t* ws_o = reinterpret_cast<bf16_t*>(wsb);
+  float* ws_lse = reinterpret_cast<float*>(wsb + n_parts * C::HB * C::DV * 2);
+  int* counter = reinterpret_cast<int*>(wsb + n_parts * C::HB * C::DV * 2 + n_parts * C::HB * 4);
   const int64_t part0 = static_cast<int64_t>(unit) * splits;   // this unit's first partial
-  constexpr uint32_t kPartBytes = C::HB * C::DV * 4;
+  constexpr uint32_t kPartBytes = C::HB * C::DV * 2;
   constexpr int SROW = C::DV + 4;                  // staging row, padded (floats)
   constexpr int F4_ROW = C::DV / 4;                // float4s per head row
   constexpr int PASSES = C::HB * F4_ROW / C::THREADS;
@@ -466,9 +489,10 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
     const auto ro = coherent_rsrc(ws_o + (part0 + ks) * C::HB * C::DV, kPartBytes);
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {
-      const int e = k * C::THREADS + static_cast<int>(threadIdx.x);   // float4 index in [HB][DV]
-      store_coherent(ro, static_cast<uint32_t>(e * 16),
-                     *reinterpret_cast<const f32x4*>(st_o + (e / F4_ROW) * SROW + 4 * (e % F4_ROW)));
+      const int e = k * C::THREADS + static_cast<int>(threadIdx.x);   // 4-dim group in [HB][DV]
+      const f32x4 v = *reinterpret_cast<const f32x4*>(st_o + (e / F4_ROW) * SROW + 4 * (e % F4_ROW));
+      const u32x2 w2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      store_coherent(ro, static_cast<uint32_t>(e * 8), __builtin_bit_cast(f32x2_t, w2));
     }
     if (threadIdx.x < C::HB)
       store_coherent(coherent_rsrc(ws_lse + (part0 + ks) * C::HB, C::HB * 4), threadIdx.x * 4,
@@ -518,9 +542,14 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
       }
     } else {
       const auto ro = coherent_rsrc(ws_o + (part0 + s2) * C::HB * C::DV, kPartBytes);
+      u32x2 w2[PASSES];
 #pragma unroll
       for (int k = 0; k < PASSES; ++k)
-        v[k] = load_coherent4(ro, static_cast<uint32_t>((k * C::THREADS + threadIdx.x) * 16));
+        w2[k] = __builtin_bit_cast(u32x2,
+                                   load_coherent2(ro, static_cast<uint32_t>((k * C::THREADS + threadIdx.x) * 8)));
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k)
+        v[k] = f32x4{bf16lo(w2[k].x), bf16hi(w2[k].x), bf16lo(w2[k].y), bf16hi(w2[k].y)};
     }
 #pragma unroll
     for (int k = 0; k < PASSES; ++k) {

@@ -97,9 +97,10 @@ def test_sparse_workspace_plan():
     size = lib.sparse_topk_decode_workspace_size
     # 32 requests x 128 heads: 64-head blocks, 64 units, 4 key splits of 512
     units, splits, hb = 64, 4, 64
-    assert size(32, 2048, 128, 512) == units * splits * hb * (512 + 1) * 4 + units * 4
+    # partials: bf16 [HB][512] + fp32 LSE [HB] per (unit, split); one counter per unit
+    assert size(32, 2048, 128, 512) == units * splits * hb * (512 * 2 + 4) + units * 4
     # one request, 32 heads: one 32-head block, 8 splits of 256 keys
-    assert size(1, 2048, 32, 512) == 8 * 32 * (512 + 1) * 4 + 4
+    assert size(1, 2048, 32, 512) == 8 * 32 * (512 * 2 + 4) + 4
     # 96 heads are three 32-head blocks; enough units for one split: no workspace
     assert size(96, 2048, 96, 512) == 0
     pf = lib.paged_attn_varlen_prefill
