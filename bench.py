@@ -32,7 +32,8 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--only", choices=["all", "decode", "prefill", "swa", "sparse", "copy"],
+    p.add_argument("--only", choices=["all", "decode", "prefill", "prefill_long", "swa", "sparse",
+                                      "copy"],
                    default="all", help="restrict to one workload (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -198,9 +199,9 @@ def run_swa(torch, pkv, workloads, args):
                 sum_kv_len=sum_l, splits=S)
 
 
-def run_prefill(torch, pkv, workloads, args):
+def run_prefill(torch, pkv, workloads, args, make_case=None):
     dev = torch.device("cuda:0")
-    c = workloads.config2(value_device=dev)
+    c = (make_case or workloads.config2)(value_device=dev)
     r2t, rpi, sl, cu = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev),
                         c.cu_seqlens_q.to(dev))
     B = sl.numel()
@@ -435,6 +436,21 @@ def main(argv=None):
                 "visible_pairs_per_head": r["pairs"]}
         except Exception as e:
             extra["prefill"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "prefill_long"):
+        try:
+            r = run_prefill(torch, pkv, workloads, args, workloads.long_prompt_prefill)
+            tf = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+            extra["prefill_long"] = {
+                "workload": "long prompts (steady state of the prefill kernel, beside config2): "
+                            "4 requests x 4096 new tokens, no prefix, 32 q / 8 kv heads, D=128, "
+                            "page 1",
+                "kernel_ms": round(r["kernel_ms"], 5), "device_ms_per_step": round(r["ms"], 5),
+                "TFLOP/s": round(tf, 2), "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS,
+                "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": r["flops"]}
+        except Exception as e:
+            extra["prefill_long"] = {"error": repr(e)}
         torch.cuda.empty_cache()
 
     if args.only in ("all", "sparse"):

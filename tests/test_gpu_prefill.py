@@ -107,3 +107,29 @@ def test_prefill_deterministic_and_page_permutation_invariant():
     c2 = workloads.PrefillCase(**{**c.__dict__, "k_cache": k, "v_cache": v, "req_to_token": r2t})
     d = run_case(c2)
     assert torch.equal(a[0], d[0]) and torch.equal(a[1], d[1])
+
+
+def test_long_prompt_sampled_rows():
+    """The long-prompt bench workload (4 x 4096 new tokens, every q tile of
+    the last request sees up to 128 key tiles): sampled rows against the
+    oracle, each row posed as a one-row extend over its visible prefix."""
+    c = to_device(workloads.long_prompt_prefill(value_device=DEV), DEV)
+    B, n = 4, 4096
+    need = pkv.paged_attn_varlen_prefill_workspace_size(B, c.q.shape[0], n, n, 32, 8, 128)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=DEV)
+    say(f"long prompt prefill 4 x 4096, workspace {need}")
+    out, lse, pt, kl = gpu_prefill(c, workspace=ws)
+    pt_np = np_i(pt)
+    g = np.random.default_rng(3)
+    rows = [(0, 0), (0, 31), (1, 32), (2, 1000), (3, 4095)] + \
+           [(int(g.integers(B)), int(g.integers(n))) for _ in range(4)]
+    for b, j in rows:
+        L = j + 1                                   # keys [0, j] (no prefix)
+        slots = torch.as_tensor(pt_np[b, :L], device=DEV)
+        k = np_f(c.k_cache[slots])                  # [L, 1, Hkv, D] with page size 1
+        v = np_f(c.v_cache[slots])
+        r = b * n + j
+        ro, rl = oracle.paged_prefill(np_f(c.q[r:r + 1]), k, v, np.arange(L)[None, :],
+                                      np.array([0, 1]), np.array([L]), 1, c.scale, causal=True)
+        assert_close(f"out row {b},{j}", np_f(out[r:r + 1]), ro, O_TOL)
+        assert_close(f"lse row {b},{j}", np_f(lse[r:r + 1]), rl, LSE_TOL)

@@ -380,6 +380,16 @@ def config5(value_device="cpu", num_pad=0):
                             value_device=value_device, name="config5")
 
 
+def long_prompt_prefill(value_device="cpu"):
+    """Causal prefill of long prompts, bf16: 4 requests x 4096 new tokens, no
+    cached prefix, 32 q / 8 kv heads, D 128, page 1 (steady-state throughput
+    of the extend kernel, next to config2's small mixed batch)."""
+    n = 4096
+    return make_prefill_case(11, prefix_lens=[0] * 4, extend_lens=[n] * 4, num_q_heads=32,
+                             num_kv_heads=8, head_dim=128, page_size=1, num_pages=4 * n + 64,
+                             value_device=value_device, name="long_prompt_prefill")
+
+
 def small_config3(seed=13, value_device="cpu"):
     """config3's shapes and layout with short sequences (several chunks, ragged tails)."""
     return make_decode_case(seed, seq_lens=(6, 1, 700), num_q_heads=32, num_kv_heads=8,
