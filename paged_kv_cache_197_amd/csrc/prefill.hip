@@ -63,10 +63,12 @@ struct PrefillKernel {
   static constexpr int IPW = TILE / 1024 / 4; // copy blocks per wave and tensor
   static constexpr int KPW = IPW * RPB;       // keys per wave per tile
   static constexpr int SWZ = 256 / ROW;       // rows sharing one 64-bank span
-  static constexpr int MERGE_FLOATS = 16 * NB + 2;   // acc, m, l of a lane
+  static constexpr int MERGE_F4 = 4 * NB + 1;        // float4s of a lane in the merge: acc, (m, l)
+  static constexpr int QPW = TILE / 2048;             // Q copies per wave (4 heads / 8 waves)
   static constexpr float kRescaleLog2 = 8.f;          // see softmax_pv
   static_assert(KPW == 8, "a wave copies 8 keys of each tile");
-  static_assert(4 * 64 * MERGE_FLOATS * 4 <= LDS_BYTES, "merge buffer fits the rings");
+  static_assert(4 * MERGE_F4 * 64 * 16 <= 2 * GROUP_LDS, "merge buffer fits the rings");
+  static_assert(4 * TILE / 1024 == 8 * QPW, "Q copies split evenly over the waves");
 
   // key of S^T accumulator register r for lane half h
   static __device__ __forceinline__ int rho(int h, int r) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -100,6 +102,37 @@ struct PrefillKernel {
                                                        uint32_t slot_base) {
     const int t = min((seg_tile + lane / 8) * KT + KPW * w + lane % 8, L - 1);
     lds_dma4(pt_row + page_col(a, t), slot_base);
+  }
+
+  // Q^T operands of the workgroup's four heads, copied once into the free
+  // fourth ring stage of the two groups (head qh: group qh / 2, K or V half
+  // qh % 2), laid out and swizzled like a K tile so that the operand read is
+  // the K operand read. Copy i (1 KB) of the 4 * TILE / 1024 belongs to wave
+  // i / QPW; its lane l fills row (i % (TILE/1024)) * RPB + l / CH at LDS chunk
+  // l % CH from chunk swz(row, l % CH) of that row's q vector. Rows past the
+  // tile's last row and heads past the group repeat the last ones.
+  static __device__ __forceinline__ void copy_q(const PrefillArgs& a, int wave, int lane, int hb,
+                                                int kvh, int G, int tok0, int rows,
+                                                uint32_t lds0) {
+    // opaque lane index: keeps these once-per-head-block addresses from being
+    // hoisted out of the head-block loop into registers held across the tiles
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int k = 0; k < QPW; ++k) {
+      const int i = wave * QPW + k;
+      const int qh = i / (TILE / 1024);
+      const int blk = i % (TILE / 1024);
+      const int row = blk * RPB + ln / CH;
+      const int tok = min(tok0 + min(row, rows - 1), a.total_q - 1);
+      const int head = kvh * G + min(4 * hb + qh, G - 1);
+      const char* src = static_cast<const char*>(a.q) +
+                        (static_cast<int64_t>(tok) * a.hq + head) * ROW + swz(row, ln % CH) * 16;
+      lds_dma16(src, lds0 + q_lds(qh) + blk * 1024);
+    }
+  }
+  static __device__ __forceinline__ uint32_t q_lds(int qh) {
+    return static_cast<uint32_t>((qh >> 1) * GROUP_LDS + (NSTAGE - 1) * STAGE + (qh & 1) * TILE);
   }
 
   // Issue the direct-to-LDS copies of key tile kt into the LDS stage at
@@ -382,27 +415,13 @@ struct PrefillKernel {
       const bool head_ok = hg < G;
       const int head = kvh * G + min(hg, G - 1);
 
-      // the first segment's page entries and the Q^T operand (row q, dims
-      // 16j + 8h + [0, 8)) in one round trip: the wait for Q covers the entries
+      // the first segment's page entries, then the workgroup's Q tile (once,
+      // into LDS): only the entries are waited for before the first copies;
+      // Q lands together with tile 0
       const uint32_t entry_lds = lds0 + 2 * GROUP_LDS + wave * 512;
       if (n_g > 0) fetch_entries(a, pt_row, L, gb, gw, lane, entry_lds);
-      u32x4 qop[NKS];
-      {
-        const int row = min(q0 + j0 + min(q, rows - 1), a.total_q - 1);
-        const char* qrow = static_cast<const char*>(a.q) +
-                           ((static_cast<int64_t>(row) * a.hq + head) * D) * 2;
-#pragma unroll
-        for (int j = 0; j < NKS; ++j)
-          qop[j] = *reinterpret_cast<const u32x4*>(qrow + (16 * j + 8 * h) * 2);
-#pragma unroll
-        for (int j = 0; j < NKS; ++j) {
-          retire(qop[j].x);
-          retire(qop[j].y);
-          retire(qop[j].z);
-          retire(qop[j].w);
-        }
-      }
-      wait_vmem<0>();
+      copy_q(a, wave, lane, hb, kvh, G, q0 + j0, rows, lds0);
+      if (n_g > 0) wait_vmem<QPW>();
       f32x16 acc[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n)
@@ -431,8 +450,14 @@ struct PrefillKernel {
         if (n_g > 2) wait_vmem<4 * IPW>();
         else if (n_g > 1) wait_vmem<2 * IPW>();
         else wait_vmem<0>();
+      } else {
+        wait_vmem<0>();   // this wave's Q copies
       }
-      __syncthreads();   // tile 0 is in LDS
+      __syncthreads();   // tile 0 and Q are in LDS
+      // Q^T operand (row q, dims 16j + 8h + [0, 8)) of this wave's head, read
+      // before the loop's first barrier (after which stage 3 takes tile 3)
+      u32x4 qop[NKS];
+      read_k(smem + q_lds(gw) - grp * GROUP_LDS, kbase, q, h, qop);
       if (n_g > 0) {
         u32x4 kw[NKS];
         read_k(smem, kbase, q, h, kw);
@@ -468,27 +493,31 @@ struct PrefillKernel {
       __syncthreads();   // every wave is done with the rings
 
       // ---- merge the two key halves (group 1 -> group 0) through LDS ----
-      float* mbuf = reinterpret_cast<float*>(smem) + (gw * 64 + lane) * MERGE_FLOATS;
+      // wave gw's region: [float4 k][lane], k < 4 NB: acc[k/4][4(k%4) .. +3], then (m, l)
+      f32x4* mbuf = reinterpret_cast<f32x4*>(smem) + gw * MERGE_F4 * 64 + lane;
       if (grp == 1) {
 #pragma unroll
-        for (int n = 0; n < NB; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mbuf[16 * n + r] = acc[n][r];
-        mbuf[16 * NB] = m_run;
-        mbuf[16 * NB + 1] = l_run;
+        for (int k = 0; k < 4 * NB; ++k)
+          mbuf[64 * k] = f32x4{acc[k >> 2][4 * (k & 3)], acc[k >> 2][4 * (k & 3) + 1],
+                               acc[k >> 2][4 * (k & 3) + 2], acc[k >> 2][4 * (k & 3) + 3]};
+        mbuf[64 * 4 * NB] = f32x4{m_run, l_run, 0.f, 0.f};
       }
       __syncthreads();
       float lse_val = 0.f, inv = 0.f;
       if (grp == 0) {
-        const float m1 = mbuf[16 * NB];
-        const float l1 = mbuf[16 * NB + 1];
+        const f32x4 ml = mbuf[64 * 4 * NB];
+        const float m1 = ml[0];
+        const float l1 = ml[1];
         const float mm = fmaxf(m_run, m1);
         const float f0 = (m_run == neg_inf()) ? 0.f : fast_exp2((m_run - mm) * a.scale_log2);
         const float f1 = (m1 == neg_inf()) ? 0.f : fast_exp2((m1 - mm) * a.scale_log2);
 #pragma unroll
-        for (int n = 0; n < NB; ++n)
+        for (int k = 0; k < 4 * NB; ++k) {
+          const f32x4 o1 = mbuf[64 * k];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[n][r] = f0 * acc[n][r] + f1 * mbuf[16 * n + r];
+          for (int c = 0; c < 4; ++c)
+            acc[k >> 2][4 * (k & 3) + c] = f0 * acc[k >> 2][4 * (k & 3) + c] + f1 * o1[c];
+        }
         const float l_m = f0 * l_run + f1 * l1;
         const float l_tot = l_m + __shfl_xor(l_m, 32);
         inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
