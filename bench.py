@@ -41,6 +41,20 @@ def parse_args(argv=None):
     return p.parse_args(argv)
 
 
+def device_clock_mhz():
+    """Peak shader clock the runtime reports for device 0 (MHz), or None."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        # hipDeviceGetAttribute(&v, hipDeviceAttributeClockRate (= 5, kHz), device 0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) != 0 or v.value <= 0:
+            return None
+        return v.value / 1000.0
+    except OSError:
+        return None
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -196,7 +210,7 @@ def run_swa(torch, pkv, workloads, args):
     kv_lens = kl.cpu().long()
     nbytes, sum_l = decode_bytes(kv_lens, B, hq, hkv, d, 1)
     return dict(ms=ms, kernel_ms=kern_ms, build_ms=build_t.kernel_ms(), bytes=nbytes,
-                sum_kv_len=sum_l, splits=S)
+                sum_kv_len=sum_l, splits=S, case=c, pt=pt, kl=kl)
 
 
 def run_prefill(torch, pkv, workloads, args, make_case=None):
@@ -225,9 +239,21 @@ def run_prefill(torch, pkv, workloads, args, make_case=None):
             timer.pairs.append((e0, timer.mark()))
 
     ms, kern_ms = device_loop(torch, step, max(args.steps, 50), args.warmup)
+    cold_ms = None
+    if make_case is None:
+        # cold: a 512 MB rewrite before each launch (outside the event pair)
+        flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+
+        def cold_step(timer):
+            flush.fill_(1)
+            step(timer)
+        _, cold_ms = device_loop(torch, cold_step, max(args.steps, 20), args.warmup,
+                                 host_us_per_step=120.0)
+        del flush
     flops, pairs = prefill_flops(c.extend_lens.tolist(), c.seq_lens.tolist(), c.q.shape[1],
                                  c.q.shape[2])
-    return dict(ms=ms, kernel_ms=kern_ms, flops=flops, pairs=pairs)
+    return dict(ms=ms, kernel_ms=kern_ms, cold_ms=cold_ms, flops=flops, pairs=pairs, case=c,
+                pt=pt, kl=kl)
 
 
 def run_sparse(torch, pkv, workloads, args):
@@ -262,7 +288,7 @@ def run_sparse(torch, pkv, workloads, args):
     n_valid = int((c.topk_idx >= 0).sum())
     nbytes = (n_valid * dqk * 2 + B * hq * dqk * 2 + B * hq * dv * 2 + B * K * 4 * 2)
     flops = 2 * n_valid * hq * (dqk + dv)
-    return dict(warm_ms=warm_kern, cold_ms=cold_ms, bytes=nbytes, flops=flops)
+    return dict(warm_ms=warm_kern, cold_ms=cold_ms, bytes=nbytes, flops=flops, case=c)
 
 
 def run_copy(torch, args):
@@ -325,6 +351,96 @@ def cpu_baseline_decode(torch, res, budget_s):
             "sample": f"config3 requests 0..{n_req - 1} ({n_req} of {B}, {sum_l} keys, all "
                       f"{hq} heads, {c.num_splits} splits + merge), float64 numpy; "
                       f"{spent:.1f} s on a host with {cores} cores available"}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_oracle_prefill(torch, r):
+    """The oracle over every request of config2 (page size 1), per request."""
+    import numpy as np
+    import oracle
+    c, pt, kl = r["case"], r["pt"].cpu().numpy(), r["kl"].cpu().numpy()
+    cu = c.cu_seqlens_q.cpu().numpy()
+    spent, flops = 0.0, 0
+    for b in range(len(kl)):
+        L, q0, q1 = int(kl[b]), int(cu[b]), int(cu[b + 1])
+        slots = torch.as_tensor(pt[b, :L].astype(np.int64), device=c.k_cache.device)
+        k = c.k_cache[slots].to(torch.float64).cpu().numpy()   # host copies: not timed
+        v = c.v_cache[slots].to(torch.float64).cpu().numpy()
+        q = c.q[q0:q1].to(torch.float64).cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.paged_prefill(q, k, v, np.arange(L)[None, :], np.array([0, q1 - q0]),
+                             np.array([L]), 1, c.scale, causal=True)
+        spent += time.perf_counter() - t0
+        M = q1 - q0
+        flops += 4 * c.q.shape[2] * c.q.shape[1] * sum(L - M + j + 1 for j in range(M))
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(),
+            "kind": "oracle", "sample": f"all {len(kl)} requests of config2, float64 numpy; "
+                                        f"{spent:.1f} s"}
+
+
+def cpu_oracle_swa(torch, r, budget_s):
+    """The oracle (split-KV decode + merge) over config4's requests in order."""
+    import numpy as np
+    import oracle
+    c, pt, kl = r["case"], r["pt"].cpu().numpy(), r["kl"].cpu().numpy()
+    hq, d = c.q.shape[1], c.q.shape[2]
+    hkv = c.k_cache.shape[2]
+    spent, nbytes, n = 0.0, 0, 0
+    for b in range(len(kl)):
+        L = int(kl[b])
+        slots = torch.as_tensor(pt[b, :L].astype(np.int64), device=c.k_cache.device)
+        k = c.k_cache[slots].to(torch.float64).cpu().numpy()
+        v = c.v_cache[slots].to(torch.float64).cpu().numpy()
+        q = c.q[b:b + 1].to(torch.float64).cpu().numpy()
+        t0 = time.perf_counter()
+        op, lp = oracle.paged_decode_splitkv(q, k, v, np.arange(L)[None, :], np.array([L]), 1,
+                                             c.scale, c.kv_chunk, c.num_splits)
+        oracle.merge_state(op, lp)
+        spent += time.perf_counter() - t0
+        nbytes += 2 * L * hkv * d * 2 + hq * d * 2 * 2 + 4 * L
+        n += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+            "kind": "oracle", "sample": f"config4 requests 0..{n - 1} ({n} of {len(kl)}), float64 "
+                                        f"numpy; {spent:.1f} s"}
+
+
+def cpu_oracle_sparse(torch, r, budget_s):
+    """The oracle over config5's requests in order (touched rows copied per request)."""
+    import numpy as np
+    import oracle
+    c = r["case"]
+    r2t = c.req_to_token.cpu().numpy()
+    rpi = c.req_pool_indices.cpu().numpy()
+    idx = c.topk_idx.cpu().numpy()
+    dqk, dv = c.q.shape[2], c.head_dim_v
+    spent, nbytes, n = 0.0, 0, 0
+    for b in range(idx.shape[0]):
+        valid = idx[b] >= 0
+        slots = r2t[rpi[b], idx[b][valid]]
+        kv = c.kv_cache[torch.as_tensor(slots.astype(np.int64), device=c.kv_cache.device)]
+        kv = kv.to(torch.float64).cpu().numpy()
+        small = np.zeros((1, r2t.shape[1]), dtype=np.int64)
+        small[0, idx[b][valid]] = np.arange(len(slots))
+        q = c.q[b:b + 1].to(torch.float64).cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.sparse_topk_decode(q, kv, small, np.array([0]), idx[b:b + 1], c.scale, dv)
+        spent += time.perf_counter() - t0
+        nbytes += int(valid.sum()) * dqk * 2 + c.q.shape[1] * (dqk + dv) * 2 + idx.shape[1] * 8
+        n += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+            "kind": "oracle", "sample": f"config5 requests 0..{n - 1} ({n} of {idx.shape[0]}), "
+                                        f"float64 numpy; {spent:.1f} s"}
 
 
 # ---------------------------------------------------------------------------
@@ -419,6 +535,8 @@ def main(argv=None):
                 "kernel_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
                                          / HBM_PEAK_GBS, 4),
                 "sum_kv_len": r["sum_kv_len"], "num_splits": r["splits"]}
+            if not args.no_cpu_baseline:
+                extra["swa_decode"]["cpu_oracle"] = cpu_oracle_swa(torch, r, 4.0)
         except Exception as e:  # report, do not hide
             extra["swa_decode"] = {"error": repr(e)}
         torch.cuda.empty_cache()
@@ -433,7 +551,11 @@ def main(argv=None):
                 "kernel_ms": round(r["kernel_ms"], 5), "device_ms_per_step": round(r["ms"], 5),
                 "TFLOP/s": round(tf, 2), "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS,
                 "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": r["flops"],
-                "visible_pairs_per_head": r["pairs"]}
+                "visible_pairs_per_head": r["pairs"],
+                "cold_kernel_ms": round(r["cold_ms"], 5),
+                "cold_TFLOP/s": round(r["flops"] / (r["cold_ms"] * 1e-3) / 1e12, 2)}
+            if not args.no_cpu_baseline:
+                extra["prefill"]["cpu_oracle"] = cpu_oracle_prefill(torch, r)
         except Exception as e:
             extra["prefill"] = {"error": repr(e)}
         torch.cuda.empty_cache()
@@ -466,9 +588,17 @@ def main(argv=None):
                 "warm_GB/s": round(r["bytes"] / (r["warm_ms"] * 1e-3) / 1e9, 2),
                 "cold_TFLOP/s": round(r["flops"] / (r["cold_ms"] * 1e-3) / 1e12, 2),
                 "bytes": r["bytes"], "flops": r["flops"]}
+            if not args.no_cpu_baseline:
+                extra["sparse_mla"]["cpu_oracle"] = cpu_oracle_sparse(torch, r, 4.0)
         except Exception as e:
             extra["sparse_mla"] = {"error": repr(e)}
 
+    clk = device_clock_mhz()
+    extra["device"] = {
+        "sclk_max_mhz": clk,
+        "bf16_mfma_peak_at_sclk_max_TFLOP/s": (round(256 * 4096 * clk * 1e6 / 1e12, 1)
+                                               if clk else None),
+        "note": "fractions use 2516.6 TFLOP/s (2.4 GHz) and 8 TB/s"}
     if line:
         line["other_workloads"] = extra
     else:
