@@ -27,6 +27,7 @@ from .reference import (  # noqa: F401
     causal_key_ranges,
     cu_seqlens,
     gather_paged,
+    kv_append,
     kv_head_of,
     merge_state,
     page_table_pa_swa,
@@ -34,6 +35,7 @@ from .reference import (  # noqa: F401
     page_table_strided,
     paged_decode_splitkv,
     paged_prefill,
+    paged_prefill_append,
     softmax_attention,
     sparse_topk_decode,
     visible_key_counts,

@@ -241,6 +241,39 @@ def paged_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, page_s
     return out, lse
 
 
+def kv_append(k_cache, v_cache, out_cache_loc, k_new, v_new):
+    """Write the new tokens' keys and values into a paged cache.
+
+    [FA] ``forward_extend`` (and ``forward_decode``): before attending, the
+    layer's new ``k`` and ``v`` go into the token pool with ``set_kv_buffer`` at
+    ``cache_loc = forward_batch.out_cache_loc``: token slot ``out_cache_loc[i]``
+    receives row ``i``. A slot indexes the cache viewed as
+    ``[num_pages * page_size, Hkv, D]`` (page ``slot // P``, position ``slot % P``).
+
+    k_new, v_new: [n, Hkv, D]; out_cache_loc: [n] distinct slots. Returns new
+    float64 caches; the inputs are left unchanged.
+    """
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    loc = np.asarray(out_cache_loc, dtype=np.int64)
+    kflat = kc.reshape(-1, kc.shape[2], kc.shape[3])   # views of the copies
+    vflat = vc.reshape(-1, vc.shape[2], vc.shape[3])
+    kflat[loc] = np.asarray(k_new, dtype=np.float64)
+    vflat[loc] = np.asarray(v_new, dtype=np.float64)
+    return kc, vc
+
+
+def paged_prefill_append(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, page_size,
+                         scale, out_cache_loc, k_new, v_new, causal=True):
+    """[FA] ``forward_extend`` with ``save_kv_cache``: ``kv_append`` of the new
+    tokens, then ``paged_prefill`` over the updated cache. Returns
+    (O, LSE, k_cache', v_cache')."""
+    kc, vc = kv_append(k_cache, v_cache, out_cache_loc, k_new, v_new)
+    out, lse = paged_prefill(q, kc, vc, page_table, cu_seqlens_q, kv_lens, page_size, scale,
+                             causal)
+    return out, lse, kc, vc
+
+
 def paged_decode_splitkv(q, k_cache, v_cache, page_table, kv_lens, page_size, scale,
                          kv_chunk, num_splits):
     """Decode (one new token per request) with the key axis cut into chunks.

@@ -418,3 +418,80 @@ def test_planted_pa_swa_gap_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "page_table_pa_swa", bad)
     with pytest.raises(AssertionError):
         test_pa_swa_formula_matches_set_construction()
+
+
+# --- kv_append: set_kv_buffer at out_cache_loc ([FA] forward_extend) ---------
+
+def _tiny_append_case(seed=0, pages=6, P=4, hkv=2, d=3, n=7):
+    g = np.random.default_rng(seed)
+    kc = g.standard_normal((pages, P, hkv, d))
+    vc = g.standard_normal((pages, P, hkv, d))
+    loc = g.permutation(pages * P)[:n]
+    kn = g.standard_normal((n, hkv, d))
+    vn = g.standard_normal((n, hkv, d))
+    return kc, vc, loc, kn, vn
+
+
+def test_kv_append_matches_elementwise_loop():
+    kc, vc, loc, kn, vn = _tiny_append_case()
+    P = kc.shape[1]
+    ek, ev = kc.copy(), vc.copy()
+    for i, s in enumerate(loc):                 # brute force: one element at a time
+        for h in range(kc.shape[2]):
+            for x in range(kc.shape[3]):
+                ek[s // P, s % P, h, x] = kn[i, h, x]
+                ev[s // P, s % P, h, x] = vn[i, h, x]
+    gk, gv = oracle.kv_append(kc, vc, loc, kn, vn)
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
+    assert not np.array_equal(kc, gk)           # the inputs are not modified in place
+    assert np.array_equal(kc, _tiny_append_case()[0])
+
+
+def test_kv_append_invariants():
+    kc, vc, loc, kn, vn = _tiny_append_case(seed=3)
+    gk, gv = oracle.kv_append(kc, vc, loc, kn, vn)
+    P = kc.shape[1]
+    flat = gk.reshape(-1, *gk.shape[2:])
+    assert np.array_equal(flat[loc], kn)        # the written slots hold the new rows
+    untouched = np.setdiff1d(np.arange(flat.shape[0]), loc)
+    assert np.array_equal(flat[untouched], kc.reshape(-1, *kc.shape[2:])[untouched])
+    # appending the values a slot already holds changes nothing
+    k2, v2 = oracle.kv_append(gk, gv, loc, kn, vn)
+    assert np.array_equal(k2, gk) and np.array_equal(v2, gv)
+
+
+def test_prefill_append_equals_prefill_over_the_written_cache():
+    """Extend with the new tokens' K/V passed separately (their cache slots
+    poisoned) equals the plain extend over a cache that already holds them."""
+    c = workloads.make_prefill_case(5, prefix_lens=[3, 0, 9], extend_lens=[4, 5, 2],
+                                    num_q_heads=4, num_kv_heads=2, head_dim=8, page_size=2,
+                                    num_pages=40)
+    r2t, rpi = i64(c.req_to_token), i64(c.req_pool_indices)
+    pre = i64(c.seq_lens) - i64(c.extend_lens)
+    loc = np.concatenate([r2t[rpi[b], pre[b]:pre[b] + int(c.extend_lens[b])]
+                          for b in range(len(pre))])
+    kc, vc = f64(c.k_cache), f64(c.v_cache)
+    P = c.page_size
+    kn = kc.reshape(-1, *kc.shape[2:])[loc].copy()
+    vn = vc.reshape(-1, *vc.shape[2:])[loc].copy()
+    pt, kl, _ = oracle.page_table_strided(i64(c.req_to_token), rpi, i64(c.seq_lens), P,
+                                          c.table_width)
+    ro, rl = oracle.paged_prefill(f64(c.q), kc, vc, pt, i64(c.cu_seqlens_q), kl, P, c.scale)
+    bad_k, bad_v = kc.copy(), vc.copy()
+    bad_k.reshape(-1, *kc.shape[2:])[loc] = np.nan
+    bad_v.reshape(-1, *vc.shape[2:])[loc] = np.nan
+    o, l, k2, v2 = oracle.paged_prefill_append(f64(c.q), bad_k, bad_v, pt, i64(c.cu_seqlens_q),
+                                               kl, P, c.scale, loc, kn, vn)
+    assert np.array_equal(o, ro) and np.array_equal(l, rl)
+    assert np.array_equal(k2, kc, equal_nan=True) and np.array_equal(v2, vc, equal_nan=True)
+
+
+def test_planted_append_slot_mistake_is_caught(monkeypatch):
+    kc, vc, loc, kn, vn = _tiny_append_case(seed=5)
+    good = oracle.kv_append(kc, vc, loc, kn, vn)
+    real = np.asarray
+    monkeypatch.setattr(ref.np, "asarray",
+                        lambda a, dtype=None: (real(a, dtype=dtype) + 1)
+                        if dtype is np.int64 else real(a, dtype=dtype))
+    bad = ref.kv_append(kc, vc, loc % (kc.shape[0] * kc.shape[1] - 1), kn, vn)
+    assert not np.array_equal(bad[0], good[0])
