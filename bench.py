@@ -32,8 +32,8 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--only", choices=["all", "decode", "prefill", "prefill_long", "swa", "sparse",
-                                      "copy"],
+    p.add_argument("--only", choices=["all", "decode", "prefill", "prefill_long",
+                                      "prefill_append", "swa", "sparse", "copy"],
                    default="all", help="restrict to one workload (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -254,6 +254,48 @@ def run_prefill(torch, pkv, workloads, args, make_case=None):
                                  c.q.shape[2])
     return dict(ms=ms, kernel_ms=kern_ms, cold_ms=cold_ms, flops=flops, pairs=pairs, case=c,
                 pt=pt, kl=kl)
+
+
+def run_prefill_append(torch, pkv, workloads, args):
+    """config2's extend step with its cache write: the new tokens' K/V are
+    written at out_cache_loc (the slots the page table maps the new positions
+    to), then the extend attention runs over the updated cache; one call."""
+    dev = torch.device("cuda:0")
+    c = workloads.config2(value_device=dev)
+    r2t, rpi, sl, cu = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev),
+                        c.cu_seqlens_q.to(dev))
+    pre = (c.seq_lens - c.extend_lens).tolist()
+    loc = torch.cat([c.req_to_token[int(c.req_pool_indices[b]), pre[b]:pre[b] + int(n)]
+                     for b, n in enumerate(c.extend_lens.tolist())]).to(torch.int64).to(dev)
+    hkv, d = c.k_cache.shape[2], c.k_cache.shape[3]
+    kn = c.k_cache.view(-1, hkv, d)[loc].clone()
+    vn = c.v_cache.view(-1, hkv, d)[loc].clone()
+    loc = loc.to(torch.int32)
+    B = sl.numel()
+    pt = torch.empty((B, c.table_width), dtype=torch.int32, device=dev)
+    kl = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(c.q)
+    lse = torch.empty(c.q.shape[:2], dtype=torch.float32, device=dev)
+    max_k = int(c.seq_lens.max())
+    ws_bytes = pkv.paged_attn_varlen_prefill_workspace_size(
+        B, c.q.shape[0], c.max_seqlen_q, max_k, c.q.shape[1], hkv, d)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def step(timer):
+        pkv.build_page_table(r2t, rpi, sl, c.page_size, c.table_width, page_table=pt,
+                             kv_lens=kl, with_cu_seqlens=False)
+        e0 = timer.mark() if timer else None
+        pkv.paged_attn_varlen_prefill(c.q, c.k_cache, c.v_cache, pt, cu, kl, c.max_seqlen_q,
+                                      c.scale, max_seqlen_k=max_k, causal=True, workspace=ws,
+                                      out=out, lse=lse, k_new=kn, v_new=vn, out_cache_loc=loc)
+        if timer:
+            timer.pairs.append((e0, timer.mark()))
+
+    ms, call_ms = device_loop(torch, step, max(args.steps, 50), args.warmup)
+    flops, _ = prefill_flops(c.extend_lens.tolist(), c.seq_lens.tolist(), c.q.shape[1],
+                             c.q.shape[2])
+    append_bytes = 2 * 2 * kn.numel() * kn.element_size() + 4 * loc.numel()
+    return dict(ms=ms, call_ms=call_ms, flops=flops, append_bytes=append_bytes)
 
 
 def run_sparse(torch, pkv, workloads, args):
@@ -573,6 +615,20 @@ def main(argv=None):
                 "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": r["flops"]}
         except Exception as e:
             extra["prefill_long"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "prefill_append"):
+        try:
+            r = run_prefill_append(torch, pkv, workloads, args)
+            extra["prefill_append"] = {
+                "workload": "config2's extend step with its cache write (new tokens' K/V "
+                            "scattered to out_cache_loc, then the extend attention; one call, "
+                            "two kernels)",
+                "call_ms": round(r["call_ms"], 5), "device_ms_per_step": round(r["ms"], 5),
+                "append_bytes": r["append_bytes"],
+                "attention_TFLOP/s_over_call": round(r["flops"] / (r["call_ms"] * 1e-3) / 1e12, 2)}
+        except Exception as e:
+            extra["prefill_append"] = {"error": repr(e)}
         torch.cuda.empty_cache()
 
     if args.only in ("all", "sparse"):

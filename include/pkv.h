@@ -138,6 +138,49 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
                                        void* stream);
 
 /*
+ * paged_kv_append -- write new tokens' keys and values into the cache.
+ * [FA] forward_extend / forward_decode: before attending, the layer's new k and
+ * v are stored with set_kv_buffer at out_cache_loc:
+ *   k_cache[out_cache_loc[i]] = k_new[i],  v_cache[out_cache_loc[i]] = v_new[i]
+ * where a slot indexes the cache viewed as [num_slots, Hkv, D]
+ * (num_slots = num_pages * page_size; slot s is page s / P, position s % P).
+ *
+ * k_new, v_new   [n_tokens, num_kv_heads, head_dim], dtype (PKV_BF16 or PKV_F32)
+ * out_cache_loc  [n_tokens] int32, distinct slots (a slot outside [0, num_slots)
+ *                is skipped; repeated slots leave an unspecified one of the rows)
+ * k_cache, v_cache  the cache, same dtype, written in place.
+ * Errors: PKV_EINVAL for NULL pointers (n_tokens > 0) or bad sizes;
+ * PKV_EUNSUPPORTED for another dtype or head_dim * element size not a multiple
+ * of 16 bytes. n_tokens == 0 enqueues nothing.
+ */
+pkv_status_t paged_kv_append(const void* k_new, const void* v_new, int32_t dtype,
+                             const int32_t* out_cache_loc, int32_t n_tokens, int32_t num_kv_heads,
+                             int32_t head_dim, void* k_cache, void* v_cache, int64_t num_slots,
+                             void* stream);
+
+/*
+ * paged_attn_varlen_prefill_append -- the extend step with its cache write:
+ * [FA] forward_extend with save_kv_cache, i.e. paged_kv_append of the new
+ * tokens (k_new / v_new [total_q, Hkv, D], one row per new token in
+ * cu_seqlens_q order, slots out_cache_loc [total_q]) followed by
+ * paged_attn_varlen_prefill over the updated cache. Arguments as for those
+ * two calls (the caches are written, hence not const). The caller's page
+ * table maps position kv_lens[b] - M_b + j of request b to slot
+ * out_cache_loc[cu_seqlens_q[b] + j], as the pages' req_to_token does, and no
+ * request's cached prefix uses those slots. Every argument is checked before
+ * anything is enqueued; then two kernels run on the stream (the scatter, then
+ * the attention).
+ */
+pkv_status_t paged_attn_varlen_prefill_append(
+    const void* q, int32_t dtype, void* k_cache, void* v_cache, int64_t num_pages,
+    const int32_t* page_table, int32_t pt_stride, const int32_t* cu_seqlens_q,
+    const int32_t* kv_lens, int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+    int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t page_size, float softmax_scale, int32_t causal, const void* k_new, const void* v_new,
+    const int32_t* out_cache_loc, void* workspace, size_t workspace_bytes, void* out, float* lse,
+    void* stream);
+
+/*
  * paged_attn_decode_splitkv -- one query token per request, key axis split.
  * [FA] forward_decode (flash_attn_with_kvcache, num_splits); [DCA]
  * _dual_chunk_flash_attn_decoding (partial decodes over disjoint key ranges

@@ -19,6 +19,7 @@ import torch
 __all__ = [
     "PkvError", "PkvLibraryMissing", "load_library", "library_path", "declared_symbols",
     "build_page_table", "paged_attn_varlen_prefill", "paged_attn_varlen_prefill_workspace_size",
+    "paged_kv_append",
     "paged_attn_decode_splitkv",
     "merge_state", "sparse_topk_decode", "sparse_topk_decode_workspace_size",
     "PKV_F32", "PKV_BF16",
@@ -68,6 +69,11 @@ _SIGNATURES = {
     "paged_attn_varlen_prefill": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _P,
                                                  _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                  _F, _I32, _P, _SZ, _P, _P, _P]),
+    "paged_kv_append": (ctypes.c_int, [_P, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _I64, _P]),
+    "paged_attn_varlen_prefill_append": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P,
+                                                        _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                        _I32, _I32, _F, _I32, _P, _P, _P, _P,
+                                                        _SZ, _P, _P, _P]),
     "paged_attn_decode_splitkv": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _I32,
                                                  _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _P,
                                                  _P, _P, _P]),
@@ -238,15 +244,40 @@ def paged_attn_varlen_prefill_workspace_size(batch, total_q, max_seqlen_q, max_s
         batch, total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim))
 
 
+def paged_kv_append(k_new, v_new, out_cache_loc, k_cache, v_cache):
+    """Write new tokens' K/V [n, Hkv, D] into the cache ([pages, P, Hkv, D],
+    modified in place) at token slots out_cache_loc [n]."""
+    lib = load_library()
+    dev = k_cache.device
+    _need(k_cache, "k_cache", k_cache.dtype, dev, 4)
+    _need(v_cache, "v_cache", k_cache.dtype, dev, 4)
+    _need(k_new, "k_new", k_cache.dtype, dev, 3)
+    _need(v_new, "v_new", k_cache.dtype, dev, 3)
+    loc = _i32(out_cache_loc, "out_cache_loc", dev)
+    num_pages, page_size, hkv, d = k_cache.shape
+    n = k_new.shape[0]
+    if k_new.shape != (n, hkv, d) or v_new.shape != (n, hkv, d) or loc.numel() != n:
+        raise ValueError("paged_kv_append: k_new / v_new must be [n, Hkv, D] and out_cache_loc [n]")
+    st = lib.paged_kv_append(_ptr(k_new), _ptr(v_new), _dtype_code(k_cache.dtype), _ptr(loc), n,
+                             hkv, d, _ptr(k_cache), _ptr(v_cache), num_pages * page_size,
+                             _stream(dev))
+    _check("paged_kv_append", st)
+    return k_cache, v_cache
+
+
 def paged_attn_varlen_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens,
                               max_seqlen_q, softmax_scale, *, max_seqlen_k=None, causal=True,
-                              workspace=None, out=None, lse=None, return_lse=True):
+                              workspace=None, out=None, lse=None, return_lse=True,
+                              k_new=None, v_new=None, out_cache_loc=None):
     """Causal varlen extend over a paged cache. Returns (out, lse or None).
 
     max_seqlen_k defaults to the page table's capacity (width * page_size).
     workspace: a uint8 device tensor of at least
     paged_attn_varlen_prefill_workspace_size(...) bytes whose counters are
-    zero (a fresh zeroed one is made when None; the call leaves them zero)."""
+    zero (a fresh zeroed one is made when None; the call leaves them zero).
+    With k_new / v_new [total_q, Hkv, D] and out_cache_loc [total_q], the new
+    tokens are first written into the cache at those slots (the extend step
+    with its cache write, one call)."""
     lib = load_library()
     dev = q.device
     _need(q, "q", torch.bfloat16, dev, 3)
@@ -269,12 +300,29 @@ def paged_attn_varlen_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev)
-    st = lib.paged_attn_varlen_prefill(
+    if k_new is None and v_new is None and out_cache_loc is None:
+        st = lib.paged_attn_varlen_prefill(
+            _ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(pt),
+            pt.shape[1], _ptr(cu), _ptr(kl), batch, total_q, int(max_seqlen_q),
+            int(max_seqlen_k), hq, hkv, d, page_size, float(softmax_scale), int(bool(causal)),
+            _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
+        _check("paged_attn_varlen_prefill", st)
+        return out, lse
+    if k_new is None or v_new is None or out_cache_loc is None:
+        raise ValueError("paged_attn_varlen_prefill: k_new, v_new and out_cache_loc go together")
+    _need(k_new, "k_new", q.dtype, dev, 3)
+    _need(v_new, "v_new", q.dtype, dev, 3)
+    loc = _i32(out_cache_loc, "out_cache_loc", dev)
+    if k_new.shape != (total_q, hkv, d) or v_new.shape != (total_q, hkv, d) or \
+            loc.numel() != total_q:
+        raise ValueError("paged_attn_varlen_prefill: k_new / v_new must be [total_q, Hkv, D] "
+                         "and out_cache_loc [total_q]")
+    st = lib.paged_attn_varlen_prefill_append(
         _ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(pt),
         pt.shape[1], _ptr(cu), _ptr(kl), batch, total_q, int(max_seqlen_q), int(max_seqlen_k),
-        hq, hkv, d, page_size, float(softmax_scale), int(bool(causal)), _ptr(workspace),
-        ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
-    _check("paged_attn_varlen_prefill", st)
+        hq, hkv, d, page_size, float(softmax_scale), int(bool(causal)), _ptr(k_new), _ptr(v_new),
+        _ptr(loc), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
+    _check("paged_attn_varlen_prefill_append", st)
     return out, lse
 
 

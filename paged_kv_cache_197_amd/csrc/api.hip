@@ -254,16 +254,21 @@ size_t paged_attn_varlen_prefill_workspace_size(int32_t batch, int32_t total_q,
       .bytes;
 }
 
-pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void* k_cache,
-                                       const void* v_cache, int64_t num_pages,
-                                       const int32_t* page_table, int32_t pt_stride,
-                                       const int32_t* cu_seqlens_q, const int32_t* kv_lens,
-                                       int32_t batch, int32_t total_q, int32_t max_seqlen_q,
-                                       int32_t max_seqlen_k, int32_t num_q_heads,
-                                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                                       float softmax_scale, int32_t causal, void* workspace,
-                                       size_t workspace_bytes, void* out, float* lse,
-                                       void* stream) {
+}  // extern "C"
+
+// Validation and argument packing shared by the prefill entry points; sets
+// *nothing when there is no work (nothing to launch).
+static pkv_status_t prefill_prepare(const void* q, int32_t dtype, const void* k_cache,
+                                    const void* v_cache, int64_t num_pages,
+                                    const int32_t* page_table, int32_t pt_stride,
+                                    const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                    int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                    int32_t max_seqlen_k, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                    float softmax_scale, int32_t causal, void* workspace,
+                                    size_t workspace_bytes, void* out, float* lse,
+                                    pkv::PrefillArgs& a, bool* nothing) {
+  *nothing = false;
   PKV_REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "prefill: dtype %d not supported (bf16)",
               dtype);
   PKV_REQUIRE(head_dim == 64 || head_dim == 128, PKV_EUNSUPPORTED,
@@ -285,7 +290,10 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
   PKV_REQUIRE(causal == 0 || causal == 1, PKV_EINVAL, "prefill: causal %d", causal);
   PKV_REQUIRE(max_seqlen_q <= total_q, PKV_EINVAL, "prefill: max_seqlen_q %d > total_q %d",
               max_seqlen_q, total_q);
-  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return pkv_host::ok();
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) {
+    *nothing = true;
+    return pkv_host::ok();
+  }
   PKV_REQUIRE(q && k_cache && v_cache && page_table && cu_seqlens_q && kv_lens && out,
               PKV_EINVAL, "prefill: NULL required pointer");
   const pkv_host::PrefillPlan plan = pkv_host::prefill_plan(
@@ -293,7 +301,6 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
   PKV_REQUIRE(plan.bytes == 0 || (workspace != nullptr && workspace_bytes >= plan.bytes),
               PKV_EINVAL, "prefill: workspace of %zu bytes, need %zu", workspace_bytes,
               plan.bytes);
-  pkv::PrefillArgs a;
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;
@@ -321,8 +328,94 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
                       : nullptr;
   a.out = out;
   a.lse = lse;
+  return pkv_host::ok();
+}
+
+extern "C" {
+
+pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void* k_cache,
+                                       const void* v_cache, int64_t num_pages,
+                                       const int32_t* page_table, int32_t pt_stride,
+                                       const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                       int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                       int32_t max_seqlen_k, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                       float softmax_scale, int32_t causal, void* workspace,
+                                       size_t workspace_bytes, void* out, float* lse,
+                                       void* stream) {
+  pkv::PrefillArgs a;
+  bool nothing = false;
+  const pkv_status_t st = prefill_prepare(
+      q, dtype, k_cache, v_cache, num_pages, page_table, pt_stride, cu_seqlens_q, kv_lens, batch,
+      total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, page_size,
+      softmax_scale, causal, workspace, workspace_bytes, out, lse, a, &nothing);
+  if (st != PKV_OK || nothing) return st;
   return pkv_host::from_hip(pkv_launch::prefill(a, head_dim, static_cast<hipStream_t>(stream)),
                             "prefill launch");
+}
+
+// checks shared by the append entry points; row_bytes = Hkv * D * element size
+static pkv_status_t append_check(const char* who, const void* k_new, const void* v_new,
+                                 int32_t dtype, const int32_t* out_cache_loc, int32_t n_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, void* k_cache,
+                                 void* v_cache, int64_t num_slots, int64_t* row_bytes) {
+  PKV_REQUIRE(dtype == PKV_BF16 || dtype == PKV_F32, PKV_EUNSUPPORTED, "%s: dtype %d", who,
+              dtype);
+  PKV_REQUIRE(n_tokens >= 0 && num_kv_heads >= 1 && head_dim >= 1 && num_slots >= 1,
+              PKV_EINVAL, "%s: bad sizes", who);
+  const int64_t es = dtype == PKV_BF16 ? 2 : 4;
+  *row_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * es;
+  PKV_REQUIRE((static_cast<int64_t>(head_dim) * es) % 16 == 0, PKV_EUNSUPPORTED,
+              "%s: head_dim %d x %lld bytes not a multiple of 16", who, head_dim, (long long)es);
+  PKV_REQUIRE(n_tokens == 0 || (k_new && v_new && out_cache_loc && k_cache && v_cache),
+              PKV_EINVAL, "%s: NULL required pointer", who);
+  return pkv_host::ok();
+}
+
+pkv_status_t paged_kv_append(const void* k_new, const void* v_new, int32_t dtype,
+                             const int32_t* out_cache_loc, int32_t n_tokens, int32_t num_kv_heads,
+                             int32_t head_dim, void* k_cache, void* v_cache, int64_t num_slots,
+                             void* stream) {
+  int64_t row_bytes = 0;
+  const pkv_status_t st = append_check("paged_kv_append", k_new, v_new, dtype, out_cache_loc,
+                                       n_tokens, num_kv_heads, head_dim, k_cache, v_cache,
+                                       num_slots, &row_bytes);
+  if (st != PKV_OK || n_tokens == 0) return st;
+  return pkv_host::from_hip(pkv_launch::kv_append(k_new, v_new, out_cache_loc, n_tokens, row_bytes,
+                                                  k_cache, v_cache, num_slots,
+                                                  static_cast<hipStream_t>(stream)),
+                            "paged_kv_append launch");
+}
+
+pkv_status_t paged_attn_varlen_prefill_append(
+    const void* q, int32_t dtype, void* k_cache, void* v_cache, int64_t num_pages,
+    const int32_t* page_table, int32_t pt_stride, const int32_t* cu_seqlens_q,
+    const int32_t* kv_lens, int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+    int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t page_size, float softmax_scale, int32_t causal, const void* k_new, const void* v_new,
+    const int32_t* out_cache_loc, void* workspace, size_t workspace_bytes, void* out, float* lse,
+    void* stream) {
+  // every check before anything is enqueued: the cache is written only when
+  // the attention will run too
+  pkv::PrefillArgs a;
+  bool nothing = false;
+  pkv_status_t st = prefill_prepare(
+      q, dtype, k_cache, v_cache, num_pages, page_table, pt_stride, cu_seqlens_q, kv_lens, batch,
+      total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, page_size,
+      softmax_scale, causal, workspace, workspace_bytes, out, lse, a, &nothing);
+  if (st != PKV_OK) return st;
+  int64_t row_bytes = 0;
+  st = append_check("paged_attn_varlen_prefill_append", k_new, v_new, dtype, out_cache_loc,
+                    total_q, num_kv_heads, head_dim, k_cache, v_cache, num_pages * page_size,
+                    &row_bytes);
+  if (st != PKV_OK || total_q == 0) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = pkv_host::from_hip(pkv_launch::kv_append(k_new, v_new, out_cache_loc, total_q, row_bytes,
+                                                k_cache, v_cache, num_pages * page_size, s),
+                          "paged_attn_varlen_prefill_append: append launch");
+  if (st != PKV_OK || nothing) return st;
+  return pkv_host::from_hip(pkv_launch::prefill(a, head_dim, s),
+                            "paged_attn_varlen_prefill_append: prefill launch");
 }
 
 size_t sparse_topk_decode_workspace_size(int32_t batch, int32_t topk, int32_t num_q_heads,

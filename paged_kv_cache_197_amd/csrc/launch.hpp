@@ -18,6 +18,9 @@ hipError_t merge_state(const float* o_parts, const float* lse_parts, int num_par
                        int dv, void* out, int out_dtype, float* lse_out, hipStream_t stream);
 hipError_t decode_splitkv(const pkv::DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t prefill(const pkv::PrefillArgs& a, int head_dim, hipStream_t stream);
+hipError_t kv_append(const void* k_new, const void* v_new, const int32_t* loc, int32_t n,
+                     int64_t row_bytes, void* k_cache, void* v_cache, int64_t num_slots,
+                     hipStream_t stream);
 size_t sparse_workspace_bytes(int batch, int topk, int num_q_heads, int head_dim_v);
 hipError_t sparse_topk(const pkv::SparseArgs& a, hipStream_t stream);
 }  // namespace pkv_launch

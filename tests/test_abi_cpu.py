@@ -15,11 +15,12 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libpkv.so not b
 EINVAL, EUNSUP = 1, 2
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_entry_points():
     names = pkv.declared_symbols()
     for fn in ["build_page_table", "paged_attn_varlen_prefill", "paged_attn_decode_splitkv",
                "merge_state", "sparse_topk_decode", "paged_attn_varlen_prefill_workspace_size",
-               "sparse_topk_decode_workspace_size"]:
+               "sparse_topk_decode_workspace_size", "paged_kv_append",
+               "paged_attn_varlen_prefill_append"]:
         assert fn in names
 
 
@@ -141,3 +142,23 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setenv("PKV_LIBRARY", str(tmp_path / "nope.so"))
     with pytest.raises(pkv.PkvLibraryMissing):
         pkv.load_library()
+
+
+def test_append_argument_errors():
+    lib = pkv.load_library()
+    ap = lib.paged_kv_append
+    fake = ctypes.c_void_p(256)
+    # k_new v_new dtype loc n Hkv D k_cache v_cache slots stream
+    assert ap(None, None, 1, None, 0, 8, 128, None, None, 100, None) == 0     # nothing to do
+    assert ap(None, None, 1, None, 4, 8, 128, None, None, 100, None) == EINVAL
+    assert ap(fake, fake, 7, fake, 4, 8, 128, fake, fake, 100, None) == EUNSUP   # dtype
+    assert ap(fake, fake, 1, fake, 4, 8, 4, fake, fake, 100, None) == EUNSUP     # 8-byte rows
+    assert ap(fake, fake, 1, fake, -1, 8, 128, fake, fake, 100, None) == EINVAL
+    pa = lib.paged_attn_varlen_prefill_append
+    # the prefill checks come first and nothing is enqueued when any check fails
+    args = [fake, 1, fake, fake, 8192, fake, 8192, fake, fake, 1, 64, 64, 64, 32, 8, 128, 1,
+            0.088, 1]
+    assert pa(*args, None, fake, fake, None, 0, fake, None, None) == EINVAL     # k_new NULL
+    bad = list(args)
+    bad[15] = 96                                                               # head_dim
+    assert pa(*bad, fake, fake, fake, None, 0, fake, None, None) == EUNSUP
