@@ -27,7 +27,9 @@ from .reference import (  # noqa: F401
     causal_key_ranges,
     cu_seqlens,
     gather_paged,
+    key_lower_bound,
     kv_append,
+    local_attention_virtual_batches,
     kv_head_of,
     merge_state,
     page_table_pa_swa,

@@ -140,6 +140,53 @@ def visible_key_counts(num_new, kv_len, causal=True) -> np.ndarray:
     return np.array([kv_len - num_new + j + 1 for j in range(num_new)], dtype=np.int64)
 
 
+def key_lower_bound(pos, window_left=-1, attn_chunk=0) -> int:
+    """First key a query at absolute position ``pos`` may see under a
+    lower-bound mask (the upper bound is ``pos`` itself, causal).
+
+    [FA] ``forward_extend`` / ``forward_decode``: ``window_size =
+    (sliding_window_size, 0)``, inclusive on both sides, so keys ``pos - W ..
+    pos``. [FA] ``make_local_attention_virtual_batches``: chunked local
+    attention, keys from the start of ``pos``'s ``attn_chunk``-aligned block
+    (the mask drawn for batch 0 of the worked example). Neither: key 0.
+    """
+    if window_left >= 0 and attn_chunk > 0:
+        raise ValueError("a sliding window and local chunks do not combine")
+    if window_left >= 0:
+        return max(0, pos - window_left)
+    if attn_chunk > 0:
+        return (pos // attn_chunk) * attn_chunk
+    return 0
+
+
+def local_attention_virtual_batches(attn_chunk, cu_seqlens_q, seq_lens):
+    """Chunked local attention as independent causal sub-batches.
+
+    [FA] ``make_local_attention_virtual_batches``: the new rows of a request
+    are grouped by the ``attn_chunk``-aligned block their position falls in;
+    each group is a batch item whose keys run from the block start to the
+    group's last row, with ordinary bottom-right causal alignment inside it.
+    Returns, per virtual batch, (request, first q row, q rows, first key, key
+    count) in request order. (The page's text is cut short after the q-length
+    step; the key ranges follow from the mask it draws.)
+    """
+    out = []
+    for b in range(len(seq_lens)):
+        q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        L, M = int(seq_lens[b]), q1 - q0
+        j = 0
+        while j < M:
+            pos = L - M + j
+            blk = pos // attn_chunk
+            j_end = j
+            while j_end < M and (L - M + j_end) // attn_chunk == blk:
+                j_end += 1
+            last = L - M + j_end - 1
+            out.append((b, q0 + j, j_end - j, blk * attn_chunk, last + 1 - blk * attn_chunk))
+            j = j_end
+    return out
+
+
 def causal_key_ranges(extend_lens, seq_lens):
     """Per new token, the key range ``[ks, ke)`` in a batch-concatenated key axis.
 
@@ -205,17 +252,21 @@ def softmax_attention(q, keys, values, scale):
 
 
 def paged_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, page_size,
-                  scale, causal=True):
+                  scale, causal=True, window_left=-1, attn_chunk=0):
     """Varlen extend/prefill over a paged cache.
 
     [FA] ``forward_extend``: ``flash_attn_with_kvcache`` with
     ``cache_seqlens`` = prefix + new length, ``cu_seqlens_q`` over the new
     tokens and ``causal=True``; the new tokens' keys are already in the cache, so
-    each row attends to prefix and new keys through the page table.
+    each row attends to prefix and new keys through the page table. With a
+    sliding window or local chunks (``key_lower_bound``; causal only) row j
+    sees keys ``[key_lower_bound(p), p]``, ``p = L - M + j``.
 
     q: [total_q, Hq, D]; caches: [pages, P, Hkv, Dk|Dv]. Returns
     O [total_q, Hq, Dv] and LSE [total_q, Hq], float64.
     """
+    if (window_left >= 0 or attn_chunk > 0) and not causal:
+        raise ValueError("lower-bound masks apply to causal rows")
     q = np.asarray(q, dtype=np.float64)
     k_cache = np.asarray(k_cache)
     v_cache = np.asarray(v_cache)
@@ -233,9 +284,10 @@ def paged_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, page_s
         counts = visible_key_counts(q1 - q0, L, causal)
         for j in range(q1 - q0):
             n = int(counts[j])
+            lo = key_lower_bound(n - 1, window_left, attn_chunk) if causal else 0
             for h in range(num_q_heads):
                 kvh = kv_head_of(h, num_q_heads, num_kv_heads)
-                o, l_ = softmax_attention(q[q0 + j, h], keys[:n, kvh], vals[:n, kvh], scale)
+                o, l_ = softmax_attention(q[q0 + j, h], keys[lo:n, kvh], vals[lo:n, kvh], scale)
                 out[q0 + j, h] = o
                 lse[q0 + j, h] = l_
     return out, lse
@@ -275,7 +327,7 @@ def paged_prefill_append(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens,
 
 
 def paged_decode_splitkv(q, k_cache, v_cache, page_table, kv_lens, page_size, scale,
-                         kv_chunk, num_splits):
+                         kv_chunk, num_splits, window_left=-1, attn_chunk=0):
     """Decode (one new token per request) with the key axis cut into chunks.
 
     Split ``s`` covers keys ``[s*C, min((s+1)*C, L_b))`` and yields the partial
@@ -284,7 +336,9 @@ def paged_decode_splitkv(q, k_cache, v_cache, page_table, kv_lens, page_size, sc
     [DCA] ``_dual_chunk_flash_attn_decoding`` runs several paged decodes over
     disjoint key ranges with ``return_softmax_lse=True`` and merges them, and
     ``_dual_chunk_flash_attn_decoding_with_exp_sums`` fixes empty ranges to
-    ``(0, -inf)``. ``kv_chunk = 0`` means a single split over all keys.
+    ``(0, -inf)``. ``kv_chunk = 0`` means a single split over all keys. With a
+    sliding window or local chunks the query (position ``L - 1``) sees keys
+    ``[key_lower_bound(L - 1), L)`` and each split keeps its part of them.
 
     q: [B, Hq, D]. Returns o_partial [S, B, Hq, Dv] and lse_partial [S, B, Hq].
     """
@@ -303,6 +357,8 @@ def paged_decode_splitkv(q, k_cache, v_cache, page_table, kv_lens, page_size, sc
                 lo, hi = (0, L) if s == 0 else (L, L)
             else:
                 lo, hi = min(s * kv_chunk, L), min((s + 1) * kv_chunk, L)
+            if L > 0:
+                lo = min(max(lo, key_lower_bound(L - 1, window_left, attn_chunk)), hi)
             for h in range(num_q_heads):
                 kvh = kv_head_of(h, num_q_heads, num_kv_heads)
                 o, l_ = softmax_attention(q[b, h], keys[lo:hi, kvh], vals[lo:hi, kvh], scale)

@@ -31,11 +31,12 @@ def dense_request_kv(cache, req_to_token, row, L):
     return flat[slots].to(torch.float64)
 
 
-def sdpa_reference(q_rows, keys, vals, scale, causal):
+def sdpa_reference(q_rows, keys, vals, scale, causal, window_left=-1):
     """torch SDPA (float64, explicit mask) and torch.logsumexp for LSE.
 
     q_rows [M, Hq, D]; keys/vals [L, Hkv, D]. Causal uses torch.tril's
-    bottom-right diagonal offset L - M.
+    bottom-right diagonal offset L - M; a sliding window of W keys to the left
+    intersects it with torch.triu at offset L - M - W (a band).
     """
     M, Hq, _ = q_rows.shape
     L, Hkv, _ = keys.shape
@@ -46,6 +47,8 @@ def sdpa_reference(q_rows, keys, vals, scale, causal):
     mask = torch.ones(M, L, dtype=torch.bool)
     if causal:
         mask = torch.tril(mask, diagonal=L - M)
+    if window_left >= 0:
+        mask = torch.triu(mask, diagonal=L - M - window_left)
     o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
     logits = torch.matmul(q, k.transpose(-1, -2)) * scale
     logits = logits.masked_fill(~mask, -math.inf)
@@ -495,3 +498,127 @@ def test_planted_append_slot_mistake_is_caught(monkeypatch):
                         if dtype is np.int64 else real(a, dtype=dtype))
     bad = ref.kv_append(kc, vc, loc % (kc.shape[0] * kc.shape[1] - 1), kn, vn)
     assert not np.array_equal(bad[0], good[0])
+
+
+# --- lower-bound masks: sliding window (W, 0) and chunked local attention -----
+
+def test_local_attention_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "local_attention_example.json")))
+    C = g["attn_chunk_size"]
+    M, L = g["q_seqlens"][0], g["kv_seqlens"][0]
+    drawn = []
+    for j in range(M):
+        p = L - M + j
+        lo = oracle.key_lower_bound(p, attn_chunk=C)
+        drawn.append("".join("1" if lo <= k <= p else "." for k in range(L)))
+    assert drawn == g["batch0_local_mask"]
+    cu = oracle.cu_seqlens(g["q_seqlens"])
+    vb = oracle.local_attention_virtual_batches(C, cu, g["kv_seqlens"])
+    assert [x[2] for x in vb] == g["q_seqlens_local"]
+    assert [x[4] for x in vb] == g["seqlens_k_local"]
+
+
+def _window_case():
+    return workloads.make_prefill_case(33, prefix_lens=[0, 9, 21, 2], extend_lens=[11, 3, 8, 6],
+                                       num_q_heads=4, num_kv_heads=2, head_dim=8, page_size=4,
+                                       num_pages=60, dtype=torch.float32)
+
+
+def _oracle_prefill(case, **kw):
+    pt, kl, _ = oracle.page_table_strided(i64(case.req_to_token), i64(case.req_pool_indices),
+                                          i64(case.seq_lens), case.page_size, case.table_width)
+    return oracle.paged_prefill(f64(case.q), f64(case.k_cache), f64(case.v_cache), pt,
+                                i64(case.cu_seqlens_q), kl, case.page_size, case.scale, **kw)
+
+
+@pytest.mark.parametrize("W", [0, 3, 7, 40])
+def test_sliding_window_prefill_matches_sdpa_band(W):
+    case = _window_case()
+    o, lse = _oracle_prefill(case, window_left=W)
+    cu = i64(case.cu_seqlens_q)
+    qd = case.q.to(torch.float64)
+    for b in range(len(cu) - 1):
+        L = int(case.seq_lens[b])
+        row = int(case.req_pool_indices[b])
+        K = dense_request_kv(case.k_cache, case.req_to_token, row, L)
+        V = dense_request_kv(case.v_cache, case.req_to_token, row, L)
+        o_ref, l_ref = sdpa_reference(qd[cu[b]:cu[b + 1]], K, V, case.scale, causal=True,
+                                      window_left=W)
+        assert np.abs(o[cu[b]:cu[b + 1]] - o_ref).max() < 1e-12
+        assert np.abs(lse[cu[b]:cu[b + 1]] - l_ref).max() < 1e-12
+
+
+def test_window_edge_cases():
+    case = _window_case()
+    plain = _oracle_prefill(case)
+    wide = _oracle_prefill(case, window_left=10_000)
+    assert np.array_equal(plain[0], wide[0]) and np.array_equal(plain[1], wide[1])
+    # W = 0: each row sees only its own key -> O = v_p, LSE = scale * q . k_p
+    o, lse = _oracle_prefill(case, window_left=0)
+    cu = i64(case.cu_seqlens_q)
+    for b in range(len(cu) - 1):
+        L, M = int(case.seq_lens[b]), int(cu[b + 1] - cu[b])
+        row = int(case.req_pool_indices[b])
+        K = dense_request_kv(case.k_cache, case.req_to_token, row, L).numpy()
+        V = dense_request_kv(case.v_cache, case.req_to_token, row, L).numpy()
+        for j in range(M):
+            p = L - M + j
+            for h in range(4):
+                kvh = h // 2
+                assert np.allclose(o[cu[b] + j, h], V[p, kvh], atol=1e-15)
+                s = case.scale * float(np.dot(f64(case.q)[cu[b] + j, h], K[p, kvh]))
+                assert abs(lse[cu[b] + j, h] - s) < 1e-12
+
+
+@pytest.mark.parametrize("C", [4, 8, 16])
+def test_local_chunks_equal_virtual_batches(C):
+    """The masked definition against the pages' formulation: each virtual
+    batch is an ordinary causal extend over its own key range."""
+    case = _window_case()
+    o, lse = _oracle_prefill(case, attn_chunk=C)
+    cu = i64(case.cu_seqlens_q)
+    qd = f64(case.q)
+    for b, qs, qn, k0, kn in oracle.local_attention_virtual_batches(C, cu, i64(case.seq_lens)):
+        row = int(case.req_pool_indices[b])
+        L = int(case.seq_lens[b])
+        K = dense_request_kv(case.k_cache, case.req_to_token, row, L).numpy()[k0:k0 + kn]
+        V = dense_request_kv(case.v_cache, case.req_to_token, row, L).numpy()[k0:k0 + kn]
+        vo, vl = oracle.paged_prefill(qd[qs:qs + qn], K[:, None], V[:, None],
+                                      np.arange(kn)[None, :], np.array([0, qn]),
+                                      np.array([kn]), 1, case.scale)
+        assert np.abs(o[qs:qs + qn] - vo).max() < 1e-12
+        assert np.abs(lse[qs:qs + qn] - vl).max() < 1e-12
+
+
+@pytest.mark.parametrize("mask", [dict(window_left=5), dict(attn_chunk=8)])
+def test_masked_decode_split_then_merge_equals_unsplit(mask):
+    case = small_decode(page_size=4)
+    pt, kl, _ = oracle.page_table_strided(i64(case.req_to_token), i64(case.req_pool_indices),
+                                          i64(case.seq_lens), case.page_size, case.table_width)
+    args = (f64(case.q), f64(case.k_cache), f64(case.v_cache), pt, kl, case.page_size, case.scale)
+    o1, l1 = oracle.paged_decode_splitkv(*args, 0, 1, **mask)
+    op, lp = oracle.paged_decode_splitkv(*args, 8, 4, **mask)
+    o2, l2 = oracle.merge_state(op, lp)
+    assert np.abs(o1[0] - o2).max() < 1e-12 and np.abs(l1[0] - l2).max() < 1e-12
+    # the masked decode of position L-1 is the last row of a masked extend over the request
+    for b in range(len(kl)):
+        L = int(kl[b])
+        if L == 0:
+            continue
+        lo = oracle.key_lower_bound(L - 1, **mask)
+        row = int(case.req_pool_indices[b])
+        K = dense_request_kv(case.k_cache, case.req_to_token, row, L).numpy()
+        V = dense_request_kv(case.v_cache, case.req_to_token, row, L).numpy()
+        for h in range(8):
+            o_ref, l_ref = oracle.softmax_attention(f64(case.q)[b, h], K[lo:, h // 4],
+                                                    V[lo:, h // 4], case.scale)
+            assert np.abs(o1[0, b, h] - o_ref).max() < 1e-15 and abs(l1[0, b, h] - l_ref) < 1e-15
+
+
+def test_planted_window_off_by_one_is_caught(monkeypatch):
+    real = ref.key_lower_bound
+    monkeypatch.setattr(ref, "key_lower_bound",
+                        lambda pos, window_left=-1, attn_chunk=0:
+                        real(pos, window_left, attn_chunk) + (1 if window_left >= 0 else 0))
+    with pytest.raises(AssertionError):
+        test_sliding_window_prefill_matches_sdpa_band(3)
