@@ -102,6 +102,13 @@ pkv_status_t build_page_table(const int32_t* req_to_token, int64_t req_to_token_
  * New row j sits at position L_b - M_b + j and, when causal, sees keys
  * [0, L_b - M_b + j] (bottom-right alignment, [NSA] _cal_indexer_k_start_end);
  * otherwise all L_b keys. q head h reads kv head h / (Hq / Hkv).
+ * Masks on top of causal ([FA] forward_extend window_size and
+ * make_local_attention_virtual_batches); at most one of the two is set:
+ *   window_left = W >= 0: sliding window (W, 0), the row at position p sees
+ *          keys [max(0, p - W), p] (W + 1 keys); -1 turns it off.
+ *   attn_chunk = C > 0: chunked local attention, the row at position p sees
+ *          keys [floor(p / C) * C, p], the same as splitting each request into
+ *          C-aligned virtual requests; 0 turns it off.
  *
  * q        [total_q, num_q_heads, head_dim]         dtype
  * k_cache, v_cache [num_pages, page_size, num_kv_heads, head_dim] dtype
@@ -119,7 +126,8 @@ pkv_status_t build_page_table(const int32_t* req_to_token, int64_t req_to_token_
  *          fp32 (out) or NULL.
  * Supported: dtype PKV_BF16, head_dim 64 or 128, Hq % Hkv == 0,
  * Hq / Hkv <= 16, causal 0 or 1, num_pages * page_size < 2^31.
- * Errors: PKV_EINVAL for bad sizes, NULL pointers or a short workspace;
+ * Errors: PKV_EINVAL for bad sizes, NULL pointers, a short workspace,
+ * window_left < -1, attn_chunk < 0, both masks set, or a mask with causal 0;
  * PKV_EUNSUPPORTED outside the supported set.
  */
 size_t paged_attn_varlen_prefill_workspace_size(int32_t batch, int32_t total_q,
@@ -133,7 +141,8 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
                                        int32_t batch, int32_t total_q, int32_t max_seqlen_q,
                                        int32_t max_seqlen_k, int32_t num_q_heads,
                                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                                       float softmax_scale, int32_t causal, void* workspace,
+                                       float softmax_scale, int32_t causal, int32_t window_left,
+                                       int32_t attn_chunk, void* workspace,
                                        size_t workspace_bytes, void* out, float* lse,
                                        void* stream);
 
@@ -176,9 +185,9 @@ pkv_status_t paged_attn_varlen_prefill_append(
     const int32_t* page_table, int32_t pt_stride, const int32_t* cu_seqlens_q,
     const int32_t* kv_lens, int32_t batch, int32_t total_q, int32_t max_seqlen_q,
     int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t page_size, float softmax_scale, int32_t causal, const void* k_new, const void* v_new,
-    const int32_t* out_cache_loc, void* workspace, size_t workspace_bytes, void* out, float* lse,
-    void* stream);
+    int32_t page_size, float softmax_scale, int32_t causal, int32_t window_left,
+    int32_t attn_chunk, const void* k_new, const void* v_new, const int32_t* out_cache_loc,
+    void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
  * paged_attn_decode_splitkv -- one query token per request, key axis split.
@@ -188,6 +197,11 @@ pkv_status_t paged_attn_varlen_prefill_append(
  * Split s of request b covers keys [s * kv_chunk, min((s + 1) * kv_chunk, L_b));
  * it yields the attention output normalised over that range alone, O_s, and
  * LSE_s; an empty range yields (0, -inf). kv_chunk == 0 means one split.
+ * The query sits at position L_b - 1. window_left = W >= 0 keeps only keys
+ * [max(0, L_b - 1 - W), L_b - 1] and attn_chunk = C > 0 only keys
+ * [floor((L_b - 1) / C) * C, L_b - 1] ([FA] forward_decode window_size, local
+ * attention); splits outside the kept range are empty. -1 / 0 turn them off;
+ * at most one may be set (PKV_EINVAL otherwise, or for W < -1 or C < 0).
  *
  * q        [batch, num_q_heads, head_dim] dtype
  * k_cache, v_cache [num_pages, page_size, num_kv_heads, head_dim] dtype
@@ -209,6 +223,7 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
                                        const int32_t* kv_lens, int32_t batch,
                                        int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t page_size, float softmax_scale,
+                                       int32_t window_left, int32_t attn_chunk,
                                        int32_t kv_chunk, int32_t num_splits, float* o_partial,
                                        float* lse_partial, void* out, float* lse, void* stream);
 

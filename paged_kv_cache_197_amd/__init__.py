@@ -68,15 +68,15 @@ _SIGNATURES = {
                                                         _I32]),
     "paged_attn_varlen_prefill": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _P,
                                                  _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
-                                                 _F, _I32, _P, _SZ, _P, _P, _P]),
+                                                 _F, _I32, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "paged_kv_append": (ctypes.c_int, [_P, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _I64, _P]),
     "paged_attn_varlen_prefill_append": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P,
                                                         _P, _I32, _I32, _I32, _I32, _I32, _I32,
-                                                        _I32, _I32, _F, _I32, _P, _P, _P, _P,
-                                                        _SZ, _P, _P, _P]),
+                                                        _I32, _I32, _F, _I32, _I32, _I32, _P, _P,
+                                                        _P, _P, _SZ, _P, _P, _P]),
     "paged_attn_decode_splitkv": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _I32,
-                                                 _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _P,
-                                                 _P, _P, _P]),
+                                                 _I32, _I32, _I32, _I32, _F, _I32, _I32, _I32,
+                                                 _I32, _P, _P, _P, _P, _P]),
     "merge_state": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P, _P]),
     "sparse_topk_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "sparse_topk_decode": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _I64, _P, _P, _I32, _I32, _I32,
@@ -182,10 +182,12 @@ def build_page_table(req_to_token, req_pool_indices, seq_lens, page_size, width,
 
 
 def paged_attn_decode_splitkv(q, k_cache, v_cache, page_table, kv_lens, softmax_scale, *,
-                              kv_chunk=0, num_splits=1, out=None, lse=None, o_partial=None,
-                              lse_partial=None):
+                              kv_chunk=0, num_splits=1, window_left=-1, attn_chunk=0, out=None,
+                              lse=None, o_partial=None, lse_partial=None):
     """Split-KV paged decode. Returns (out, lse) for one split, else
-    (o_partial [S,B,Hq,D] fp32, lse_partial [S,B,Hq] fp32)."""
+    (o_partial [S,B,Hq,D] fp32, lse_partial [S,B,Hq] fp32).
+    window_left >= 0: sliding window (keys [L-1-W, L-1]); attn_chunk > 0:
+    chunked local attention (keys from the start of the query's chunk)."""
     lib = load_library()
     dev = q.device
     _need(q, "q", None, dev, 3)
@@ -211,8 +213,8 @@ def paged_attn_decode_splitkv(q, k_cache, v_cache, page_table, kv_lens, softmax_
             lse_partial = torch.empty((num_splits, batch, hq), dtype=torch.float32, device=dev)
     st = lib.paged_attn_decode_splitkv(
         _ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(pt),
-        pt.shape[1], _ptr(kl), batch, hq, hkv, d, page_size, float(softmax_scale), int(kv_chunk),
-        int(num_splits), _ptr(o_partial), _ptr(lse_partial),
+        pt.shape[1], _ptr(kl), batch, hq, hkv, d, page_size, float(softmax_scale),
+        int(window_left), int(attn_chunk), int(kv_chunk), int(num_splits), _ptr(o_partial), _ptr(lse_partial),
         _ptr(out) if num_splits == 1 else None, _ptr(lse) if num_splits == 1 else None,
         _stream(dev))
     _check("paged_attn_decode_splitkv", st)
@@ -267,7 +269,7 @@ def paged_kv_append(k_new, v_new, out_cache_loc, k_cache, v_cache):
 
 def paged_attn_varlen_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens,
                               max_seqlen_q, softmax_scale, *, max_seqlen_k=None, causal=True,
-                              workspace=None, out=None, lse=None, return_lse=True,
+                              window_left=-1, attn_chunk=0, workspace=None, out=None, lse=None, return_lse=True,
                               k_new=None, v_new=None, out_cache_loc=None):
     """Causal varlen extend over a paged cache. Returns (out, lse or None).
 
@@ -277,7 +279,9 @@ def paged_attn_varlen_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_
     zero (a fresh zeroed one is made when None; the call leaves them zero).
     With k_new / v_new [total_q, Hkv, D] and out_cache_loc [total_q], the new
     tokens are first written into the cache at those slots (the extend step
-    with its cache write, one call)."""
+    with its cache write, one call). window_left >= 0 (sliding window: row
+    at position p sees keys [p-W, p]) or attn_chunk > 0 (chunked local
+    attention: keys from the start of p's chunk) narrow causal rows."""
     lib = load_library()
     dev = q.device
     _need(q, "q", torch.bfloat16, dev, 3)
@@ -305,7 +309,7 @@ def paged_attn_varlen_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_
             _ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(pt),
             pt.shape[1], _ptr(cu), _ptr(kl), batch, total_q, int(max_seqlen_q),
             int(max_seqlen_k), hq, hkv, d, page_size, float(softmax_scale), int(bool(causal)),
-            _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
+            int(window_left), int(attn_chunk), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
         _check("paged_attn_varlen_prefill", st)
         return out, lse
     if k_new is None or v_new is None or out_cache_loc is None:
@@ -320,7 +324,8 @@ def paged_attn_varlen_prefill(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_
     st = lib.paged_attn_varlen_prefill_append(
         _ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(pt),
         pt.shape[1], _ptr(cu), _ptr(kl), batch, total_q, int(max_seqlen_q), int(max_seqlen_k),
-        hq, hkv, d, page_size, float(softmax_scale), int(bool(causal)), _ptr(k_new), _ptr(v_new),
+        hq, hkv, d, page_size, float(softmax_scale), int(bool(causal)), int(window_left),
+        int(attn_chunk), _ptr(k_new), _ptr(v_new),
         _ptr(loc), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
     _check("paged_attn_varlen_prefill_append", st)
     return out, lse

@@ -179,6 +179,7 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
                                        const int32_t* kv_lens, int32_t batch,
                                        int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t page_size, float softmax_scale,
+                                       int32_t window_left, int32_t attn_chunk,
                                        int32_t kv_chunk, int32_t num_splits, float* o_partial,
                                        float* lse_partial, void* out, float* lse, void* stream) {
   PKV_REQUIRE(dtype == PKV_F32 || dtype == PKV_BF16, PKV_EUNSUPPORTED,
@@ -195,6 +196,9 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
   PKV_REQUIRE(page_size >= 1 && pt_stride >= 1 && num_pages >= 1, PKV_EINVAL,
               "decode: page_size %d pt_stride %d num_pages %lld", page_size, pt_stride,
               (long long)num_pages);
+  PKV_REQUIRE(window_left >= -1 && attn_chunk >= 0 && !(window_left >= 0 && attn_chunk > 0),
+              PKV_EINVAL, "decode: window_left %d / attn_chunk %d (at most one of them)",
+              window_left, attn_chunk);
   PKV_REQUIRE(kv_chunk >= 0, PKV_EINVAL, "decode: kv_chunk %d < 0", kv_chunk);
   PKV_REQUIRE(kv_chunk % page_size == 0, PKV_EINVAL,
               "decode: kv_chunk %d is not a multiple of page_size %d", kv_chunk, page_size);
@@ -233,6 +237,8 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
                          : static_cast<int32_t>(((cap < 0x40000000LL ? cap : 0x40000000LL) + 31) /
                                                 32 * 32);
   a.num_splits = num_splits;
+  a.window_left = window_left;
+  a.attn_chunk = attn_chunk;
   a.o_part = o_partial;
   a.lse_part = lse_partial;
   a.out = out;
@@ -265,7 +271,8 @@ static pkv_status_t prefill_prepare(const void* q, int32_t dtype, const void* k_
                                     int32_t batch, int32_t total_q, int32_t max_seqlen_q,
                                     int32_t max_seqlen_k, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                                    float softmax_scale, int32_t causal, void* workspace,
+                                    float softmax_scale, int32_t causal, int32_t window_left,
+                                    int32_t attn_chunk, void* workspace,
                                     size_t workspace_bytes, void* out, float* lse,
                                     pkv::PrefillArgs& a, bool* nothing) {
   *nothing = false;
@@ -288,6 +295,11 @@ static pkv_status_t prefill_prepare(const void* q, int32_t dtype, const void* k_
               "prefill: a cache of %lld slots (more than 2^31)",
               (long long)(num_pages * page_size));
   PKV_REQUIRE(causal == 0 || causal == 1, PKV_EINVAL, "prefill: causal %d", causal);
+  PKV_REQUIRE(window_left >= -1 && attn_chunk >= 0 && !(window_left >= 0 && attn_chunk > 0),
+              PKV_EINVAL, "prefill: window_left %d / attn_chunk %d (at most one of them)",
+              window_left, attn_chunk);
+  PKV_REQUIRE(causal == 1 || (window_left < 0 && attn_chunk == 0), PKV_EINVAL,
+              "prefill: a sliding window or local chunks need causal rows");
   PKV_REQUIRE(max_seqlen_q <= total_q, PKV_EINVAL, "prefill: max_seqlen_q %d > total_q %d",
               max_seqlen_q, total_q);
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) {
@@ -328,6 +340,8 @@ static pkv_status_t prefill_prepare(const void* q, int32_t dtype, const void* k_
                       : nullptr;
   a.out = out;
   a.lse = lse;
+  a.window_left = window_left;
+  a.attn_chunk = attn_chunk;
   return pkv_host::ok();
 }
 
@@ -340,7 +354,8 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
                                        int32_t batch, int32_t total_q, int32_t max_seqlen_q,
                                        int32_t max_seqlen_k, int32_t num_q_heads,
                                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                                       float softmax_scale, int32_t causal, void* workspace,
+                                       float softmax_scale, int32_t causal, int32_t window_left,
+                                       int32_t attn_chunk, void* workspace,
                                        size_t workspace_bytes, void* out, float* lse,
                                        void* stream) {
   pkv::PrefillArgs a;
@@ -348,7 +363,8 @@ pkv_status_t paged_attn_varlen_prefill(const void* q, int32_t dtype, const void*
   const pkv_status_t st = prefill_prepare(
       q, dtype, k_cache, v_cache, num_pages, page_table, pt_stride, cu_seqlens_q, kv_lens, batch,
       total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, page_size,
-      softmax_scale, causal, workspace, workspace_bytes, out, lse, a, &nothing);
+      softmax_scale, causal, window_left, attn_chunk, workspace, workspace_bytes, out, lse, a,
+      &nothing);
   if (st != PKV_OK || nothing) return st;
   return pkv_host::from_hip(pkv_launch::prefill(a, head_dim, static_cast<hipStream_t>(stream)),
                             "prefill launch");
@@ -392,9 +408,9 @@ pkv_status_t paged_attn_varlen_prefill_append(
     const int32_t* page_table, int32_t pt_stride, const int32_t* cu_seqlens_q,
     const int32_t* kv_lens, int32_t batch, int32_t total_q, int32_t max_seqlen_q,
     int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t page_size, float softmax_scale, int32_t causal, const void* k_new, const void* v_new,
-    const int32_t* out_cache_loc, void* workspace, size_t workspace_bytes, void* out, float* lse,
-    void* stream) {
+    int32_t page_size, float softmax_scale, int32_t causal, int32_t window_left,
+    int32_t attn_chunk, const void* k_new, const void* v_new, const int32_t* out_cache_loc,
+    void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
   // every check before anything is enqueued: the cache is written only when
   // the attention will run too
   pkv::PrefillArgs a;
@@ -402,7 +418,8 @@ pkv_status_t paged_attn_varlen_prefill_append(
   pkv_status_t st = prefill_prepare(
       q, dtype, k_cache, v_cache, num_pages, page_table, pt_stride, cu_seqlens_q, kv_lens, batch,
       total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, page_size,
-      softmax_scale, causal, workspace, workspace_bytes, out, lse, a, &nothing);
+      softmax_scale, causal, window_left, attn_chunk, workspace, workspace_bytes, out, lse, a,
+      &nothing);
   if (st != PKV_OK) return st;
   int64_t row_bytes = 0;
   st = append_check("paged_attn_varlen_prefill_append", k_new, v_new, dtype, out_cache_loc,

@@ -34,7 +34,18 @@ struct DecodeArgs {
   float* lse_part;    // [S, B, Hq]
   void* out;          // [B, Hq, D] dtype (num_splits == 1)
   float* lse;         // [B, Hq] or nullptr
+  int32_t window_left;   // >= 0: sliding window (W, 0); else none
+  int32_t attn_chunk;    // > 0: chunked local attention; else none
 };
+
+// First key a query at absolute position pos may see: pos - W for a sliding
+// window (W, 0) (inclusive on both sides), the start of pos's aligned block
+// for chunked local attention, else 0. The last key is pos (causal).
+__host__ __device__ inline int key_lower_bound(int pos, int window_left, int attn_chunk) {
+  if (window_left >= 0) return pos - window_left > 0 ? pos - window_left : 0;
+  if (attn_chunk > 0) return pos / attn_chunk * attn_chunk;
+  return 0;
+}
 
 struct PrefillArgs {
   const void* q;
@@ -57,6 +68,8 @@ struct PrefillArgs {
   int32_t* counters;    // [qtile_slots, Hkv, ceil(G / 4)], zero between calls
   void* out;
   float* lse;
+  int32_t window_left;  // >= 0: sliding window (W, 0); else none (causal only)
+  int32_t attn_chunk;   // > 0: chunked local attention; else none (causal only)
 };
 
 struct SparseArgs {

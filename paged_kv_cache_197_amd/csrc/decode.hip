@@ -159,7 +159,7 @@ struct DecodeKernel {
   }
 
   // One tile: S^T = K . Q^T, online softmax (base 2), O^T += V^T . P^T.
-  static __device__ __forceinline__ void consume(const Tile& cur, int ts, int end, int g,
+  static __device__ __forceinline__ void consume(const Tile& cur, int ts, int end, int lo, int g,
                                                  float scale_log2, const Chunk<KDW> (&qop)[NK],
                                                  f32x4 (&acc)[NB], float& m_run, float& l_run) {
     f32x4 st[2];
@@ -184,10 +184,11 @@ struct DecodeKernel {
 
     float x[8];
     const int valid = end - ts;  // tokens of this tile inside the split (may exceed 32)
+    const int first = lo - ts;   // tokens before it are below the key window (first tile only)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float sv = st[e >> 2][e & 3] * scale_log2;
-      x[e] = (tok_of(g, e) < valid) ? sv : neg_inf();
+      x[e] = (tok_of(g, e) < valid && tok_of(g, e) >= first) ? sv : neg_inf();
     }
     float mt = x[0];
 #pragma unroll
@@ -256,11 +257,15 @@ struct DecodeKernel {
 
     const int64_t cap = static_cast<int64_t>(a.pt_stride) * a.page_size;
     const int L = static_cast<int>(min<int64_t>(max(a.kv_lens[b], 0), cap));
-    const int start = static_cast<int>(min<int64_t>(static_cast<int64_t>(s) * a.chunk, L));
-    const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(start) + a.chunk, L));
+    const int start0 = static_cast<int>(min<int64_t>(static_cast<int64_t>(s) * a.chunk, L));
+    const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(start0) + a.chunk, L));
+    // first visible key under a sliding window / local chunks; tiles start on
+    // a multiple of 32 (splits do), keys below lo are masked
+    const int lo = L > 0 ? key_lower_bound(L - 1, a.window_left, a.attn_chunk) : 0;
+    const int start = max(start0, lo / 32 * 32);
 
     const bool single = (a.num_splits == 1);
-    if (start >= end) {
+    if (max(start0, lo) >= end) {
       // empty split: (0, -inf)
       for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
         const int hh = h0 + i / D;
@@ -333,7 +338,7 @@ struct DecodeKernel {
           fetch_data(a, slot_base(a, raw_n, ts, end, lane), ts, end, kvh, c, g, tb);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-        consume(ta, start + 32 * tile, end, g, a.scale_log2, qop, acc, m_run, l_run);
+        consume(ta, start + 32 * tile, end, lo, g, a.scale_log2, qop, acc, m_run, l_run);
         tile += 4;
         if (tile > last) break;
         raw_n = raw_nn;
@@ -343,7 +348,7 @@ struct DecodeKernel {
           fetch_data(a, slot_base(a, raw_n, ts, end, lane), ts, end, kvh, c, g, ta);
         }
         __builtin_amdgcn_sched_barrier(0);
-        consume(tb, start + 32 * tile, end, g, a.scale_log2, qop, acc, m_run, l_run);
+        consume(tb, start + 32 * tile, end, lo, g, a.scale_log2, qop, acc, m_run, l_run);
         tile += 4;
         if (tile > last) break;
         raw_n = raw_nn;
@@ -507,8 +512,10 @@ struct DecodeGroupKernel {
     }
   }
 
+  template <bool WINDOW>
   static __device__ __forceinline__ void compute(const char* my, int c, int g, int valid,
-                                                 float scale_log2, const u32x4 (&qop)[8],
+                                                 int first, float scale_log2,
+                                                 const u32x4 (&qop)[8],
                                                  f32x4 (&acc)[16], float& m_run, float& l_run) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -518,7 +525,9 @@ struct DecodeGroupKernel {
     }
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (4 * g + i < valid) ? s[i] * scale_log2 : neg_inf();
+    for (int i = 0; i < 4; ++i)
+      x[i] = (4 * g + i < valid && (!WINDOW || 4 * g + i >= first)) ? s[i] * scale_log2
+                                                                     : neg_inf();
     float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mt = max_over_groups16(mt);
     const float m_new = fmaxf(m_run, mt);
@@ -560,7 +569,7 @@ struct DecodeGroupKernel {
     }
   }
 
-  template <bool UNIFORM>
+  template <bool UNIFORM, bool WINDOW>
   static __device__ void run(const DecodeArgs& a) {
     extern __shared__ __align__(16) char smem[];
     __shared__ float sm_m[4][16];
@@ -581,11 +590,15 @@ struct DecodeGroupKernel {
 
     const int64_t cap = static_cast<int64_t>(a.pt_stride) * a.page_size;
     const int L = static_cast<int>(min<int64_t>(max(a.kv_lens[b], 0), cap));
-    const int start = static_cast<int>(min<int64_t>(static_cast<int64_t>(s) * a.chunk, L));
-    const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(start) + a.chunk, L));
+    const int start0 = static_cast<int>(min<int64_t>(static_cast<int64_t>(s) * a.chunk, L));
+    const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(start0) + a.chunk, L));
+    // first visible key under a sliding window / local chunks; tiles start on
+    // a multiple of TT (splits do), keys below lo are masked
+    const int lo = (WINDOW && L > 0) ? key_lower_bound(L - 1, a.window_left, a.attn_chunk) : 0;
+    const int start = WINDOW ? max(start0, lo / TT * TT) : start0;
     const bool single = (a.num_splits == 1);
 
-    if (start >= end) {   // empty split: (0, -inf)
+    if (max(start0, lo) >= end) {   // empty split: (0, -inf)
       for (int i = threadIdx.x; i < ncol * D; i += blockDim.x) {
         const int64_t row = static_cast<int64_t>(b) * a.hq + h0 + i / D;
         const int d = i % D;
@@ -653,7 +666,8 @@ struct DecodeGroupKernel {
         if (more)
           load<UNIFORM>(a, raw_n, start + TT * (tile + 4), end, lane, row_bytes, col, st);
         __builtin_amdgcn_sched_barrier(0);   // the next tile's loads go out before the MFMAs
-        compute(my, c, g, end - (start + TT * tile), a.scale_log2, qop, acc, m_run, l_run);
+        compute<WINDOW>(my, c, g, end - (start + TT * tile), lo - (start + TT * tile),
+                        a.scale_log2, qop, acc, m_run, l_run);
         if (!more) break;
         tile += 4;
         stash(my, lane, st);   // same wave: its LDS reads above complete first
@@ -734,9 +748,9 @@ struct DecodeGroupKernel {
   }
 };
 
-template <int D, bool UNIFORM>
+template <int D, bool UNIFORM, bool WINDOW>
 __global__ __launch_bounds__(256, 2) void decode_group_kernel(DecodeArgs a) {
-  DecodeGroupKernel<D>::template run<UNIFORM>(a);
+  DecodeGroupKernel<D>::template run<UNIFORM, WINDOW>(a);
 }
 
 // bf16 tiles fit two workgroups per CU (<= 256 VGPRs); fp32 tiles are twice
@@ -780,10 +794,22 @@ static hipError_t launch_decode_group(const pkv::DecodeArgs& a, hipStream_t stre
   const dim3 grid(static_cast<unsigned>(a.hkv / HPW) * a.batch * a.num_splits);
   constexpr unsigned lds = pkv::DecodeGroupKernel<D>::LDS_BYTES;
   // whole 16-token tiles on one page: page_size % 16 == 0 (splits start on pages)
-  if (a.page_size % 16 == 0)
-    hipLaunchKernelGGL((pkv::decode_group_kernel<D, true>), grid, dim3(256), lds, stream, a);
-  else
-    hipLaunchKernelGGL((pkv::decode_group_kernel<D, false>), grid, dim3(256), lds, stream, a);
+  // (a sliding window or local chunks take the variant with the lower key mask)
+  const bool window = a.window_left >= 0 || a.attn_chunk > 0;
+  if (a.page_size % 16 == 0) {
+    if (window)
+      hipLaunchKernelGGL((pkv::decode_group_kernel<D, true, true>), grid, dim3(256), lds, stream, a);
+    else
+      hipLaunchKernelGGL((pkv::decode_group_kernel<D, true, false>), grid, dim3(256), lds, stream,
+                         a);
+  } else {
+    if (window)
+      hipLaunchKernelGGL((pkv::decode_group_kernel<D, false, true>), grid, dim3(256), lds, stream,
+                         a);
+    else
+      hipLaunchKernelGGL((pkv::decode_group_kernel<D, false, false>), grid, dim3(256), lds, stream,
+                         a);
+  }
   return hipGetLastError();
 }
 

@@ -182,20 +182,21 @@ struct PrefillKernel {
   // tile run on the VALU. Returns the next tile's S^T.
   // m_run is a reference max in raw score units; scale_log2 > 0 is applied
   // inside the exponent (exp2(s * c - m * c)). Masked tiles apply the per-row
-  // key limit (key kt*32 + rho(h, r) is visible iff rho(h, r) - 4h < rel).
+  // key window (key kt*32 + rho(h, r) is visible iff rel_lo <= rho(h, r) - 4h
+  // < rel).
   static __device__ __forceinline__ f32x16 softmax_pv(f32x16 s, const char* stage_v,
                                                       const int (&vofs)[2][NB], bool masked,
-                                                      int rel, int h, float scale_log2,
+                                                      int rel, int rel_lo, int h, float scale_log2,
                                                       const u32x4 (&kw)[NKS],
                                                       const u32x4 (&qop)[NKS], f32x16 (&acc)[NB],
                                                       float& m_run, float& l_run) {
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = s[r];
-    if (masked) {   // wave-uniform: only tiles that reach past some row's limit
+    if (masked) {   // wave-uniform: only tiles that reach past some row's window
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + (r & 3) >= rel) x[r] = neg_inf();
+        if (8 * (r >> 2) + (r & 3) >= rel || 8 * (r >> 2) + (r & 3) < rel_lo) x[r] = neg_inf();
     }
     float mt = fmaxf(x[0], x[1]);
 #pragma unroll
@@ -360,9 +361,21 @@ struct PrefillKernel {
     // keys this q tile can see: up to position L - M + j0 + rows - 1
     const int key_end = a.causal ? min(L, L - M + j0 + rows) : L;
     const int n_ktiles = key_end > 0 ? (key_end + KT - 1) / KT : 0;
-    const int n_split = max(1, min((n_ktiles + a.split_tiles - 1) / a.split_tiles, a.max_splits));
+    // sliding window / local chunks (causal only): row q's first key is
+    // key_lower_bound(L - M + j0 + q), non-decreasing in q; the tile's key tiles
+    // start at row 0's bound, and tiles before row rows-1's bound need the mask
+    const bool windowed = a.causal && (a.window_left >= 0 || a.attn_chunk > 0);
+    const int lo_first = windowed ? key_lower_bound(max(L - M + j0, 0), a.window_left, a.attn_chunk)
+                                  : 0;
+    const int lo_last = windowed ? key_lower_bound(max(L - M + j0 + rows - 1, 0), a.window_left,
+                                                   a.attn_chunk)
+                                 : 0;
+    const int kt_lo = min(lo_first / KT, n_ktiles);
+    const int low_full = (lo_last + KT - 1) / KT;   // tiles from here on need no lower mask
+    const int n_range = n_ktiles - kt_lo;
+    const int n_split = max(1, min((n_range + a.split_tiles - 1) / a.split_tiles, a.max_splits));
     if (split >= n_split) return;
-    const int t_begin = split * a.split_tiles;
+    const int t_begin = kt_lo + split * a.split_tiles;
     const int t_end = (split == n_split - 1) ? n_ktiles : t_begin + a.split_tiles;
     const int n_all = max(t_end - t_begin, 0);
     const int n_iter = (n_all + 1) / 2;           // group 0 takes the first half
@@ -377,6 +390,9 @@ struct PrefillKernel {
     const bool row_ok = q < rows && q0 + j0 + q < a.total_q;
     // keys visible to row q (rows past the tile's end compute discarded values)
     const int limit = a.causal ? min(L, L - M + j0 + q + 1) : L;
+    const int row_lo = windowed ? key_lower_bound(max(L - M + j0 + q, 0), a.window_left,
+                                                  a.attn_chunk)
+                                : 0;
     // tiles entirely below every row's limit need no mask
     const int full_tiles = max(a.causal ? min(L, L - M + j0 + 1) : L, 0) / KT;
     const int64_t row_bytes = static_cast<int64_t>(a.hkv) * ROW;
@@ -486,8 +502,10 @@ struct PrefillKernel {
           const int kt = gb + it;
           u32x4 kw[NKS];
           read_k(smem + ((it + 1) % NSTAGE) * STAGE, kbase, q, h, kw);
-          s_cur = softmax_pv(s_cur, smem + (it % NSTAGE) * STAGE + TILE, vofs, kt >= full_tiles,
-                             limit - kt * KT - 4 * h, h, a.scale_log2, kw, qop, acc, m_run, l_run);
+          s_cur = softmax_pv(s_cur, smem + (it % NSTAGE) * STAGE + TILE, vofs,
+                             kt >= full_tiles || kt < low_full, limit - kt * KT - 4 * h,
+                             row_lo - kt * KT - 4 * h, h, a.scale_log2, kw, qop, acc, m_run,
+                             l_run);
         }
       }
       __syncthreads();   // every wave is done with the rings

@@ -40,12 +40,13 @@ def test_status_strings():
 
 def _decode(lib, **kw):
     a = dict(q=None, dtype=1, k=None, v=None, num_pages=16, pt=None, pt_stride=8, kv_lens=None,
-             batch=2, hq=32, hkv=8, d=128, P=64, scale=0.1, chunk=4096, S=2, op=None, lp=None,
-             out=None, lse=None, stream=None)
+             batch=2, hq=32, hkv=8, d=128, P=64, scale=0.1, wl=-1, ac=0, chunk=4096, S=2, op=None,
+             lp=None, out=None, lse=None, stream=None)
     a.update(kw)
     return lib.paged_attn_decode_splitkv(a["q"], a["dtype"], a["k"], a["v"], a["num_pages"],
                                          a["pt"], a["pt_stride"], a["kv_lens"], a["batch"], a["hq"],
-                                         a["hkv"], a["d"], a["P"], a["scale"], a["chunk"], a["S"],
+                                         a["hkv"], a["d"], a["P"], a["scale"], a["wl"], a["ac"],
+                                         a["chunk"], a["S"],
                                          a["op"], a["lp"], a["out"], a["lse"], a["stream"])
 
 
@@ -59,6 +60,9 @@ def test_decode_argument_errors():
     assert _decode(lib, chunk=48, P=16) == EINVAL         # chunk not a multiple of 32
     assert _decode(lib, chunk=0, S=2) == EINVAL           # one split needs S == 1
     assert _decode(lib, S=0) == EINVAL
+    assert _decode(lib, wl=-2) == EINVAL                  # window below -1
+    assert _decode(lib, ac=-1) == EINVAL
+    assert _decode(lib, wl=128, ac=256) == EINVAL         # both masks at once
     assert _decode(lib) == EINVAL                         # NULL device pointers
     assert b"NULL" in lib.pkv_last_error()
     assert _decode(lib, batch=0) == 0                     # empty batch: nothing to do
@@ -105,15 +109,21 @@ def test_sparse_workspace_plan():
     # 96 heads are three 32-head blocks; enough units for one split: no workspace
     assert size(96, 2048, 96, 512) == 0
     pf = lib.paged_attn_varlen_prefill
-    # q dtype k v pages pt stride cu kl  B  Tq Mq Mk  Hq Hkv D   P  scale causal ws  bytes out lse st
-    assert pf(None, 0, None, None, 8, None, 4, None, None, 2, 10, 5, 40, 8, 2, 128, 1, 0.1, 1, None,
-              0, None, None, None) == EUNSUP                # fp32 prefill not instantiated
-    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, 40, 8, 3, 128, 1, 0.1, 1, None,
-              0, None, None, None) == EINVAL
-    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, 40, 8, 2, 128, 1, 0.1, 2, None,
-              0, None, None, None) == EINVAL
-    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, -1, 8, 2, 128, 1, 0.1, 1, None,
-              0, None, None, None) == EINVAL              # negative max_seqlen_k
+    # q dtype k v pages pt stride cu kl  B  Tq Mq Mk  Hq Hkv D   P  scale causal window chunk
+    #   ws bytes out lse st
+    assert pf(None, 0, None, None, 8, None, 4, None, None, 2, 10, 5, 40, 8, 2, 128, 1, 0.1, 1, -1, 0,
+              None, 0, None, None, None) == EUNSUP        # fp32 prefill not instantiated
+    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, 40, 8, 3, 128, 1, 0.1, 1, -1, 0,
+              None, 0, None, None, None) == EINVAL
+    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, 40, 8, 2, 128, 1, 0.1, 2, -1, 0,
+              None, 0, None, None, None) == EINVAL
+    assert pf(None, 1, None, None, 8, None, 4, None, None, 2, 10, 5, -1, 8, 2, 128, 1, 0.1, 1, -1, 0,
+              None, 0, None, None, None) == EINVAL        # negative max_seqlen_k
+    fake = ctypes.c_void_p(256)
+    ok = [fake, 1, fake, fake, 8, fake, 4, fake, fake, 2, 10, 5, 40, 8, 2, 128, 1, 0.1]
+    for causal, wl, ac in [(1, -2, 0), (1, 8, 16), (1, -1, -4), (0, 8, 0), (0, -1, 16)]:
+        assert pf(*ok, causal, wl, ac, None, 0, fake, None, None) == EINVAL, (causal, wl, ac)
+        assert b"window" in lib.pkv_last_error() or b"chunk" in lib.pkv_last_error()
 
 
 def test_prefill_workspace_plan():
@@ -131,7 +141,7 @@ def test_prefill_workspace_plan():
     fake = ctypes.c_void_p(256)
     pf = lib.paged_attn_varlen_prefill
     args = [fake, 1, fake, fake, 8192, fake, 8192, fake, fake, 1, 64, 64, 8192, 32, 8, 128, 1,
-            0.088, 1]
+            0.088, 1, -1, 0]
     assert pf(*args, None, 0, fake, None, None) == EINVAL
     assert pf(*args, fake, small - 1, fake, None, None) == EINVAL
     assert b"workspace" in lib.pkv_last_error()
@@ -157,7 +167,7 @@ def test_append_argument_errors():
     pa = lib.paged_attn_varlen_prefill_append
     # the prefill checks come first and nothing is enqueued when any check fails
     args = [fake, 1, fake, fake, 8192, fake, 8192, fake, fake, 1, 64, 64, 64, 32, 8, 128, 1,
-            0.088, 1]
+            0.088, 1, -1, 0]
     assert pa(*args, None, fake, fake, None, 0, fake, None, None) == EINVAL     # k_new NULL
     bad = list(args)
     bad[15] = 96                                                               # head_dim
