@@ -32,8 +32,9 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--only", choices=["all", "decode", "prefill", "prefill_long",
-                                      "prefill_append", "swa", "sparse", "copy"],
+    p.add_argument("--only", choices=["all", "decode", "decode_window", "prefill",
+                                      "prefill_long", "prefill_window", "prefill_append", "swa",
+                                      "sparse", "copy"],
                    default="all", help="restrict to one workload (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -130,26 +131,41 @@ def decode_bytes(seq_lens, batch, hq, hkv, d, page_size, elem=2):
     return kv + batch * hq * d * elem * 2 + 4 * n_pages, sum_l
 
 
-def prefill_flops(extend_lens, kv_lens, hq, d):
-    """4 * D * Hq * (visible (q, k) pairs), causal bottom-right."""
+def prefill_flops(extend_lens, kv_lens, hq, d, window_left=-1):
+    """4 * D * Hq * (visible (q, k) pairs), causal bottom-right; a sliding
+    window (W, 0) keeps at most W + 1 keys per row."""
     pairs = 0
     for m, L in zip(extend_lens, kv_lens):
         m, L = int(m), int(L)
-        pairs += sum(L - m + j + 1 for j in range(m))
+        cap = window_left + 1 if window_left >= 0 else None
+        pairs += sum(L - m + j + 1 if cap is None else min(L - m + j + 1, cap) for j in range(m))
     return 4 * d * hq * pairs, pairs
+
+
+def window_decode_bytes(seq_lens, window_left, batch, hq, hkv, d, page_size, elem=2):
+    """decode_bytes over the last min(L, W + 1) keys of each request (and the
+    pages holding them)."""
+    kv_keys, pages = 0, 0
+    for L in seq_lens.tolist():
+        lo = max(L - 1 - window_left, 0)
+        kv_keys += L - lo
+        pages += (L + page_size - 1) // page_size - lo // page_size
+    kv = 2 * kv_keys * hkv * d * elem
+    return kv + batch * hq * d * elem * 2 + 4 * pages, kv_keys
 
 
 # ---------------------------------------------------------------------------
 # Workloads
 # ---------------------------------------------------------------------------
 
-def run_decode(torch, pkv, workloads, args):
+def run_decode(torch, pkv, workloads, args, window_left=-1, kv_chunk=None):
     dev = torch.device("cuda:0")
     c = workloads.config3(value_device=dev)
     r2t, rpi, sl = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev))
     B, hq, d = c.q.shape
     _, P, hkv, _ = c.k_cache.shape
-    S = c.num_splits
+    chunk = kv_chunk or c.kv_chunk
+    S = -(-int(c.seq_lens.max()) // chunk)
     pt = torch.empty((B, c.table_width), dtype=torch.int32, device=dev)
     kl = torch.empty((B,), dtype=torch.int32, device=dev)
     op = torch.empty((S, B, hq, d), dtype=torch.float32, device=dev)
@@ -162,14 +178,18 @@ def run_decode(torch, pkv, workloads, args):
                              with_cu_seqlens=False)
         e0 = timer.mark() if timer else None
         pkv.paged_attn_decode_splitkv(c.q, c.k_cache, c.v_cache, pt, kl, c.scale,
-                                      kv_chunk=c.kv_chunk, num_splits=S, o_partial=op,
-                                      lse_partial=lp)
+                                      kv_chunk=chunk, num_splits=S, window_left=window_left,
+                                      o_partial=op, lse_partial=lp)
         if timer:
             timer.pairs.append((e0, timer.mark()))
         pkv.merge_state(op, lp, out=out, lse_out=lse)
 
-    ms, kern_ms = timed_loop(torch, step, args.steps, args.warmup)
-    nbytes, sum_l = decode_bytes(c.seq_lens.long(), B, hq, hkv, d, P)
+    if window_left >= 0:
+        ms, kern_ms = device_loop(torch, step, args.steps, args.warmup, host_us_per_step=80.0)
+        nbytes, sum_l = window_decode_bytes(c.seq_lens.long(), window_left, B, hq, hkv, d, P)
+    else:
+        ms, kern_ms = timed_loop(torch, step, args.steps, args.warmup)
+        nbytes, sum_l = decode_bytes(c.seq_lens.long(), B, hq, hkv, d, P)
     res = dict(ms=ms, kernel_ms=kern_ms, bytes=nbytes, sum_l=sum_l, batch=B, splits=S,
                case=c)
     return res
@@ -213,7 +233,7 @@ def run_swa(torch, pkv, workloads, args):
                 sum_kv_len=sum_l, splits=S, case=c, pt=pt, kl=kl)
 
 
-def run_prefill(torch, pkv, workloads, args, make_case=None):
+def run_prefill(torch, pkv, workloads, args, make_case=None, window_left=-1):
     dev = torch.device("cuda:0")
     c = (make_case or workloads.config2)(value_device=dev)
     r2t, rpi, sl, cu = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev),
@@ -233,8 +253,8 @@ def run_prefill(torch, pkv, workloads, args, make_case=None):
                              kv_lens=kl, with_cu_seqlens=False)
         e0 = timer.mark() if timer else None
         pkv.paged_attn_varlen_prefill(c.q, c.k_cache, c.v_cache, pt, cu, kl, c.max_seqlen_q,
-                                      c.scale, max_seqlen_k=max_k, causal=True, workspace=ws,
-                                      out=out, lse=lse)
+                                      c.scale, max_seqlen_k=max_k, causal=True,
+                                      window_left=window_left, workspace=ws, out=out, lse=lse)
         if timer:
             timer.pairs.append((e0, timer.mark()))
 
@@ -251,7 +271,7 @@ def run_prefill(torch, pkv, workloads, args, make_case=None):
                                  host_us_per_step=120.0)
         del flush
     flops, pairs = prefill_flops(c.extend_lens.tolist(), c.seq_lens.tolist(), c.q.shape[1],
-                                 c.q.shape[2])
+                                 c.q.shape[2], window_left)
     return dict(ms=ms, kernel_ms=kern_ms, cold_ms=cold_ms, flops=flops, pairs=pairs, case=c,
                 pt=pt, kl=kl)
 
@@ -564,6 +584,24 @@ def main(argv=None):
         del r
         torch.cuda.empty_cache()
 
+    if args.only in ("all", "decode_window"):
+        try:
+            W = 4095
+            r = run_decode(torch, pkv, workloads, args, window_left=W, kv_chunk=2048)
+            extra["decode_window"] = {
+                "workload": "config3 under an in-kernel sliding window (W, 0) with W = 4095 "
+                            "(each query sees its last 4096 keys) over the strided table; "
+                            "2048-token chunks, 16 splits",
+                "device_ms_per_step": round(r["ms"], 4), "decode_kernel_ms": round(r["kernel_ms"], 4),
+                "kernel_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
+                "kernel_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4),
+                "visible_keys": r["sum_l"], "algorithmic_bytes": r["bytes"],
+                "num_splits": r["splits"]}
+        except Exception as e:
+            extra["decode_window"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
     if args.only in ("all", "swa"):
         try:
             r = run_swa(torch, pkv, workloads, args)
@@ -615,6 +653,22 @@ def main(argv=None):
                 "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": r["flops"]}
         except Exception as e:
             extra["prefill_long"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "prefill_window"):
+        try:
+            W = 1023
+            r = run_prefill(torch, pkv, workloads, args, workloads.long_prompt_prefill,
+                            window_left=W)
+            tf = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+            extra["prefill_window"] = {
+                "workload": "long prompts (4 x 4096 new tokens, 32 q / 8 kv heads, D=128, "
+                            "page 1) under a sliding window (W, 0), W = 1023",
+                "kernel_ms": round(r["kernel_ms"], 5), "device_ms_per_step": round(r["ms"], 5),
+                "TFLOP/s": round(tf, 2), "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS,
+                "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": r["flops"]}
+        except Exception as e:
+            extra["prefill_window"] = {"error": repr(e)}
         torch.cuda.empty_cache()
 
     if args.only in ("all", "prefill_append"):
