@@ -24,6 +24,8 @@ pins are the closed forms and the library/brute-force special cases.
 
 from .reference import (  # noqa: F401
     NEG_INF,
+    cascade_attention,
+    cascade_expand_table,
     causal_key_ranges,
     cu_seqlens,
     gather_paged,
@@ -40,5 +42,6 @@ from .reference import (  # noqa: F401
     paged_prefill_append,
     softmax_attention,
     sparse_topk_decode,
+    tree_verify_attention,
     visible_key_counts,
 )

@@ -400,6 +400,117 @@ def merge_state(o_parts, lse_parts):
     return out, lse
 
 
+# ---------------------------------------------------------------------------
+# Cascade attention (speculative target verify with a draft tree)
+# ---------------------------------------------------------------------------
+
+def cascade_expand_table(custom_mask, req_to_token, req_pool_indices, seq_lens, num_draft):
+    """Per-draft-row key lists for the expand pass of cascade attention.
+
+    [FA] ``init_forward_metadata``, target verify with ``topk > 1`` ("create
+    expand page table"): request ``b`` has ``L_b = seq_lens[b]`` committed
+    tokens and ``n = num_draft`` draft tokens at positions ``L_b .. L_b+n-1``.
+    ``custom_mask`` is flat: request blocks in order, each ``n`` rows of
+    ``L_b + n`` entries (row ``i`` of request ``b`` tells which of the
+    ``L_b + n`` positions draft token ``i`` may see). The expand pass keeps only
+    the draft columns: row ``(b, i)`` lists the slots
+    ``req_to_token[req_pool_indices[b], L_b + j]`` of the visible drafts ``j``
+    in increasing ``j``, then the masked ones, also in increasing ``j`` (the
+    page sorts the keys ``j`` / ``j + n``); its length is the number visible.
+    The page's comment prints a three-row example.
+
+    Returns (table [B*n, n] int32 slots, lens [B*n] int32, cu_lens [B*n+1]).
+    """
+    mask = np.asarray(custom_mask).astype(bool).reshape(-1)
+    r2t = np.asarray(req_to_token)
+    rpi = np.asarray(req_pool_indices)
+    seq_lens = np.asarray(seq_lens)
+    n = int(num_draft)
+    batch = len(seq_lens)
+    table = np.zeros((batch * n, n), dtype=np.int32)
+    lens = np.zeros(batch * n, dtype=np.int32)
+    start = 0
+    for b in range(batch):
+        L = int(seq_lens[b])
+        drafts = [int(r2t[int(rpi[b]), L + j]) for j in range(n)]
+        for i in range(n):
+            cols = mask[start + L:start + L + n]
+            seen = [j for j in range(n) if cols[j]]
+            hidden = [j for j in range(n) if not cols[j]]
+            table[b * n + i] = [drafts[j] for j in seen + hidden]
+            lens[b * n + i] = len(seen)
+            start += L + n
+    return table, lens, cu_seqlens(lens)
+
+
+def tree_verify_attention(q, k_cache, v_cache, req_to_token, req_pool_indices, seq_lens,
+                          custom_mask, num_draft, scale):
+    """What cascade attention computes, by its plain definition: draft row
+    ``(b, i)`` attends over the positions ``t < L_b + n`` its custom-mask row
+    allows (all committed tokens and its visible drafts), keys and values read
+    at slot ``req_to_token[req_pool_indices[b], t]``.
+
+    [FA] ``forward_extend`` with ``use_cascade_attn`` (target verify with
+    ``topk > 1``) splits exactly this attention into a prefix pass and an
+    expand pass. Caches are ``[pages, P, Hkv, D]`` (slot ``s`` = page ``s // P``,
+    position ``s % P``); q is ``[B*n, Hq, D]``. Returns O, LSE (float64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kflat = np.asarray(k_cache).reshape(-1, k_cache.shape[2], k_cache.shape[3])
+    vflat = np.asarray(v_cache).reshape(-1, v_cache.shape[2], v_cache.shape[3])
+    mask = np.asarray(custom_mask).astype(bool).reshape(-1)
+    r2t = np.asarray(req_to_token)
+    rpi = np.asarray(req_pool_indices)
+    n = int(num_draft)
+    total, num_q_heads, _ = q.shape
+    num_kv_heads = kflat.shape[1]
+    out = np.zeros((total, num_q_heads, vflat.shape[2]), dtype=np.float64)
+    lse = np.full((total, num_q_heads), NEG_INF, dtype=np.float64)
+    start = 0
+    for b in range(len(seq_lens)):
+        L = int(seq_lens[b])
+        slots = [int(r2t[int(rpi[b]), t]) for t in range(L + n)]
+        for i in range(n):
+            row = mask[start:start + L + n]
+            vis = [slots[t] for t in range(L + n) if row[t]]
+            for h in range(num_q_heads):
+                kvh = kv_head_of(h, num_q_heads, num_kv_heads)
+                o, l_ = softmax_attention(q[b * n + i, h], kflat[vis, kvh], vflat[vis, kvh],
+                                          scale)
+                out[b * n + i, h] = o
+                lse[b * n + i, h] = l_
+            start += L + n
+    return out, lse
+
+
+def cascade_attention(q, k_cache, v_cache, page_table, seq_lens, page_size, expand_table,
+                      expand_lens, scale):
+    """Cascade attention in the pages' three steps.
+
+    [FA] ``forward_extend`` / ``forward_decode`` with ``use_cascade_attn``:
+    (1) prefix pass -- the ``n`` draft rows of request ``b``
+    (``cu_seqlens_q`` in steps of ``n``) attend non-causally over its ``L_b``
+    committed tokens through the page table, returning LSE; (2) expand pass --
+    every draft row is its own one-token request whose keys are the slots
+    ``expand_table[row, :expand_lens[row]]`` of the cache viewed with page
+    size 1, non-causal, returning LSE; (3) ``merge_state_v2`` of the two.
+
+    Returns O [B*n, Hq, Dv], LSE [B*n, Hq] (float64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    total = q.shape[0]
+    batch = len(seq_lens)
+    n = total // batch
+    cu = np.arange(0, total + 1, n)
+    o1, l1 = paged_prefill(q, k_cache, v_cache, page_table, cu, seq_lens, page_size, scale,
+                           causal=False)
+    k1 = np.asarray(k_cache).reshape(-1, 1, k_cache.shape[2], k_cache.shape[3])
+    v1 = np.asarray(v_cache).reshape(-1, 1, v_cache.shape[2], v_cache.shape[3])
+    o2, l2 = paged_decode_splitkv(q, k1, v1, np.asarray(expand_table), expand_lens, 1, scale,
+                                  0, 1)
+    return merge_state(np.stack([o1, o2[0]]), np.stack([l1, l2[0]]))
+
+
 def sparse_topk_decode(q, kv_cache, req_to_token, req_pool_indices, topk_idx, scale,
                        head_dim_v):
     """Top-k index-gathered MLA decode over one latent KV head.

@@ -622,3 +622,142 @@ def test_planted_window_off_by_one_is_caught(monkeypatch):
                         real(pos, window_left, attn_chunk) + (1 if window_left >= 0 else 0))
     with pytest.raises(AssertionError):
         test_sliding_window_prefill_matches_sdpa_band(3)
+
+
+# ---------------------------------------------------------------------------
+# Cascade attention (draft-tree verification)
+# ---------------------------------------------------------------------------
+
+def test_cascade_expand_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "cascade_expand_example.json")))
+    n = len(g["draft_slots"])
+    L = 2                                             # committed tokens: all visible
+    r2t = np.array([[0, 0, 0, 0, 0], [5, 6] + g["draft_slots"]])
+    mask = np.concatenate([np.array([1] * L + row) for row in g["draft_mask"]])
+    table, lens, cu = oracle.cascade_expand_table(mask, r2t, [1], [L], n)
+    assert table.tolist() == g["expand_table"]
+    assert lens.tolist() == g["expand_lens"]
+    assert cu.tolist() == [0, 1, 3, 5]
+
+
+def _tiny_cascade(seed, P=4, n=5, tree="random", prefix=(3, 0, 9, 1), dtype=torch.float32):
+    return workloads.make_cascade_case(seed, prefix_lens=list(prefix), num_draft=n,
+                                       num_q_heads=4, num_kv_heads=2, head_dim=8, page_size=P,
+                                       num_pages=sum(prefix) // P + len(prefix) * (n // P + 2)
+                                       + 4, tree=tree, dtype=dtype)
+
+
+def _oracle_cascade(c):
+    pt, _, _ = oracle.page_table_strided(i64(c.req_to_token), i64(c.req_pool_indices),
+                                         i64(c.seq_lens), c.page_size, c.table_width)
+    table, lens, _ = oracle.cascade_expand_table(i64(c.custom_mask), i64(c.req_to_token),
+                                                 i64(c.req_pool_indices), i64(c.seq_lens),
+                                                 c.num_draft)
+    return oracle.cascade_attention(f64(c.q), f64(c.k_cache), f64(c.v_cache), pt,
+                                    i64(c.seq_lens), c.page_size, table, lens, c.scale)
+
+
+def _oracle_tree(c):
+    return oracle.tree_verify_attention(f64(c.q), f64(c.k_cache), f64(c.v_cache),
+                                        i64(c.req_to_token), i64(c.req_pool_indices),
+                                        i64(c.seq_lens), i64(c.custom_mask), c.num_draft,
+                                        c.scale)
+
+
+def test_cascade_expand_table_matches_stable_sort():
+    """Each row is the request's draft slots, visible ones first, both groups in
+    position order: numpy's stable argsort of 'hidden' gives the same order."""
+    for seed in range(20):
+        n = 1 + seed % 9
+        c = _tiny_cascade(100 + seed, n=n, P=1 + seed % 3)
+        r2t, rpi, sl = i64(c.req_to_token), i64(c.req_pool_indices), i64(c.seq_lens)
+        mask = i64(c.custom_mask).astype(bool)
+        table, lens, cu = oracle.cascade_expand_table(mask, r2t, rpi, sl, n)
+        start = 0
+        for b in range(len(sl)):
+            L = int(sl[b])
+            drafts = r2t[rpi[b], L:L + n]
+            for i in range(n):
+                vis = mask[start + L:start + L + n]
+                order = np.argsort(~vis, kind="stable")
+                assert table[b * n + i].tolist() == drafts[order].tolist()
+                assert lens[b * n + i] == vis.sum()
+                assert sorted(table[b * n + i].tolist()) == sorted(drafts.tolist())
+                start += L + n
+        assert cu[-1] == lens.sum() and (np.diff(cu) == lens).all()
+
+
+def test_tree_verify_matches_sdpa_with_custom_mask():
+    """The plain definition against torch SDPA (float64) with each request's
+    custom-mask rows as an explicit boolean mask over its L + n positions."""
+    c = _tiny_cascade(7)
+    o, lse = _oracle_tree(c)
+    n, sl = c.num_draft, i64(c.seq_lens)
+    mask = torch.as_tensor(i64(c.custom_mask).astype(bool))
+    start = 0
+    for b in range(len(sl)):
+        L = int(sl[b])
+        row = int(c.req_pool_indices[b])
+        K = dense_request_kv(c.k_cache, c.req_to_token, row, L + n)
+        V = dense_request_kv(c.v_cache, c.req_to_token, row, L + n)
+        m = mask[start:start + n * (L + n)].view(n, L + n)
+        start += n * (L + n)
+        q = c.q[b * n:(b + 1) * n].to(torch.float64)
+        g = q.shape[1] // K.shape[1]
+        qq = q.permute(1, 0, 2).unsqueeze(0)
+        kk = K.permute(1, 0, 2).repeat_interleave(g, dim=0).unsqueeze(0)
+        vv = V.permute(1, 0, 2).repeat_interleave(g, dim=0).unsqueeze(0)
+        ref_o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=m,
+                                                                 scale=c.scale)
+        logits = (torch.matmul(qq, kk.transpose(-1, -2)) * c.scale).masked_fill(~m, -math.inf)
+        ref_l = torch.logsumexp(logits, dim=-1)
+        assert np.abs(o[b * n:(b + 1) * n] - ref_o[0].permute(1, 0, 2).numpy()).max() < 1e-12
+        assert np.abs(lse[b * n:(b + 1) * n] - ref_l[0].permute(1, 0).numpy()).max() < 1e-12
+
+
+@pytest.mark.parametrize("P,n,tree", [(1, 5, "random"), (4, 5, "random"), (4, 8, "chain"),
+                                      (3, 1, "random"), (2, 12, "random")])
+def test_cascade_equals_tree_attention(P, n, tree):
+    """Prefix pass + expand pass + merge reach the plain tree attention."""
+    c = _tiny_cascade(40 + P + n, P=P, n=n, tree=tree)
+    o, lse = _oracle_cascade(c)
+    o_ref, l_ref = _oracle_tree(c)
+    assert np.abs(o - o_ref).max() < 1e-12
+    assert np.abs(lse - l_ref).max() < 1e-12
+
+
+def test_chain_tree_is_causal_extend():
+    """A chain of drafts (each sees all earlier ones) is ordinary causal extend
+    of the n drafts over L + n keys."""
+    c = _tiny_cascade(51, P=4, n=6, tree="chain")
+    o, lse = _oracle_tree(c)
+    n, sl = c.num_draft, i64(c.seq_lens)
+    pt, kl, _ = oracle.page_table_strided(i64(c.req_to_token), i64(c.req_pool_indices), sl + n,
+                                          c.page_size, c.table_width)
+    cu = np.arange(0, len(sl) * n + 1, n)
+    o2, l2 = oracle.paged_prefill(f64(c.q), f64(c.k_cache), f64(c.v_cache), pt, cu, kl,
+                                  c.page_size, c.scale, causal=True)
+    assert np.abs(o - o2).max() < 1e-12 and np.abs(lse - l2).max() < 1e-12
+
+
+def test_planted_causal_prefix_pass_is_caught(monkeypatch):
+    real = ref.paged_prefill
+    monkeypatch.setattr(ref, "paged_prefill", lambda *a, **kw: real(*a, **{**kw, "causal": True}))
+    with pytest.raises(AssertionError):
+        test_cascade_equals_tree_attention(4, 5, "random")
+
+
+def test_planted_expand_order_mistake_is_caught(monkeypatch):
+    """Listing each row's drafts by slot number instead of visible-first
+    (keeping the count) attends to the wrong drafts."""
+    real = ref.cascade_expand_table
+
+    def unsorted(mask, r2t, rpi, sl, n):
+        table, lens, cu = real(mask, r2t, rpi, sl, n)
+        for r in range(table.shape[0]):
+            table[r] = np.sort(table[r])
+        return table, lens, cu
+    monkeypatch.setattr(ref, "cascade_expand_table", unsorted)
+    monkeypatch.setattr(oracle, "cascade_expand_table", unsorted)
+    with pytest.raises(AssertionError):
+        test_cascade_equals_tree_attention(1, 5, "random")

@@ -30,8 +30,9 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "DecodeCase", "PrefillCase", "SwaCase", "SparseCase",
+    "DecodeCase", "PrefillCase", "SwaCase", "SparseCase", "CascadeCase",
     "make_decode_case", "make_prefill_case", "make_swa_case", "make_sparse_case",
+    "make_cascade_case", "cascade_verify",
     "config1", "config2", "config3", "config4", "config5",
     "small_config3", "small_config4", "small_config5",
 ]
@@ -100,6 +101,23 @@ class SparseCase:
     topk_idx: torch.Tensor          # [B, K] logical token indices, -1 = padding
     head_dim_v: int
     scale: float
+    name: str = ""
+
+
+@dataclass
+class CascadeCase:
+    q: torch.Tensor                 # [B*n, Hq, D] draft-token queries, request-major
+    k_cache: torch.Tensor           # [num_pages, P, Hkv, D]; committed and draft tokens
+    v_cache: torch.Tensor
+    req_to_token: torch.Tensor      # [2B, ctx] int32 slots
+    req_pool_indices: torch.Tensor  # [B]
+    seq_lens: torch.Tensor          # [B] committed tokens L_b (drafts follow at L_b..L_b+n-1)
+    custom_mask: torch.Tensor       # flat bool: per request n rows of L_b + n entries
+    parents: torch.Tensor           # [B, n] draft tree, -1 = child of the last committed token
+    num_draft: int
+    page_size: int
+    scale: float
+    table_width: int                # pages per row of the committed-token page table
     name: str = ""
 
 
@@ -265,6 +283,62 @@ def make_prefill_case(seed, *, prefix_lens, extend_lens, num_q_heads, num_kv_hea
                        table_width=ctx // page_size, name=name)
 
 
+def make_cascade_case(seed, *, prefix_lens, num_draft, num_q_heads, num_kv_heads, head_dim,
+                      page_size, num_pages, tree="random", dtype=torch.bfloat16,
+                      value_device="cpu", name="") -> CascadeCase:
+    """Speculative verification of a draft tree: request b has ``L_b`` committed
+    tokens and ``n = num_draft`` draft tokens at positions ``L_b .. L_b+n-1``,
+    all resident in the paged cache. ``prefix_lens`` is a list or a
+    ``(batch, lo, hi)`` tuple (uniform, inclusive). The tree: draft 0 hangs off
+    the last committed token, draft ``j > 0`` off a parent drawn uniformly from
+    ``0 .. j-1`` (``tree="random"``), or off ``j-1`` (``"chain"``). A draft row
+    sees every committed position, itself and its ancestors (the custom mask of
+    a tree-structured verify step).
+    """
+    g = torch.Generator().manual_seed(seed)
+    if isinstance(prefix_lens, tuple):
+        batch, lo, hi = prefix_lens
+        prefix = _randint_incl(g, lo, hi, batch)
+    else:
+        prefix = torch.tensor(list(prefix_lens), dtype=torch.int64)
+    n = int(num_draft)
+    lens = prefix + n
+    batch = len(lens)
+    ctx = -(-int(lens.max()) // page_size) * page_size
+    r2t, rpi, owned, _poison, pool_pages = _place_pages(g, batch, lens, page_size, num_pages, ctx)
+    parents = torch.full((batch, n), -1, dtype=torch.int64)
+    for b in range(batch):
+        for j in range(1, n):
+            if tree == "chain":
+                parents[b, j] = j - 1
+            else:
+                parents[b, j] = int(torch.randint(0, j, (1,), generator=g))
+    blocks = []
+    for b in range(batch):
+        L = int(prefix[b])
+        rows = torch.zeros((n, L + n), dtype=torch.bool)
+        rows[:, :L] = True
+        for i in range(n):
+            a = i
+            while a >= 0:
+                rows[i, L + a] = True
+                a = int(parents[b, a])
+        blocks.append(rows.reshape(-1))
+    mask = torch.cat(blocks) if blocks else torch.zeros(0, dtype=torch.bool)
+    gv, dev = _value_generator(seed, value_device)
+    q = _normal(gv, dev, (batch * n, num_q_heads, head_dim), dtype)
+    k_parts, v_parts = _draw_kv(gv, dev, lens, num_kv_heads, head_dim, dtype)
+    k_cache = _fill_cache(k_parts, owned, lens, page_size, pool_pages, num_kv_heads, head_dim,
+                          dtype, dev)
+    v_cache = _fill_cache(v_parts, owned, lens, page_size, pool_pages, num_kv_heads, head_dim,
+                          dtype, dev)
+    return CascadeCase(q=q, k_cache=k_cache, v_cache=v_cache, req_to_token=r2t.to(torch.int32),
+                       req_pool_indices=rpi.to(torch.int32), seq_lens=prefix.to(torch.int32),
+                       custom_mask=mask, parents=parents.to(torch.int32), num_draft=n,
+                       page_size=page_size, scale=1.0 / math.sqrt(head_dim),
+                       table_width=ctx // page_size, name=name)
+
+
 def make_swa_case(seed, *, batch, prefill_range, decode_range, window, num_q_heads,
                   num_kv_heads, head_dim, pool_slots, dtype=torch.bfloat16, kv_chunk=0,
                   value_device="cpu", with_values=True, name="") -> SwaCase:
@@ -336,6 +410,15 @@ def make_sparse_case(seed, *, batch, ctx, topk, num_q_heads, head_dim_qk, head_d
 # ---------------------------------------------------------------------------
 # The five workloads at full size, and reduced copies the oracle finishes fast
 # ---------------------------------------------------------------------------
+
+def cascade_verify(value_device="cpu"):
+    """Tree verification by cascade attention, bf16: B 64, committed L ~
+    U[1024, 16384], 8 draft tokens per request in a random tree, 32 q / 8 kv
+    heads, D 128, page 64 over a 20000-page pool."""
+    return make_cascade_case(6, prefix_lens=(64, 1024, 16384), num_draft=8, num_q_heads=32,
+                             num_kv_heads=8, head_dim=128, page_size=64, num_pages=20000,
+                             value_device=value_device, name="cascade_verify")
+
 
 def config1(value_device="cpu"):
     """Tiny paged GQA decode, fp32: seq_lens [37, 100], 4 q / 2 kv heads, D 64,
