@@ -113,7 +113,7 @@ pkv_status_t build_page_table(const int32_t* req_to_token, int64_t req_to_token_
  * q        [total_q, num_q_heads, head_dim]         dtype
  * k_cache, v_cache [num_pages, page_size, num_kv_heads, head_dim] dtype
  * page_table [batch, pt_stride] int32 page ids; cu_seqlens_q [batch + 1];
- * kv_lens [batch] int32 (requires M_b <= L_b <= pt_stride * page_size)
+ * kv_lens [batch] int32 (requires L_b <= pt_stride * page_size, and M_b <= L_b when causal)
  * max_seqlen_q >= every M_b and max_seqlen_k >= every L_b: launch bounds, as
  *          in flash_attn_varlen_func; they size the grid and the key splits.
  *          (A max_seqlen_k below some L_b is still correct, only slower.)
@@ -283,6 +283,83 @@ pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num
                                 int32_t num_q_heads, int32_t head_dim_qk, int32_t head_dim_v,
                                 float softmax_scale, void* workspace, size_t workspace_bytes,
                                 void* out, float* lse, void* stream);
+
+/*
+ * build_cascade_expand_table -- key lists of cascade attention's expand pass.
+ * [FA] init_forward_metadata, target verify with topk > 1 ("create expand page
+ * table"). Request b has L_b = seq_lens[b] committed tokens and n = num_draft
+ * draft tokens at positions L_b .. L_b + n - 1 of its req_to_token row
+ * r = req_pool_indices[b]. custom_mask is flat, one byte per entry (0 = hidden):
+ * request blocks in order, each n rows of L_b + n entries; row i says which
+ * positions draft i may see. Row b*n + i of the output lists the slots
+ * req_to_token[r, L_b + j] of the drafts j that row i sees, in increasing j,
+ * then the hidden ones, also in increasing j; expand_lens[b*n + i] is the
+ * count seen, cu_expand_lens (if non-NULL) its zero-led prefix sum.
+ *
+ * custom_mask    [mask_len] uint8, mask_len = sum_b n * (L_b + n)
+ * req_to_token   [req_to_token_rows, req_to_token_stride] int32 (L_b + n <= stride)
+ * expand_table   [batch * n, n] int32 (out); expand_lens [batch * n] int32 (out);
+ * cu_expand_lens [batch * n + 1] int32 (out) or NULL.
+ * Supported: 1 <= num_draft <= 256. Errors: PKV_EINVAL for NULL pointers
+ * (batch > 0) or bad sizes; batch == 0 enqueues nothing. Indices read from
+ * device memory are clamped into their arrays.
+ */
+pkv_status_t build_cascade_expand_table(const uint8_t* custom_mask, int64_t mask_len,
+                                        const int32_t* req_to_token, int64_t req_to_token_rows,
+                                        int64_t req_to_token_stride,
+                                        const int32_t* req_pool_indices, const int32_t* seq_lens,
+                                        int32_t batch, int32_t num_draft, int32_t* expand_table,
+                                        int32_t* expand_lens, int32_t* cu_expand_lens,
+                                        void* stream);
+
+/*
+ * paged_attn_expand_merge -- cascade attention's expand pass and merge.
+ * [FA] forward_extend / forward_decode with use_cascade_attn: every q row is
+ * its own one-token request whose keys are the slots
+ * expand_table[row, :expand_lens[row]] of the cache viewed with page size 1
+ * (non-causal), and its (O, LSE) is merged into the prefix pass's state with
+ * merge_state_v2's combine:
+ *   m = max(LSE_a, LSE_b); w = exp(LSE - m);
+ *   O = (w_a O_a + w_b O_b) / (w_a + w_b); LSE = m + ln(w_a + w_b)
+ * (both -inf: O = 0, LSE = -inf; a row with no keys leaves the state as is).
+ *
+ * q        [n_rows, num_q_heads, head_dim] bf16
+ * k_cache, v_cache  the cache as [num_slots, num_kv_heads, head_dim] bf16
+ * expand_table [n_rows, expand_stride] int32 slots; expand_lens [n_rows] int32
+ * out      [n_rows, num_q_heads, head_dim] bf16, in: prefix-pass O, out: merged O
+ * lse      [n_rows, num_q_heads] fp32, in: prefix-pass LSE, out: merged LSE
+ * Supported: head_dim 64 or 128, Hq % Hkv == 0, Hq / Hkv <= 16.
+ */
+pkv_status_t paged_attn_expand_merge(const void* q, int32_t dtype, const void* k_cache,
+                                     const void* v_cache, int64_t num_slots,
+                                     const int32_t* expand_table, int32_t expand_stride,
+                                     const int32_t* expand_lens, int32_t n_rows,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     float softmax_scale, void* out, float* lse, void* stream);
+
+/*
+ * paged_attn_cascade -- cascade attention in one call: the prefix pass, then
+ * the expand pass with its merge ([FA] forward_extend / forward_decode with
+ * use_cascade_attn). The prefix pass is paged_attn_varlen_prefill with
+ * causal = 0: the rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of request b see
+ * all kv_lens[b] committed keys through page_table (for draft-tree
+ * verification, cu_seqlens_q steps by n and kv_lens are the committed
+ * lengths); its O and LSE go to out / lse, then paged_attn_expand_merge over
+ * the total_q rows merges each row's expand keys (slots in expand_table, the
+ * cache viewed with page size 1) into them. Arguments as for those two
+ * calls; lse is required. Every argument is checked before anything is
+ * enqueued; then two kernels run on the stream.
+ */
+pkv_status_t paged_attn_cascade(const void* q, int32_t dtype, const void* k_cache,
+                                const void* v_cache, int64_t num_pages, const int32_t* page_table,
+                                int32_t pt_stride, const int32_t* cu_seqlens_q,
+                                const int32_t* kv_lens, int32_t batch, int32_t total_q,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                float softmax_scale, const int32_t* expand_table,
+                                int32_t expand_stride, const int32_t* expand_lens,
+                                void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                void* stream);
 
 #ifdef __cplusplus
 }

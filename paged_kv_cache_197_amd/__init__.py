@@ -81,6 +81,13 @@ _SIGNATURES = {
     "sparse_topk_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "sparse_topk_decode": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _I64, _P, _P, _I32, _I32, _I32,
                                           _I32, _I32, _F, _P, _SZ, _P, _P, _P]),
+    "build_cascade_expand_table": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _P, _I32, _I32,
+                                                  _P, _P, _P, _P]),
+    "paged_attn_expand_merge": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _I32,
+                                               _I32, _I32, _F, _P, _P, _P]),
+    "paged_attn_cascade": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32,
+                                          _I32, _I32, _I32, _I32, _I32, _I32, _F, _P, _I32, _P,
+                                          _P, _SZ, _P, _P, _P]),
 }
 
 
@@ -364,4 +371,96 @@ def sparse_topk_decode(q, kv_cache, req_to_token, req_pool_indices, topk_idx, so
                                 head_dim_v, float(softmax_scale), _ptr(workspace), ws_bytes,
                                 _ptr(out), _ptr(lse), _stream(dev))
     _check("sparse_topk_decode", st)
+    return out, lse
+
+
+def build_cascade_expand_table(custom_mask, req_to_token, req_pool_indices, seq_lens, num_draft,
+                               *, expand_table=None, expand_lens=None, cu_expand_lens=None,
+                               with_cu=True):
+    """Expand-pass key lists of cascade attention (see include/pkv.h).
+    custom_mask: flat bool / uint8, per request num_draft rows of L_b + num_draft
+    entries. Returns (expand_table [B*n, n], expand_lens [B*n], cu [B*n+1] or None)."""
+    lib = load_library()
+    dev = req_to_token.device
+    mask = custom_mask
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    _need(mask.reshape(-1), "custom_mask", torch.uint8, dev)
+    r2t = _i32(req_to_token, "req_to_token", dev)
+    rpi = _i32(req_pool_indices, "req_pool_indices", dev)
+    sl = _i32(seq_lens, "seq_lens", dev)
+    batch, n = rpi.numel(), int(num_draft)
+    if expand_table is None:
+        expand_table = torch.empty((batch * n, n), dtype=torch.int32, device=dev)
+    if expand_lens is None:
+        expand_lens = torch.empty((batch * n,), dtype=torch.int32, device=dev)
+    if cu_expand_lens is None and with_cu:
+        cu_expand_lens = torch.empty((batch * n + 1,), dtype=torch.int32, device=dev)
+    _need(expand_table, "expand_table", torch.int32, dev)
+    _need(expand_lens, "expand_lens", torch.int32, dev)
+    st = lib.build_cascade_expand_table(_ptr(mask), mask.numel(), _ptr(r2t), r2t.shape[0],
+                                        r2t.shape[1], _ptr(rpi), _ptr(sl), batch, n,
+                                        _ptr(expand_table), _ptr(expand_lens),
+                                        _ptr(cu_expand_lens), _stream(dev))
+    _check("build_cascade_expand_table", st)
+    return expand_table, expand_lens, cu_expand_lens
+
+
+def paged_attn_expand_merge(q, k_cache, v_cache, expand_table, expand_lens, softmax_scale, out,
+                            lse):
+    """Expand pass + merge of cascade attention, in place on (out, lse)."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(k_cache, "k_cache", q.dtype, dev)
+    _need(v_cache, "v_cache", q.dtype, dev)
+    tab = _i32(expand_table, "expand_table", dev)
+    lens = _i32(expand_lens, "expand_lens", dev)
+    _need(out, "out", q.dtype, dev, 3)
+    _need(lse, "lse", torch.float32, dev, 2)
+    rows, hq, d = q.shape
+    hkv = k_cache.shape[-2]
+    num_slots = k_cache.numel() // (hkv * d)
+    st = lib.paged_attn_expand_merge(_ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache),
+                                     num_slots, _ptr(tab), tab.shape[1], _ptr(lens), rows, hq, hkv,
+                                     d, float(softmax_scale), _ptr(out), _ptr(lse), _stream(dev))
+    _check("paged_attn_expand_merge", st)
+    return out, lse
+
+
+def paged_attn_cascade(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, max_seqlen_q,
+                       softmax_scale, expand_table, expand_lens, *, max_seqlen_k=None,
+                       workspace=None, out=None, lse=None):
+    """Cascade attention (prefix pass + expand pass + merge) in one call.
+    Returns (out, lse)."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(k_cache, "k_cache", q.dtype, dev, 4)
+    _need(v_cache, "v_cache", q.dtype, dev, 4)
+    pt = _i32(page_table, "page_table", dev)
+    cu = _i32(cu_seqlens_q, "cu_seqlens_q", dev)
+    kl = _i32(kv_lens, "kv_lens", dev)
+    tab = _i32(expand_table, "expand_table", dev)
+    lens = _i32(expand_lens, "expand_lens", dev)
+    total_q, hq, d = q.shape
+    num_pages, page_size, hkv, _ = k_cache.shape
+    batch = kl.numel()
+    if max_seqlen_k is None:
+        max_seqlen_k = pt.shape[1] * page_size
+    need = paged_attn_varlen_prefill_workspace_size(batch, total_q, int(max_seqlen_q),
+                                                    int(max_seqlen_k), hq, hkv, d)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev)
+    st = lib.paged_attn_cascade(
+        _ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(pt),
+        pt.shape[1], _ptr(cu), _ptr(kl), batch, total_q, int(max_seqlen_q), int(max_seqlen_k),
+        hq, hkv, d, page_size, float(softmax_scale), _ptr(tab), tab.shape[1], _ptr(lens),
+        _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
+    _check("paged_attn_cascade", st)
     return out, lse

@@ -50,6 +50,10 @@ static float scale_log2(float softmax_scale) {
 // that about kPrefillWorkgroups workgroups run, never below kMinSplitTiles
 // tiles per split. The workspace holds the split counters (zero between
 // calls), then the partial LSEs and outputs.
+// Largest draft count per request of the cascade expand table (one thread
+// walks a request's n x n mask entries).
+constexpr int32_t kMaxDraft = 256;
+
 constexpr int64_t kPrefillWorkgroups = 256;
 constexpr int64_t kMinSplitTiles = 4;
 
@@ -487,6 +491,129 @@ pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num
   a.lse = lse;
   return pkv_host::from_hip(pkv_launch::sparse_topk(a, static_cast<hipStream_t>(stream)),
                             "sparse_topk_decode launch");
+}
+
+pkv_status_t build_cascade_expand_table(const uint8_t* custom_mask, int64_t mask_len,
+                                        const int32_t* req_to_token, int64_t req_to_token_rows,
+                                        int64_t req_to_token_stride,
+                                        const int32_t* req_pool_indices, const int32_t* seq_lens,
+                                        int32_t batch, int32_t num_draft, int32_t* expand_table,
+                                        int32_t* expand_lens, int32_t* cu_expand_lens,
+                                        void* stream) {
+  PKV_REQUIRE(batch >= 0 && mask_len >= 0, PKV_EINVAL,
+              "build_cascade_expand_table: batch %d, mask_len %lld", batch, (long long)mask_len);
+  PKV_REQUIRE(num_draft >= 1, PKV_EINVAL, "build_cascade_expand_table: num_draft %d < 1",
+              num_draft);
+  PKV_REQUIRE(num_draft <= pkv_host::kMaxDraft, PKV_EUNSUPPORTED,
+              "build_cascade_expand_table: num_draft %d > %d", num_draft, pkv_host::kMaxDraft);
+  if (batch == 0) return pkv_host::ok();
+  PKV_REQUIRE(custom_mask && req_to_token && req_pool_indices && seq_lens && expand_table &&
+                  expand_lens,
+              PKV_EINVAL, "build_cascade_expand_table: NULL required pointer");
+  PKV_REQUIRE(req_to_token_rows >= 1 && req_to_token_stride >= 1, PKV_EINVAL,
+              "build_cascade_expand_table: empty token table");
+  pkv::CascadeExpandArgs a;
+  a.mask = custom_mask;
+  a.mask_len = mask_len;
+  a.req_to_token = req_to_token;
+  a.r2t_rows = req_to_token_rows;
+  a.r2t_stride = req_to_token_stride;
+  a.req_pool_indices = req_pool_indices;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.num_draft = num_draft;
+  a.table = expand_table;
+  a.lens = expand_lens;
+  a.cu = cu_expand_lens;
+  return pkv_host::from_hip(pkv_launch::cascade_expand(a, static_cast<hipStream_t>(stream)),
+                            "build_cascade_expand_table launch");
+}
+
+static pkv_status_t expand_merge_prepare(const char* who, const void* q, int32_t dtype,
+                                         const void* k_cache, const void* v_cache,
+                                         int64_t num_slots, const int32_t* expand_table,
+                                         int32_t expand_stride, const int32_t* expand_lens,
+                                         int32_t n_rows, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         float softmax_scale, void* out, float* lse,
+                                         pkv::ExpandMergeArgs& a) {
+  PKV_REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "%s: dtype %d not supported (bf16)", who,
+              dtype);
+  PKV_REQUIRE(head_dim == 64 || head_dim == 128, PKV_EUNSUPPORTED,
+              "%s: head_dim %d not supported (64, 128)", who, head_dim);
+  PKV_REQUIRE(n_rows >= 0 && num_q_heads >= 1 && num_kv_heads >= 1 && expand_stride >= 1,
+              PKV_EINVAL, "%s: bad sizes", who);
+  PKV_REQUIRE(num_q_heads % num_kv_heads == 0, PKV_EINVAL,
+              "%s: num_q_heads %d not a multiple of num_kv_heads %d", who, num_q_heads,
+              num_kv_heads);
+  PKV_REQUIRE(num_q_heads / num_kv_heads <= 16, PKV_EUNSUPPORTED, "%s: GQA group %d > 16", who,
+              num_q_heads / num_kv_heads);
+  PKV_REQUIRE(n_rows == 0 || (q && k_cache && v_cache && expand_table && expand_lens && out &&
+                              lse),
+              PKV_EINVAL, "%s: NULL required pointer (out and lse are both needed)", who);
+  PKV_REQUIRE(n_rows == 0 || num_slots >= 1, PKV_EINVAL, "%s: empty cache", who);
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.num_slots = num_slots;
+  a.table = expand_table;
+  a.lens = expand_lens;
+  a.stride = expand_stride;
+  a.rows = n_rows;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.scale_log2 = pkv_host::scale_log2(softmax_scale);
+  a.out = out;
+  a.lse = lse;
+  return pkv_host::ok();
+}
+
+pkv_status_t paged_attn_expand_merge(const void* q, int32_t dtype, const void* k_cache,
+                                     const void* v_cache, int64_t num_slots,
+                                     const int32_t* expand_table, int32_t expand_stride,
+                                     const int32_t* expand_lens, int32_t n_rows,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     float softmax_scale, void* out, float* lse, void* stream) {
+  pkv::ExpandMergeArgs a;
+  const pkv_status_t st = expand_merge_prepare(
+      "paged_attn_expand_merge", q, dtype, k_cache, v_cache, num_slots, expand_table,
+      expand_stride, expand_lens, n_rows, num_q_heads, num_kv_heads, head_dim, softmax_scale,
+      out, lse, a);
+  if (st != PKV_OK || n_rows == 0) return st;
+  return pkv_host::from_hip(pkv_launch::expand_merge(a, head_dim, static_cast<hipStream_t>(stream)),
+                            "paged_attn_expand_merge launch");
+}
+
+pkv_status_t paged_attn_cascade(const void* q, int32_t dtype, const void* k_cache,
+                                const void* v_cache, int64_t num_pages, const int32_t* page_table,
+                                int32_t pt_stride, const int32_t* cu_seqlens_q,
+                                const int32_t* kv_lens, int32_t batch, int32_t total_q,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                float softmax_scale, const int32_t* expand_table,
+                                int32_t expand_stride, const int32_t* expand_lens,
+                                void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                void* stream) {
+  // every check before anything is enqueued
+  pkv::PrefillArgs pa;
+  bool nothing = false;
+  pkv_status_t st = prefill_prepare(
+      q, dtype, k_cache, v_cache, num_pages, page_table, pt_stride, cu_seqlens_q, kv_lens, batch,
+      total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, page_size,
+      softmax_scale, 0, -1, 0, workspace, workspace_bytes, out, lse, pa, &nothing);
+  if (st != PKV_OK) return st;
+  pkv::ExpandMergeArgs ea;
+  st = expand_merge_prepare("paged_attn_cascade", q, dtype, k_cache, v_cache,
+                            num_pages * page_size, expand_table, expand_stride, expand_lens,
+                            total_q, num_q_heads, num_kv_heads, head_dim, softmax_scale, out, lse,
+                            ea);
+  if (st != PKV_OK || nothing) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = pkv_host::from_hip(pkv_launch::prefill(pa, head_dim, s),
+                          "paged_attn_cascade: prefix pass launch");
+  if (st != PKV_OK) return st;
+  return pkv_host::from_hip(pkv_launch::expand_merge(ea, head_dim, s),
+                            "paged_attn_cascade: expand pass launch");
 }
 
 }  // extern "C"

@@ -88,4 +88,32 @@ struct SparseArgs {
   float* lse;
 };
 
+// Expand-pass key lists of cascade attention (one row per draft token).
+struct CascadeExpandArgs {
+  const uint8_t* mask;   // flat custom mask: per request n rows of L_b + n entries
+  int64_t mask_len;
+  const int32_t* req_to_token;
+  int64_t r2t_rows, r2t_stride;
+  const int32_t* req_pool_indices;
+  const int32_t* seq_lens;   // committed tokens L_b
+  int32_t batch, num_draft;
+  int32_t* table;            // [batch * n, n] slots
+  int32_t* lens;             // [batch * n]
+  int32_t* cu;               // [batch * n + 1] or null
+};
+
+// Expand pass + merge: each q row over its listed slots, merged into out / lse.
+struct ExpandMergeArgs {
+  const void* q;   // [rows, hq, D] bf16
+  const void* k;   // cache viewed as [num_slots, hkv, D] bf16
+  const void* v;
+  int64_t num_slots;
+  const int32_t* table;   // [rows, stride] slots
+  const int32_t* lens;    // [rows]
+  int32_t stride, rows, hq, hkv;
+  float scale_log2;
+  void* out;    // [rows, hq, D] bf16, in: prefix-pass O, out: merged O
+  float* lse;   // [rows, hq], in: prefix-pass LSE, out: merged LSE
+};
+
 }  // namespace pkv

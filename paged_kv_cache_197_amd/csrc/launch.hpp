@@ -10,6 +10,8 @@ struct PageTableArgs;
 struct DecodeArgs;
 struct PrefillArgs;
 struct SparseArgs;
+struct CascadeExpandArgs;
+struct ExpandMergeArgs;
 }  // namespace pkv
 
 namespace pkv_launch {
@@ -23,4 +25,6 @@ hipError_t kv_append(const void* k_new, const void* v_new, const int32_t* loc, i
                      hipStream_t stream);
 size_t sparse_workspace_bytes(int batch, int topk, int num_q_heads, int head_dim_v);
 hipError_t sparse_topk(const pkv::SparseArgs& a, hipStream_t stream);
+hipError_t cascade_expand(const pkv::CascadeExpandArgs& a, hipStream_t stream);
+hipError_t expand_merge(const pkv::ExpandMergeArgs& a, int head_dim, hipStream_t stream);
 }  // namespace pkv_launch

@@ -20,7 +20,8 @@ def test_header_declares_the_entry_points():
     for fn in ["build_page_table", "paged_attn_varlen_prefill", "paged_attn_decode_splitkv",
                "merge_state", "sparse_topk_decode", "paged_attn_varlen_prefill_workspace_size",
                "sparse_topk_decode_workspace_size", "paged_kv_append",
-               "paged_attn_varlen_prefill_append"]:
+               "paged_attn_varlen_prefill_append", "build_cascade_expand_table",
+               "paged_attn_expand_merge", "paged_attn_cascade"]:
         assert fn in names
 
 
@@ -172,3 +173,32 @@ def test_append_argument_errors():
     bad = list(args)
     bad[15] = 96                                                               # head_dim
     assert pa(*bad, fake, fake, fake, None, 0, fake, None, None) == EUNSUP
+
+
+def test_cascade_argument_errors():
+    lib = pkv.load_library()
+    fake = ctypes.c_void_p(256)
+    ex = lib.build_cascade_expand_table
+    # mask len r2t rows stride rpi sl B n table lens cu stream
+    assert ex(None, 0, None, 1, 1, None, None, 0, 4, None, None, None, None) == 0   # no requests
+    assert ex(fake, 100, fake, 4, 64, fake, fake, 2, 0, fake, fake, None, None) == EINVAL
+    assert ex(fake, 100, fake, 4, 64, fake, fake, 2, 257, fake, fake, None, None) == EUNSUP
+    assert ex(None, 100, fake, 4, 64, fake, fake, 2, 4, fake, fake, None, None) == EINVAL
+    assert ex(fake, 100, fake, 0, 64, fake, fake, 2, 4, fake, fake, None, None) == EINVAL
+    em = lib.paged_attn_expand_merge
+    # q dtype k v slots table stride lens rows Hq Hkv D scale out lse stream
+    assert em(None, 1, None, None, 0, None, 8, None, 0, 32, 8, 128, 0.1, None, None, None) == 0
+    assert em(fake, 0, fake, fake, 9, fake, 8, fake, 4, 32, 8, 128, 0.1, fake, fake, None) == EUNSUP
+    assert em(fake, 1, fake, fake, 9, fake, 8, fake, 4, 32, 8, 96, 0.1, fake, fake, None) == EUNSUP
+    assert em(fake, 1, fake, fake, 9, fake, 8, fake, 4, 30, 8, 128, 0.1, fake, fake, None) == EINVAL
+    assert em(fake, 1, fake, fake, 9, fake, 8, fake, 4, 32, 8, 128, 0.1, fake, None, None) == EINVAL
+    assert b"lse" in lib.pkv_last_error()
+    cz = lib.paged_attn_cascade
+    # q dtype k v pages pt stride cu kl B Tq Mq Mk Hq Hkv D P scale tab tstride lens ws bytes
+    #   out lse stream
+    base = [fake, 1, fake, fake, 64, fake, 4, fake, fake, 2, 16, 8, 256, 32, 8, 128, 64, 0.1]
+    assert cz(*base, fake, 8, fake, None, 0, fake, None, None) == EINVAL        # lse required
+    assert cz(*base, None, 8, fake, None, 0, fake, fake, None) == EINVAL        # no table
+    bad = list(base)
+    bad[15] = 96
+    assert cz(*bad, fake, 8, fake, None, 0, fake, fake, None) == EUNSUP
