@@ -34,7 +34,7 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--only", choices=["all", "decode", "decode_window", "prefill",
                                       "prefill_long", "prefill_window", "prefill_append", "swa",
-                                      "sparse", "copy"],
+                                      "sparse", "cascade", "copy"],
                    default="all", help="restrict to one workload (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -316,6 +316,51 @@ def run_prefill_append(torch, pkv, workloads, args):
                              c.q.shape[2])
     append_bytes = 2 * 2 * kn.numel() * kn.element_size() + 4 * loc.numel()
     return dict(ms=ms, call_ms=call_ms, flops=flops, append_bytes=append_bytes)
+
+
+def run_cascade(torch, pkv, workloads, args):
+    """Draft-tree verification by cascade attention: expand-table build, then
+    the prefix pass (prefill kernel, non-causal) and the expand pass + merge."""
+    dev = torch.device("cuda:0")
+    c = workloads.cascade_verify(value_device=dev)
+    r2t, rpi, sl = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev))
+    mask = c.custom_mask.to(dev)
+    B, n = sl.numel(), c.num_draft
+    _, hq, d = c.q.shape
+    hkv = c.k_cache.shape[2]
+    pt, kl, _ = pkv.build_page_table(r2t, rpi, sl, c.page_size, c.table_width,
+                                     with_cu_seqlens=False)
+    tab = torch.empty((B * n, n), dtype=torch.int32, device=dev)
+    lens = torch.empty((B * n,), dtype=torch.int32, device=dev)
+    cu_q = torch.arange(0, B * n + 1, n, dtype=torch.int32, device=dev)
+    out = torch.empty_like(c.q)
+    lse = torch.empty((B * n, hq), dtype=torch.float32, device=dev)
+    max_k = int(c.seq_lens.max())
+    ws_bytes = pkv.paged_attn_varlen_prefill_workspace_size(B, B * n, n, max_k, hq, hkv, d)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    build_t = Timer(torch)
+
+    def step(timer):
+        e_b = build_t.mark() if timer else None
+        pkv.build_cascade_expand_table(mask, r2t, rpi, sl, n, expand_table=tab, expand_lens=lens,
+                                       with_cu=False)
+        e0 = timer.mark() if timer else None
+        if timer:
+            build_t.pairs.append((e_b, e0))
+        pkv.paged_attn_cascade(c.q, c.k_cache, c.v_cache, pt, cu_q, kl, n, c.scale, tab, lens,
+                               max_seqlen_k=max_k, workspace=ws, out=out, lse=lse)
+        if timer:
+            timer.pairs.append((e0, timer.mark()))
+
+    ms, kern_ms = device_loop(torch, step, max(args.steps, 20), args.warmup, host_us_per_step=150.0)
+    torch.cuda.synchronize()
+    sum_l = int(c.seq_lens.long().sum())
+    vis = int(lens.long().sum())
+    row_bytes = 2 * hkv * d * 2                     # K and V of one token, all kv heads
+    nbytes = (sum_l + B * n) * row_bytes + 2 * B * n * hq * d * 2 + B * n * hq * 4
+    flops = 4 * d * hq * (n * sum_l + vis)
+    return dict(ms=ms, kernel_ms=kern_ms, build_ms=build_t.kernel_ms(), bytes=nbytes, flops=flops,
+                sum_l=sum_l, batch=B, n=n, ws=ws_bytes)
 
 
 def run_sparse(torch, pkv, workloads, args):
@@ -683,6 +728,26 @@ def main(argv=None):
                 "attention_TFLOP/s_over_call": round(r["flops"] / (r["call_ms"] * 1e-3) / 1e12, 2)}
         except Exception as e:
             extra["prefill_append"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "cascade"):
+        try:
+            r = run_cascade(torch, pkv, workloads, args)
+            extra["cascade_verify"] = {
+                "workload": "draft-tree verification by cascade attention: B=64, committed "
+                            "L~U[1024,16384], 8 drafts per request (random tree), 32 q / 8 kv "
+                            "heads, D=128, page 64; expand-table build + prefix pass (prefill "
+                            "kernel, non-causal) + expand pass and merge",
+                "device_ms_per_step": round(r["ms"], 4),
+                "cascade_ms": round(r["kernel_ms"], 4), "table_build_ms": round(r["build_ms"], 4),
+                "cascade_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
+                "cascade_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+                                          / HBM_PEAK_GBS, 4),
+                "TFLOP/s": round(r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12, 2),
+                "algorithmic_bytes": r["bytes"], "flops": r["flops"],
+                "sum_committed_len": r["sum_l"], "prefill_workspace_bytes": r["ws"]}
+        except Exception as e:
+            extra["cascade_verify"] = {"error": repr(e)}
         torch.cuda.empty_cache()
 
     if args.only in ("all", "sparse"):

@@ -50,8 +50,8 @@ static float scale_log2(float softmax_scale) {
 // that about kPrefillWorkgroups workgroups run, never below kMinSplitTiles
 // tiles per split. The workspace holds the split counters (zero between
 // calls), then the partial LSEs and outputs.
-// Largest draft count per request of the cascade expand table (one thread
-// walks a request's n x n mask entries).
+// Largest draft count per request of the cascade expand table (a wave holds a
+// request's draft columns, four per lane).
 constexpr int32_t kMaxDraft = 256;
 
 constexpr int64_t kPrefillWorkgroups = 256;

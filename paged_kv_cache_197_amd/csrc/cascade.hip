@@ -10,10 +10,8 @@
 //
 // cascade_expand_kernel builds the expand pass's key lists: row (b, i) lists
 // the slots of the visible drafts in position order, then the hidden ones, and
-// its length is the visible count (plus the lengths' prefix sum). One
-// workgroup walks the requests 256 at a time; a block scan gives each
-// request's offset into the flat mask (request blocks of n rows of L_b + n
-// entries) and into the prefix sum.
+// its length is the visible count; expand_cu_kernel adds the lengths' prefix
+// sum when asked for.
 //
 // expand_merge_kernel runs the expand pass and the merge in one pass: one
 // wave per (draft row, kv head) holds the G query heads of that kv head with
@@ -27,77 +25,88 @@
 
 namespace pkv {
 
+// One wave per request. Its mask block starts after the blocks of the
+// requests before it: n * (sum of their L) + b * n * n entries, summed by the
+// wave from seq_lens. Lane j holds draft column j (and j + 64, ... for n > 64):
+// its slot, and per row its mask byte; a ballot gives each visible column its
+// place among the visible ones and each hidden column its place after them.
+constexpr int kExpandChunks = 4;   // columns per lane: n <= 256
+
 __global__ __launch_bounds__(256) void cascade_expand_kernel(CascadeExpandArgs a) {
-  __shared__ int64_t s_off[256];
-  __shared__ int32_t s_cnt[256];
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= a.batch) return;   // wave-uniform
   const int n = a.num_draft;
-  int64_t mask_base = 0;   // mask entries of the requests before this chunk
-  int32_t cu_base = 0;     // listed keys of the requests before this chunk
-  if (tid == 0 && a.cu != nullptr) a.cu[0] = 0;
-  for (int b0 = 0; b0 < a.batch; b0 += 256) {
-    const int b = b0 + tid;
-    const bool live = b < a.batch;
-    const int L = live ? max(a.seq_lens[b], 0) : 0;
-    const int64_t blk = live ? static_cast<int64_t>(n) * (L + n) : 0;
+  const uint8_t* __restrict__ mask = a.mask;
+  int32_t* __restrict__ table = a.table;
 
-    // inclusive scan of the requests' mask block sizes
-    s_off[tid] = blk;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int64_t v = tid >= off ? s_off[tid - off] : 0;
-      __syncthreads();
-      s_off[tid] += v;
-      __syncthreads();
+  int64_t before = 0;   // committed tokens of the requests before b
+  for (int t = lane; t < b; t += 64) before += max(a.seq_lens[t], 0);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) before += __shfl_xor(before, m);
+  const int L = max(a.seq_lens[b], 0);
+  const int64_t start = static_cast<int64_t>(n) * before + static_cast<int64_t>(b) * n * n;
+
+  const int64_t row = clamp_index(a.req_pool_indices[b], a.r2t_rows);
+  const int32_t* r2t = a.req_to_token + row * a.r2t_stride;
+  const int64_t last_col = a.r2t_stride - 1;
+  int32_t slot[kExpandChunks];
+#pragma unroll
+  for (int c = 0; c < kExpandChunks; ++c) {
+    const int j = 64 * c + lane;
+    slot[c] = j < n ? r2t[min(static_cast<int64_t>(L) + j, last_col)] : 0;
+  }
+  const uint64_t below = (1ull << lane) - 1;   // lanes before this one
+  for (int i = 0; i < n; ++i) {
+    const int64_t m0 = start + static_cast<int64_t>(i) * (L + n) + L;
+    uint64_t vis[kExpandChunks];
+    int total = 0;
+#pragma unroll
+    for (int c = 0; c < kExpandChunks; ++c) {
+      const int j = 64 * c + lane;
+      const int64_t mi = m0 + j;
+      const bool v = j < n && mi < a.mask_len && mask[mi] != 0;
+      vis[c] = __ballot(v);
+      total += __popcll(vis[c]);
     }
-    const int64_t start = mask_base + s_off[tid] - blk;
-
-    int32_t listed = 0;
-    if (live) {
-      const int64_t row = clamp_index(a.req_pool_indices[b], a.r2t_rows);
-      const int32_t* r2t = a.req_to_token + row * a.r2t_stride;
-      const int64_t last_col = a.r2t_stride - 1;
-      for (int i = 0; i < n; ++i) {
-        const int64_t m0 = start + static_cast<int64_t>(i) * (L + n) + L;
-        int32_t* out = a.table + (static_cast<int64_t>(b) * n + i) * n;
-        int k = 0;
-        for (int pass = 0; pass < 2; ++pass) {   // visible drafts, then hidden ones
-          for (int j = 0; j < n; ++j) {
-            const int64_t mi = m0 + j;
-            const bool vis = mi < a.mask_len && a.mask[mi] != 0;
-            if (vis == (pass == 0)) {
-              const int64_t col = min(static_cast<int64_t>(L) + j, last_col);
-              out[k++] = r2t[col];
-            }
-          }
-          if (pass == 0) {
-            a.lens[static_cast<int64_t>(b) * n + i] = k;
-            listed += k;
-          }
-        }
+    int32_t* out = table + (static_cast<int64_t>(b) * n + i) * n;
+    int vis_before = 0;   // visible columns in earlier chunks
+#pragma unroll
+    for (int c = 0; c < kExpandChunks; ++c) {
+      const int j = 64 * c + lane;
+      if (j < n) {
+        const bool v = (vis[c] >> lane) & 1;
+        const int vb = vis_before + __popcll(vis[c] & below);   // visible columns before j
+        out[v ? vb : total + (j - vb)] = slot[c];
       }
+      vis_before += __popcll(vis[c]);
     }
+    if (lane == 0) a.lens[static_cast<int64_t>(b) * n + i] = total;
+  }
+}
 
-    // exclusive scan of the requests' listed keys for the prefix sum
-    s_cnt[tid] = listed;
+// Zero-led prefix sum of the expand lengths (rows = batch * n), one workgroup
+// of 1024 threads scanning 1024 rows at a time.
+__global__ __launch_bounds__(1024) void expand_cu_kernel(const int32_t* __restrict__ lens,
+                                                         int64_t rows, int32_t* __restrict__ cu) {
+  __shared__ int32_t s[1024];
+  const int tid = threadIdx.x;
+  int32_t carry = 0;
+  if (tid == 0) cu[0] = 0;
+  for (int64_t r0 = 0; r0 < rows; r0 += 1024) {
+    const int64_t r = r0 + tid;
+    const int32_t v = r < rows ? lens[r] : 0;
+    s[tid] = v;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int32_t v = tid >= off ? s_cnt[tid - off] : 0;
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int32_t u = tid >= off ? s[tid - off] : 0;
       __syncthreads();
-      s_cnt[tid] += v;
+      s[tid] += u;
       __syncthreads();
     }
-    if (live && a.cu != nullptr) {
-      int32_t run = cu_base + s_cnt[tid] - listed;
-      for (int i = 0; i < n; ++i) {
-        const int64_t r = static_cast<int64_t>(b) * n + i;
-        run += a.lens[r];   // written above by this thread
-        a.cu[r + 1] = run;
-      }
-    }
-    mask_base += s_off[255];
-    cu_base += s_cnt[255];
-    __syncthreads();   // the next chunk reuses the scan arrays
+    if (r < rows) cu[r + 1] = carry + s[tid];
+    carry += s[1023];
+    __syncthreads();   // the next chunk reuses s
   }
 }
 
@@ -205,7 +214,11 @@ __global__ __launch_bounds__(256) void expand_merge_kernel(ExpandMergeArgs a) {
 namespace pkv_launch {
 
 hipError_t cascade_expand(const pkv::CascadeExpandArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(pkv::cascade_expand_kernel, dim3(1), dim3(256), 0, stream, a);
+  if (a.batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pkv::cascade_expand_kernel, dim3((a.batch + 3) / 4), dim3(256), 0, stream, a);
+  if (a.cu != nullptr)
+    hipLaunchKernelGGL(pkv::expand_cu_kernel, dim3(1), dim3(1024), 0, stream, a.lens,
+                       static_cast<int64_t>(a.batch) * a.num_draft, a.cu);
   return hipGetLastError();
 }
 
