@@ -28,6 +28,11 @@ from .reference import (  # noqa: F401
     cascade_expand_table,
     causal_key_ranges,
     cu_seqlens,
+    dca_decode,
+    dca_decode_reference,
+    dca_decode_tables,
+    dca_query_chunk,
+    dca_scaling_factor,
     gather_paged,
     key_lower_bound,
     kv_append,
@@ -40,6 +45,7 @@ from .reference import (  # noqa: F401
     paged_decode_splitkv,
     paged_prefill,
     paged_prefill_append,
+    round_to_bf16,
     softmax_attention,
     sparse_topk_decode,
     tree_verify_attention,

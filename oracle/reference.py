@@ -511,6 +511,146 @@ def cascade_attention(q, k_cache, v_cache, page_table, seq_lens, page_size, expa
     return merge_state(np.stack([o1, o2[0]]), np.stack([l1, l2[0]]))
 
 
+# ---------------------------------------------------------------------------
+# Dual chunk attention, decode (intra / succ / inter stages)
+# ---------------------------------------------------------------------------
+
+def round_to_bf16(x) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16 (ties to even), returned
+    as float32: keep the upper 16 bits of the IEEE single after adding half an
+    upper-unit (minus one when the kept part is even). NaN stays NaN."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
+    out = r.view(np.float32)
+    return np.where(np.isnan(f), f, out)
+
+
+def dca_scaling_factor(seq_lens, original_max_position_embeddings) -> np.ndarray:
+    """[DCA] ``init_forward_metadata``: with ``original_max_position_embeddings
+    > 0`` each request's queries are multiplied by
+    ``max(0.1 * ln(L / original_max_position_embeddings) + 1, 1)``."""
+    L = np.asarray(seq_lens, dtype=np.float64)
+    return np.maximum(0.1 * np.log(L / float(original_max_position_embeddings)) + 1.0, 1.0)
+
+
+def dca_query_chunk(seq_lens, chunk_len) -> np.ndarray:
+    """[DCA] ``init_forward_metadata`` (decode): the chunk holding the query,
+    ``chunk_num_curr = (L - 1) // chunk_len``."""
+    return (np.asarray(seq_lens, dtype=np.int64) - 1) // int(chunk_len)
+
+
+def dca_decode_tables(block_tables, seq_lens, chunk_size, local_size, page_size):
+    """Per-request key ranges and page tables of the three decode stages.
+
+    [DCA] ``init_forward_metadata`` (decode): ``chunk_len = chunk_size -
+    local_size``, ``c = (L - 1) // chunk_len`` (the chunk holding the query);
+    intra: keys ``[c*chunk_len, L)``, table ``block_tables[b, st:ed]`` from
+    ``st = c*chunk_len // P`` up to ``(L - 1) // P + 1``; succ: ``chunk_len``
+    keys (0 when ``c = 0``) from page ``max(c - 1, 0)*chunk_len // P``; inter:
+    ``max(c - 1, 0)*chunk_len`` keys from key 0 through the full table. Table
+    widths follow the page: ``(max length - 1) // P + 1`` columns, zero past a
+    row's pages; the succ table exists only when some request has succ keys.
+
+    Returns dict(lens_intra, table_intra, lens_succ, table_succ or None,
+    lens_inter), int64 arrays.
+    """
+    bt = np.asarray(block_tables, dtype=np.int64)
+    L = np.asarray(seq_lens, dtype=np.int64)
+    batch = len(L)
+    chunk_len = int(chunk_size) - int(local_size)
+    P = int(page_size)
+    c = dca_query_chunk(L, chunk_len)
+    lens_intra = L - c * chunk_len
+    w = (int(lens_intra.max()) - 1) // P + 1
+    table_intra = np.zeros((batch, w), dtype=np.int64)
+    for i in range(batch):
+        st = int(c[i]) * chunk_len // P
+        ed = min(st + w, (int(L[i]) - 1) // P + 1)
+        table_intra[i, :ed - st] = bt[i, st:ed]
+    lens_succ = (c - np.maximum(c - 1, 0)) * chunk_len
+    table_succ = None
+    if int(lens_succ.max()) > 0:
+        ws = (int(lens_succ.max()) - 1) // P + 1
+        table_succ = np.zeros((batch, ws), dtype=np.int64)
+        for i in range(batch):
+            st = int(max(c[i] - 1, 0)) * chunk_len // P
+            ed = min(st + ws, (int(L[i]) - 1) // P + 1)
+            table_succ[i, :ed - st] = bt[i, st:ed]
+    lens_inter = np.maximum(c - 1, 0) * chunk_len
+    return dict(lens_intra=lens_intra, table_intra=table_intra, lens_succ=lens_succ,
+                table_succ=table_succ, lens_inter=lens_inter)
+
+
+def dca_decode(q, q_succ, q_inter, k_cache, v_cache, block_tables, seq_lens, page_size, scale,
+               chunk_size, local_size, original_max_position_embeddings=0, q_bf16=True):
+    """Dual chunk attention decode in the page's three stages.
+
+    [DCA] ``_dual_chunk_flash_attn_decoding``: (optionally) scale the three
+    queries per request by ``dca_scaling_factor`` and round them back to the
+    query dtype; run a non-causal paged decode per stage -- ``q`` over the
+    intra table, ``q_succ`` over the succ table, ``q_inter`` over the full
+    table with the inter lengths -- each returning LSE, an empty stage giving
+    ``(0, -inf)`` (``_dual_chunk_flash_attn_decoding_with_exp_sums``); merge
+    the stages by their LSEs. Returns O [B, Hq, D] and the merged LSE.
+    """
+    qs = [np.asarray(x, dtype=np.float64) for x in (q, q_succ, q_inter)]
+    if original_max_position_embeddings > 0:
+        sf = dca_scaling_factor(seq_lens, original_max_position_embeddings).astype(np.float32)
+        scaled = []
+        for x in qs:
+            y = x.astype(np.float32) * sf[:, None, None]
+            scaled.append((round_to_bf16(y) if q_bf16 else y).astype(np.float64))
+        qs = scaled
+    t = dca_decode_tables(block_tables, seq_lens, chunk_size, local_size, page_size)
+    parts_o, parts_l = [], []
+    o, l_ = paged_decode_splitkv(qs[0], k_cache, v_cache, t["table_intra"], t["lens_intra"],
+                                 page_size, scale, 0, 1)
+    parts_o.append(o[0])
+    parts_l.append(l_[0])
+    if t["table_succ"] is not None:
+        o, l_ = paged_decode_splitkv(qs[1], k_cache, v_cache, t["table_succ"], t["lens_succ"],
+                                     page_size, scale, 0, 1)
+        parts_o.append(o[0])
+        parts_l.append(l_[0])
+    if int(t["lens_inter"].max()) > 0:
+        o, l_ = paged_decode_splitkv(qs[2], k_cache, v_cache, np.asarray(block_tables),
+                                     t["lens_inter"], page_size, scale, 0, 1)
+        parts_o.append(o[0])
+        parts_l.append(l_[0])
+    return merge_state(np.stack(parts_o), np.stack(parts_l))
+
+
+def dca_decode_reference(q, q_succ, q_inter, k_cache, v_cache, block_tables, seq_lens,
+                         page_size, scale, chunk_len):
+    """The plain definition the three stages reach: one softmax over all ``L``
+    keys in which key ``t`` is scored with the query of its stage -- ``q`` in
+    the query's own chunk ``[c*chunk_len, L)``, ``q_succ`` in the chunk before
+    it, ``q_inter`` before that (``c = (L - 1) // chunk_len``)."""
+    qs = [np.asarray(x, dtype=np.float64) for x in (q, q_succ, q_inter)]
+    batch, num_q_heads, _ = qs[0].shape
+    num_kv_heads = k_cache.shape[2]
+    out = np.zeros((batch, num_q_heads, v_cache.shape[3]), dtype=np.float64)
+    lse = np.full((batch, num_q_heads), NEG_INF, dtype=np.float64)
+    for b in range(batch):
+        L = int(seq_lens[b])
+        keys = gather_paged(k_cache, block_tables[b], L, page_size)
+        vals = gather_paged(v_cache, block_tables[b], L, page_size)
+        c = (L - 1) // chunk_len
+        stage = np.where(np.arange(L) >= c * chunk_len, 0,
+                         np.where(np.arange(L) >= (c - 1) * chunk_len, 1, 2))
+        for h in range(num_q_heads):
+            kvh = kv_head_of(h, num_q_heads, num_kv_heads)
+            s = np.array([scale * float(qs[stage[t]][b, h] @ keys[t, kvh]) for t in range(L)])
+            m = s.max()
+            w = np.exp(s - m)
+            total = math.fsum(w)
+            out[b, h] = (w[:, None] * vals[:, kvh]).sum(axis=0) / total
+            lse[b, h] = m + math.log(total)
+    return out, lse
+
+
 def sparse_topk_decode(q, kv_cache, req_to_token, req_pool_indices, topk_idx, scale,
                        head_dim_v):
     """Top-k index-gathered MLA decode over one latent KV head.

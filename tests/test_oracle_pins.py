@@ -761,3 +761,105 @@ def test_planted_expand_order_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "cascade_expand_table", unsorted)
     with pytest.raises(AssertionError):
         test_cascade_equals_tree_attention(1, 5, "random")
+
+
+# ---------------------------------------------------------------------------
+# Dual chunk attention decode
+# ---------------------------------------------------------------------------
+
+def test_round_to_bf16_matches_torch():
+    x = torch.randn(20000, generator=torch.Generator().manual_seed(3)) * 7
+    x[:4] = torch.tensor([0.0, -0.0, 1e-30, 3.0e38])
+    assert np.array_equal(oracle.round_to_bf16(x.numpy()),
+                          x.to(torch.bfloat16).to(torch.float32).numpy())
+
+
+def test_dca_scaling_factor_closed_forms():
+    omp = 4096
+    sf = oracle.dca_scaling_factor([4096, 2048, 1, int(round(4096 * math.e ** 10)), 4096 * 2],
+                                   omp)
+    assert sf[0] == 1.0 and sf[1] == 1.0 and sf[2] == 1.0          # clipped at 1
+    assert abs(sf[3] - 2.0) < 1e-9
+    assert abs(sf[4] - (1 + 0.1 * math.log(2))) < 1e-15
+
+
+def _dca_case(seed, lens, P, dtype=torch.float32, hq=4, hkv=2, d=8):
+    c = workloads.make_decode_case(seed, seq_lens=lens, num_q_heads=hq, num_kv_heads=hkv,
+                                   head_dim=d, page_size=P,
+                                   num_pages=sum(-(-x // P) for x in lens) + 3, dtype=dtype)
+    g = torch.Generator().manual_seed(seed + 1000)
+    q_succ = torch.randn(c.q.shape, generator=g).to(dtype)
+    q_inter = torch.randn(c.q.shape, generator=g).to(dtype)
+    pt, kl, _ = oracle.page_table_strided(i64(c.req_to_token), i64(c.req_pool_indices),
+                                          i64(c.seq_lens), P, c.table_width)
+    return c, q_succ, q_inter, pt, kl
+
+
+def test_dca_tables_cover_the_three_ranges():
+    """Brute force: the slots each stage reads are exactly the request's
+    positions [cC, L), [(c-1)C, cC) and [0, (c-1)C), read in order."""
+    chunk_size, local_size, P = 24, 8, 4
+    C = chunk_size - local_size
+    lens = [1, 15, 16, 17, 31, 32, 33, 48, 49, 70]
+    c, _, _, pt, kl = _dca_case(61, lens, P)
+    t = oracle.dca_decode_tables(pt, kl, chunk_size, local_size, P)
+    for b, L in enumerate(lens):
+        slot = lambda row, pos: int(row[pos // P]) * P + pos % P
+        full = [slot(pt[b], p) for p in range(L)]
+        cc = (L - 1) // C
+        got = [slot(t["table_intra"][b], p) for p in range(int(t["lens_intra"][b]))]
+        assert got == full[cc * C:L]
+        if t["table_succ"] is not None:
+            got = [slot(t["table_succ"][b], p) for p in range(int(t["lens_succ"][b]))]
+            assert got == full[max(cc - 1, 0) * C:cc * C] if cc >= 1 else got == []
+        assert int(t["lens_inter"][b]) == max(cc - 1, 0) * C
+
+
+@pytest.mark.parametrize("P,chunk_size,local_size", [(4, 24, 8), (1, 9, 1), (8, 40, 8)])
+def test_dca_decode_equals_single_softmax_definition(P, chunk_size, local_size):
+    C = chunk_size - local_size
+    lens = [1, C - 1, C, C + 1, 2 * C, 2 * C + 3, 3 * C + 5, 5 * C]
+    c, qs, qi, pt, kl = _dca_case(71 + P, lens, P)
+    o, lse = oracle.dca_decode(f64(c.q), f64(qs), f64(qi), f64(c.k_cache), f64(c.v_cache), pt, kl,
+                               P, c.scale, chunk_size, local_size)
+    o2, l2 = oracle.dca_decode_reference(f64(c.q), f64(qs), f64(qi), f64(c.k_cache),
+                                         f64(c.v_cache), pt, kl, P, c.scale, C)
+    assert np.abs(o - o2).max() < 1e-12 and np.abs(lse - l2).max() < 1e-12
+
+
+def test_dca_with_one_query_is_plain_decode():
+    """Equal queries in all stages: ordinary decode over all L keys (torch SDPA)."""
+    lens = [5, 16, 40, 77]
+    c, _, _, pt, kl = _dca_case(81, lens, 4)
+    o, lse = oracle.dca_decode(f64(c.q), f64(c.q), f64(c.q), f64(c.k_cache), f64(c.v_cache), pt,
+                               kl, 4, c.scale, 20, 4)
+    for b, L in enumerate(lens):
+        row = int(c.req_pool_indices[b])
+        K = dense_request_kv(c.k_cache, c.req_to_token, row, L)
+        V = dense_request_kv(c.v_cache, c.req_to_token, row, L)
+        ro, rl = sdpa_reference(c.q[b:b + 1].to(torch.float64), K, V, c.scale, causal=False)
+        assert np.abs(o[b] - ro[0]).max() < 1e-12 and np.abs(lse[b] - rl[0]).max() < 1e-12
+
+
+def test_dca_query_scaling_is_rounded_prescaling():
+    """With original_max_position_embeddings the stages see q * factor rounded
+    to bf16 (torch's own conversion here), the same as prescaled queries."""
+    lens = [30, 100, 257]
+    omp = 40
+    c, qs, qi, pt, kl = _dca_case(91, lens, 4, dtype=torch.bfloat16)
+    o, lse = oracle.dca_decode(f64(c.q), f64(qs), f64(qi), f64(c.k_cache), f64(c.v_cache), pt, kl,
+                               4, c.scale, 48, 16, original_max_position_embeddings=omp)
+    sf = torch.as_tensor(oracle.dca_scaling_factor(lens, omp), dtype=torch.float32)[:, None, None]
+    pre = [(x.float() * sf).to(torch.bfloat16) for x in (c.q, qs, qi)]
+    o2, l2 = oracle.dca_decode(*[f64(x) for x in pre], f64(c.k_cache), f64(c.v_cache), pt, kl, 4,
+                               c.scale, 48, 16)
+    assert np.abs(o - o2).max() < 1e-12 and np.abs(lse - l2).max() < 1e-12
+    assert sf.max() > 1.0
+
+
+def test_planted_dca_chunk_index_is_caught(monkeypatch):
+    """The query's chunk taken as L // chunk_len (off by one at chunk ends)."""
+    monkeypatch.setattr(ref, "dca_query_chunk",
+                        lambda sl, chunk_len: np.asarray(sl, dtype=np.int64) // int(chunk_len))
+    with pytest.raises(AssertionError):
+        test_dca_decode_equals_single_softmax_definition(4, 24, 8)
