@@ -285,6 +285,61 @@ pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num
                                 void* out, float* lse, void* stream);
 
 /*
+ * build_dca_decode_tables -- per-request metadata of dual chunk attention
+ * decode. [DCA] init_forward_metadata (decode): chunk_len = chunk_size -
+ * local_size, c = (L - 1) / chunk_len for L = seq_lens[b] (the cached length
+ * including the query token, L >= 1; L = 0 is read as c = 0):
+ *   lens_intra = L - c * chunk_len, table_intra row = block_tables row from
+ *     page c * chunk_len / page_size;
+ *   lens_succ = chunk_len if c >= 1 else 0, table_succ row from page
+ *     max(c - 1, 0) * chunk_len / page_size;
+ *   lens_inter = max(c - 1, 0) * chunk_len (read through the request's own row);
+ *   scaling_factor = max(0.1 * ln(L / original_max_position_embeddings) + 1, 1)
+ *     when original_max_position_embeddings > 0, else 1.
+ * Table rows hold chunk_len / page_size entries (the widest the pages' tables
+ * can be); entries past the request's last page, (L - 1) / page_size, are 0.
+ *
+ * block_tables [batch, bt_stride] int32 page ids (the strided page table)
+ * table_intra, table_succ [batch, chunk_len / page_size] int32 (out; table_succ
+ *   may be NULL); lens_intra, lens_succ, lens_inter [batch] int32 (out);
+ * scaling_factor [batch] fp32 (out) or NULL.
+ * Errors: PKV_EINVAL for chunk_len not a multiple of page_size ([DCA]
+ * _dual_chunk_flash_attn_decoding rejects it), bad sizes or NULL pointers.
+ */
+pkv_status_t build_dca_decode_tables(const int32_t* block_tables, int32_t bt_stride,
+                                     const int32_t* seq_lens, int32_t batch, int32_t chunk_len,
+                                     int32_t page_size, int32_t original_max_position_embeddings,
+                                     int32_t* table_intra, int32_t* lens_intra,
+                                     int32_t* table_succ, int32_t* lens_succ,
+                                     int32_t* lens_inter, float* scaling_factor, void* stream);
+
+/*
+ * paged_attn_dca_decode -- dual chunk attention decode as one split-KV pass.
+ * [DCA] _dual_chunk_flash_attn_decoding runs three decodes -- q over the
+ * query's own chunk (intra), q_succ over the chunk before it (succ), q_inter
+ * over all earlier keys (inter) -- and merges them by LSE. Here the key axis
+ * is cut into kv_chunk splits as in paged_attn_decode_splitkv (kv_chunk
+ * divides chunk_len, so a split lies inside one chunk) and each split scores
+ * its keys with the query of the stage its chunk belongs to; merge_state of
+ * the partials gives the three-stage result. With q_scale non-NULL the
+ * queries of request b are multiplied by q_scale[b] and rounded back to the
+ * query dtype first (the pages' scaling_factor; see build_dca_decode_tables).
+ *
+ * q, q_succ, q_inter [batch, num_q_heads, head_dim] dtype; other arguments,
+ * outputs, dtypes and errors as for paged_attn_decode_splitkv, plus
+ * PKV_EINVAL for chunk_len < 1 or not a multiple of kv_chunk (kv_chunk > 0).
+ */
+pkv_status_t paged_attn_dca_decode(const void* q, const void* q_succ, const void* q_inter,
+                                   int32_t dtype, const void* k_cache, const void* v_cache,
+                                   int64_t num_pages, const int32_t* page_table,
+                                   int32_t pt_stride, const int32_t* kv_lens, int32_t batch,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t page_size, float softmax_scale, int32_t chunk_len,
+                                   const float* q_scale, int32_t kv_chunk, int32_t num_splits,
+                                   float* o_partial, float* lse_partial, void* out, float* lse,
+                                   void* stream);
+
+/*
  * build_cascade_expand_table -- key lists of cascade attention's expand pass.
  * [FA] init_forward_metadata, target verify with topk > 1 ("create expand page
  * table"). Request b has L_b = seq_lens[b] committed tokens and n = num_draft

@@ -81,6 +81,11 @@ _SIGNATURES = {
     "sparse_topk_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "sparse_topk_decode": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _I64, _P, _P, _I32, _I32, _I32,
                                           _I32, _I32, _F, _P, _SZ, _P, _P, _P]),
+    "build_dca_decode_tables": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P,
+                                               _P, _P, _P, _P, _P]),
+    "paged_attn_dca_decode": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I64, _P, _I32, _P, _I32,
+                                             _I32, _I32, _I32, _I32, _F, _I32, _P, _I32, _I32, _P,
+                                             _P, _P, _P, _P]),
     "build_cascade_expand_table": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _P, _I32, _I32,
                                                   _P, _P, _P, _P]),
     "paged_attn_expand_merge": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _I32,
@@ -464,3 +469,71 @@ def paged_attn_cascade(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, m
         _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
     _check("paged_attn_cascade", st)
     return out, lse
+
+
+def build_dca_decode_tables(page_table, seq_lens, chunk_len, page_size,
+                            original_max_position_embeddings=0):
+    """Dual chunk attention decode metadata (see include/pkv.h). Returns a dict
+    of table_intra, lens_intra, table_succ, lens_succ, lens_inter,
+    scaling_factor (GPU tensors)."""
+    lib = load_library()
+    dev = page_table.device
+    pt = _i32(page_table, "page_table", dev)
+    sl = _i32(seq_lens, "seq_lens", dev)
+    batch = sl.numel()
+    width = max(int(chunk_len) // int(page_size), 1)
+    r = dict(table_intra=torch.empty((batch, width), dtype=torch.int32, device=dev),
+             table_succ=torch.empty((batch, width), dtype=torch.int32, device=dev),
+             lens_intra=torch.empty((batch,), dtype=torch.int32, device=dev),
+             lens_succ=torch.empty((batch,), dtype=torch.int32, device=dev),
+             lens_inter=torch.empty((batch,), dtype=torch.int32, device=dev),
+             scaling_factor=torch.empty((batch,), dtype=torch.float32, device=dev))
+    st = lib.build_dca_decode_tables(_ptr(pt), pt.shape[1], _ptr(sl), batch, int(chunk_len),
+                                     int(page_size), int(original_max_position_embeddings),
+                                     _ptr(r["table_intra"]), _ptr(r["lens_intra"]),
+                                     _ptr(r["table_succ"]), _ptr(r["lens_succ"]),
+                                     _ptr(r["lens_inter"]), _ptr(r["scaling_factor"]),
+                                     _stream(dev))
+    _check("build_dca_decode_tables", st)
+    return r
+
+
+def paged_attn_dca_decode(q, q_succ, q_inter, k_cache, v_cache, page_table, kv_lens,
+                          softmax_scale, chunk_len, *, kv_chunk=None, num_splits=None,
+                          q_scale=None, out=None, lse=None, o_partial=None, lse_partial=None):
+    """Dual chunk attention decode as one split-KV pass (see include/pkv.h).
+    kv_chunk defaults to chunk_len; num_splits to the page table's capacity.
+    Returns (out, lse) for one split, else (o_partial, lse_partial)."""
+    lib = load_library()
+    dev = q.device
+    for t, name in ((q, "q"), (q_succ, "q_succ"), (q_inter, "q_inter")):
+        _need(t, name, None, dev, 3)
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError(f"{name} must match q")
+    _need(k_cache, "k_cache", q.dtype, dev, 4)
+    _need(v_cache, "v_cache", q.dtype, dev, 4)
+    pt = _i32(page_table, "page_table", dev)
+    kl = _i32(kv_lens, "kv_lens", dev)
+    if q_scale is not None:
+        _need(q_scale, "q_scale", torch.float32, dev, 1)
+    batch, hq, d = q.shape
+    num_pages, page_size, hkv, _ = k_cache.shape
+    kv_chunk = int(chunk_len if kv_chunk is None else kv_chunk)
+    if num_splits is None:
+        num_splits = max(1, -(-(pt.shape[1] * page_size) // kv_chunk))
+    if num_splits == 1:
+        out = torch.empty_like(q) if out is None else out
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev) if lse is None else lse
+    else:
+        if o_partial is None:
+            o_partial = torch.empty((num_splits, batch, hq, d), dtype=torch.float32, device=dev)
+        if lse_partial is None:
+            lse_partial = torch.empty((num_splits, batch, hq), dtype=torch.float32, device=dev)
+    st = lib.paged_attn_dca_decode(
+        _ptr(q), _ptr(q_succ), _ptr(q_inter), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache),
+        num_pages, _ptr(pt), pt.shape[1], _ptr(kl), batch, hq, hkv, d, page_size,
+        float(softmax_scale), int(chunk_len), _ptr(q_scale), kv_chunk, int(num_splits),
+        _ptr(o_partial), _ptr(lse_partial), _ptr(out) if num_splits == 1 else None,
+        _ptr(lse) if num_splits == 1 else None, _stream(dev))
+    _check("paged_attn_dca_decode", st)
+    return (out, lse) if num_splits == 1 else (o_partial, lse_partial)

@@ -102,6 +102,94 @@ using pkv_host::fail;
     if (!(cond)) return fail(code, __VA_ARGS__); \
   } while (0)
 
+static pkv_status_t decode_impl(const void* q, const void* q_succ, const void* q_inter,
+                                int32_t dca_chunk, const float* q_scale, int32_t dtype,
+                                const void* k_cache, const void* v_cache, int64_t num_pages,
+                                const int32_t* page_table, int32_t pt_stride,
+                                const int32_t* kv_lens, int32_t batch, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                float softmax_scale, int32_t window_left, int32_t attn_chunk,
+                                int32_t kv_chunk, int32_t num_splits, float* o_partial,
+                                float* lse_partial, void* out, float* lse, void* stream) {
+  PKV_REQUIRE(dtype == PKV_F32 || dtype == PKV_BF16, PKV_EUNSUPPORTED,
+              "decode: dtype %d not supported", dtype);
+  PKV_REQUIRE(head_dim == 64 || head_dim == 128, PKV_EUNSUPPORTED,
+              "decode: head_dim %d not supported (64, 128)", head_dim);
+  PKV_REQUIRE(batch >= 0 && num_q_heads >= 1 && num_kv_heads >= 1, PKV_EINVAL,
+              "decode: bad sizes batch %d Hq %d Hkv %d", batch, num_q_heads, num_kv_heads);
+  PKV_REQUIRE(num_q_heads % num_kv_heads == 0, PKV_EINVAL,
+              "decode: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+              num_kv_heads);
+  PKV_REQUIRE(num_q_heads / num_kv_heads <= 16, PKV_EUNSUPPORTED,
+              "decode: GQA group %d > 16", num_q_heads / num_kv_heads);
+  PKV_REQUIRE(page_size >= 1 && pt_stride >= 1 && num_pages >= 1, PKV_EINVAL,
+              "decode: page_size %d pt_stride %d num_pages %lld", page_size, pt_stride,
+              (long long)num_pages);
+  PKV_REQUIRE(window_left >= -1 && attn_chunk >= 0 && !(window_left >= 0 && attn_chunk > 0),
+              PKV_EINVAL, "decode: window_left %d / attn_chunk %d (at most one of them)",
+              window_left, attn_chunk);
+  PKV_REQUIRE(kv_chunk >= 0, PKV_EINVAL, "decode: kv_chunk %d < 0", kv_chunk);
+  PKV_REQUIRE(kv_chunk % page_size == 0, PKV_EINVAL,
+              "decode: kv_chunk %d is not a multiple of page_size %d", kv_chunk, page_size);
+  PKV_REQUIRE(kv_chunk % 32 == 0, PKV_EINVAL, "decode: kv_chunk %d is not a multiple of 32",
+              kv_chunk);
+  PKV_REQUIRE(num_splits >= 1, PKV_EINVAL, "decode: num_splits %d < 1", num_splits);
+  PKV_REQUIRE(kv_chunk > 0 || num_splits == 1, PKV_EINVAL,
+              "decode: kv_chunk 0 (one split) needs num_splits 1, got %d", num_splits);
+  PKV_REQUIRE(dca_chunk >= 0, PKV_EINVAL, "decode: chunk_len %d < 0", dca_chunk);
+  if (dca_chunk > 0) {
+    PKV_REQUIRE(kv_chunk > 0 && dca_chunk % kv_chunk == 0, PKV_EINVAL,
+                "decode: chunk_len %d is not a multiple of kv_chunk %d", dca_chunk, kv_chunk);
+    PKV_REQUIRE(window_left < 0 && attn_chunk == 0, PKV_EINVAL,
+                "decode: dual chunk attention takes no window or local chunks");
+  }
+  if (batch == 0) return pkv_host::ok();
+  PKV_REQUIRE(q && k_cache && v_cache && page_table && kv_lens, PKV_EINVAL,
+              "decode: NULL required pointer");
+  PKV_REQUIRE(dca_chunk == 0 || (q_succ && q_inter), PKV_EINVAL,
+              "decode: dual chunk attention needs q_succ and q_inter");
+  if (num_splits == 1) {
+    PKV_REQUIRE(out != nullptr, PKV_EINVAL, "decode: num_splits 1 needs out");
+  } else {
+    PKV_REQUIRE(o_partial && lse_partial, PKV_EINVAL,
+                "decode: num_splits %d needs o_partial and lse_partial", num_splits);
+  }
+  const int64_t grid = static_cast<int64_t>(num_kv_heads) * batch * num_splits;
+  PKV_REQUIRE(grid <= 0x7fffffff, PKV_EUNSUPPORTED, "decode: grid too large");
+  const int64_t cap = static_cast<int64_t>(pt_stride) * page_size;
+  pkv::DecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.pt = page_table;
+  a.pt_stride = pt_stride;
+  a.kv_lens = kv_lens;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.scale_log2 = pkv_host::scale_log2(softmax_scale);
+  // one split: a chunk that covers every representable key position
+  a.chunk = kv_chunk > 0 ? kv_chunk
+                         : static_cast<int32_t>(((cap < 0x40000000LL ? cap : 0x40000000LL) + 31) /
+                                                32 * 32);
+  a.num_splits = num_splits;
+  a.window_left = window_left;
+  a.attn_chunk = attn_chunk;
+  a.q_succ = q_succ;
+  a.q_inter = q_inter;
+  a.dca_chunk = dca_chunk;
+  a.q_scale = q_scale;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  a.out = out;
+  a.lse = lse;
+  return pkv_host::from_hip(
+      pkv_launch::decode_splitkv(a, dtype, head_dim, static_cast<hipStream_t>(stream)),
+      "decode launch");
+}
+
 extern "C" {
 
 const char* pkv_status_string(int status) {
@@ -186,70 +274,26 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
                                        int32_t window_left, int32_t attn_chunk,
                                        int32_t kv_chunk, int32_t num_splits, float* o_partial,
                                        float* lse_partial, void* out, float* lse, void* stream) {
-  PKV_REQUIRE(dtype == PKV_F32 || dtype == PKV_BF16, PKV_EUNSUPPORTED,
-              "decode: dtype %d not supported", dtype);
-  PKV_REQUIRE(head_dim == 64 || head_dim == 128, PKV_EUNSUPPORTED,
-              "decode: head_dim %d not supported (64, 128)", head_dim);
-  PKV_REQUIRE(batch >= 0 && num_q_heads >= 1 && num_kv_heads >= 1, PKV_EINVAL,
-              "decode: bad sizes batch %d Hq %d Hkv %d", batch, num_q_heads, num_kv_heads);
-  PKV_REQUIRE(num_q_heads % num_kv_heads == 0, PKV_EINVAL,
-              "decode: num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
-              num_kv_heads);
-  PKV_REQUIRE(num_q_heads / num_kv_heads <= 16, PKV_EUNSUPPORTED,
-              "decode: GQA group %d > 16", num_q_heads / num_kv_heads);
-  PKV_REQUIRE(page_size >= 1 && pt_stride >= 1 && num_pages >= 1, PKV_EINVAL,
-              "decode: page_size %d pt_stride %d num_pages %lld", page_size, pt_stride,
-              (long long)num_pages);
-  PKV_REQUIRE(window_left >= -1 && attn_chunk >= 0 && !(window_left >= 0 && attn_chunk > 0),
-              PKV_EINVAL, "decode: window_left %d / attn_chunk %d (at most one of them)",
-              window_left, attn_chunk);
-  PKV_REQUIRE(kv_chunk >= 0, PKV_EINVAL, "decode: kv_chunk %d < 0", kv_chunk);
-  PKV_REQUIRE(kv_chunk % page_size == 0, PKV_EINVAL,
-              "decode: kv_chunk %d is not a multiple of page_size %d", kv_chunk, page_size);
-  PKV_REQUIRE(kv_chunk % 32 == 0, PKV_EINVAL, "decode: kv_chunk %d is not a multiple of 32",
-              kv_chunk);
-  PKV_REQUIRE(num_splits >= 1, PKV_EINVAL, "decode: num_splits %d < 1", num_splits);
-  PKV_REQUIRE(kv_chunk > 0 || num_splits == 1, PKV_EINVAL,
-              "decode: kv_chunk 0 (one split) needs num_splits 1, got %d", num_splits);
-  if (batch == 0) return pkv_host::ok();
-  PKV_REQUIRE(q && k_cache && v_cache && page_table && kv_lens, PKV_EINVAL,
-              "decode: NULL required pointer");
-  if (num_splits == 1) {
-    PKV_REQUIRE(out != nullptr, PKV_EINVAL, "decode: num_splits 1 needs out");
-  } else {
-    PKV_REQUIRE(o_partial && lse_partial, PKV_EINVAL,
-                "decode: num_splits %d needs o_partial and lse_partial", num_splits);
-  }
-  const int64_t grid = static_cast<int64_t>(num_kv_heads) * batch * num_splits;
-  PKV_REQUIRE(grid <= 0x7fffffff, PKV_EUNSUPPORTED, "decode: grid too large");
-  const int64_t cap = static_cast<int64_t>(pt_stride) * page_size;
-  pkv::DecodeArgs a;
-  a.q = q;
-  a.k = k_cache;
-  a.v = v_cache;
-  a.pt = page_table;
-  a.pt_stride = pt_stride;
-  a.kv_lens = kv_lens;
-  a.batch = batch;
-  a.hq = num_q_heads;
-  a.hkv = num_kv_heads;
-  a.page_size = page_size;
-  a.num_pages = num_pages;
-  a.scale_log2 = pkv_host::scale_log2(softmax_scale);
-  // one split: a chunk that covers every representable key position
-  a.chunk = kv_chunk > 0 ? kv_chunk
-                         : static_cast<int32_t>(((cap < 0x40000000LL ? cap : 0x40000000LL) + 31) /
-                                                32 * 32);
-  a.num_splits = num_splits;
-  a.window_left = window_left;
-  a.attn_chunk = attn_chunk;
-  a.o_part = o_partial;
-  a.lse_part = lse_partial;
-  a.out = out;
-  a.lse = lse;
-  return pkv_host::from_hip(
-      pkv_launch::decode_splitkv(a, dtype, head_dim, static_cast<hipStream_t>(stream)),
-      "decode launch");
+  return decode_impl(q, nullptr, nullptr, 0, nullptr, dtype, k_cache, v_cache, num_pages,
+                     page_table, pt_stride, kv_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                     page_size, softmax_scale, window_left, attn_chunk, kv_chunk, num_splits,
+                     o_partial, lse_partial, out, lse, stream);
+}
+
+pkv_status_t paged_attn_dca_decode(const void* q, const void* q_succ, const void* q_inter,
+                                   int32_t dtype, const void* k_cache, const void* v_cache,
+                                   int64_t num_pages, const int32_t* page_table,
+                                   int32_t pt_stride, const int32_t* kv_lens, int32_t batch,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t page_size, float softmax_scale, int32_t chunk_len,
+                                   const float* q_scale, int32_t kv_chunk, int32_t num_splits,
+                                   float* o_partial, float* lse_partial, void* out, float* lse,
+                                   void* stream) {
+  PKV_REQUIRE(chunk_len >= 1, PKV_EINVAL, "paged_attn_dca_decode: chunk_len %d < 1", chunk_len);
+  return decode_impl(q, q_succ, q_inter, chunk_len, q_scale, dtype, k_cache, v_cache, num_pages,
+                     page_table, pt_stride, kv_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                     page_size, softmax_scale, -1, 0, kv_chunk, num_splits, o_partial,
+                     lse_partial, out, lse, stream);
 }
 
 size_t paged_attn_varlen_prefill_workspace_size(int32_t batch, int32_t total_q,
@@ -491,6 +535,42 @@ pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num
   a.lse = lse;
   return pkv_host::from_hip(pkv_launch::sparse_topk(a, static_cast<hipStream_t>(stream)),
                             "sparse_topk_decode launch");
+}
+
+pkv_status_t build_dca_decode_tables(const int32_t* block_tables, int32_t bt_stride,
+                                     const int32_t* seq_lens, int32_t batch, int32_t chunk_len,
+                                     int32_t page_size, int32_t original_max_position_embeddings,
+                                     int32_t* table_intra, int32_t* lens_intra,
+                                     int32_t* table_succ, int32_t* lens_succ,
+                                     int32_t* lens_inter, float* scaling_factor, void* stream) {
+  PKV_REQUIRE(batch >= 0 && bt_stride >= 1 && page_size >= 1 && chunk_len >= 1, PKV_EINVAL,
+              "build_dca_decode_tables: bad sizes");
+  PKV_REQUIRE(chunk_len % page_size == 0, PKV_EINVAL,
+              "build_dca_decode_tables: chunk_len %d is not a multiple of page_size %d",
+              chunk_len, page_size);
+  PKV_REQUIRE(original_max_position_embeddings >= 0, PKV_EINVAL,
+              "build_dca_decode_tables: original_max_position_embeddings %d < 0",
+              original_max_position_embeddings);
+  if (batch == 0) return pkv_host::ok();
+  PKV_REQUIRE(block_tables && seq_lens && table_intra && lens_intra && lens_succ && lens_inter,
+              PKV_EINVAL, "build_dca_decode_tables: NULL required pointer");
+  pkv::DcaTableArgs a;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.chunk_len = chunk_len;
+  a.page_size = page_size;
+  a.width = chunk_len / page_size;
+  a.original_max_position_embeddings = original_max_position_embeddings;
+  a.table_intra = table_intra;
+  a.table_succ = table_succ;
+  a.lens_intra = lens_intra;
+  a.lens_succ = lens_succ;
+  a.lens_inter = lens_inter;
+  a.scaling_factor = scaling_factor;
+  return pkv_host::from_hip(pkv_launch::dca_tables(a, static_cast<hipStream_t>(stream)),
+                            "build_dca_decode_tables launch");
 }
 
 pkv_status_t build_cascade_expand_table(const uint8_t* custom_mask, int64_t mask_len,

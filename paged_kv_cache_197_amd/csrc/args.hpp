@@ -36,7 +36,23 @@ struct DecodeArgs {
   float* lse;         // [B, Hq] or nullptr
   int32_t window_left;   // >= 0: sliding window (W, 0); else none
   int32_t attn_chunk;    // > 0: chunked local attention; else none
+  // dual chunk attention: with dca_chunk > 0 the keys of the query's own
+  // chunk ((L - 1) / dca_chunk) are scored with q, the chunk before it with
+  // q_succ, earlier ones with q_inter (a split lies inside one chunk)
+  const void* q_succ;
+  const void* q_inter;
+  int32_t dca_chunk;
+  const float* q_scale;   // [B] factors applied to the queries (rounded back), or null
 };
+
+// Query a split scores its keys with: q, or under dual chunk attention the
+// query of the stage its chunk belongs to. L >= 1 (the split is not empty).
+__device__ inline const void* split_query(const DecodeArgs& a, int split_start, int L) {
+  if (a.dca_chunk <= 0) return a.q;
+  const int c = (L - 1) / a.dca_chunk;
+  const int ci = split_start / a.dca_chunk;
+  return ci >= c ? a.q : (ci == c - 1 ? a.q_succ : a.q_inter);
+}
 
 // First key a query at absolute position pos may see: pos - W for a sliding
 // window (W, 0) (inclusive on both sides), the start of pos's aligned block
@@ -86,6 +102,21 @@ struct SparseArgs {
   size_t workspace_bytes;
   void* out;
   float* lse;
+};
+
+// Metadata of dual chunk attention decode (per request).
+struct DcaTableArgs {
+  const int32_t* block_tables;   // [batch, bt_stride] page ids
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  int32_t batch, chunk_len, page_size, width;   // width = chunk_len / page_size
+  int32_t original_max_position_embeddings;
+  int32_t* table_intra;   // [batch, width]
+  int32_t* table_succ;    // [batch, width] or null
+  int32_t* lens_intra;
+  int32_t* lens_succ;
+  int32_t* lens_inter;
+  float* scaling_factor;  // [batch] or null
 };
 
 // Expand-pass key lists of cascade attention (one row per draft token).

@@ -292,11 +292,26 @@ struct DecodeKernel {
     // Q^T operand: head c (zero for padding columns), dims 32j + 8g + [0, 8)
     Chunk<KDW> qop[NK];
     {
-      const char* qrow = static_cast<const char*>(a.q) +
+      const char* qrow = static_cast<const char*>(split_query(a, start0, L)) +
                          (static_cast<int64_t>(b) * a.hq + h0 + min(c, G - 1)) * D * EB;
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
         qop[j] = load_chunk<KDW>(qrow + (32 * j + 8 * g) * EB);
+      }
+      if (a.q_scale != nullptr) {   // q * factor, rounded back to the element type
+        const float f = a.q_scale[b];
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+          if constexpr (IS_BF16) {
+#pragma unroll
+            for (int w = 0; w < KDW; ++w)
+              qop[j].w[w] = pack_bf16x2(bf16lo(qop[j].w[w]) * f, bf16hi(qop[j].w[w]) * f);
+          } else {
+#pragma unroll
+            for (int w = 0; w < KDW; ++w)
+              qop[j].w[w] = __float_as_uint(__uint_as_float(qop[j].w[w]) * f);
+          }
+        }
       }
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
@@ -512,7 +527,7 @@ struct DecodeGroupKernel {
     }
   }
 
-  template <bool WINDOW>
+  template <bool EXT>
   static __device__ __forceinline__ void compute(const char* my, int c, int g, int valid,
                                                  int first, float scale_log2,
                                                  const u32x4 (&qop)[8],
@@ -526,7 +541,7 @@ struct DecodeGroupKernel {
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      x[i] = (4 * g + i < valid && (!WINDOW || 4 * g + i >= first)) ? s[i] * scale_log2
+      x[i] = (4 * g + i < valid && (!EXT || 4 * g + i >= first)) ? s[i] * scale_log2
                                                                      : neg_inf();
     float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mt = max_over_groups16(mt);
@@ -569,7 +584,9 @@ struct DecodeGroupKernel {
     }
   }
 
-  template <bool UNIFORM, bool WINDOW>
+  // EXT: the variant with a lower key bound (sliding window, local chunks)
+  // and the per-split query choice and scaling of dual chunk attention.
+  template <bool UNIFORM, bool EXT>
   static __device__ void run(const DecodeArgs& a) {
     extern __shared__ __align__(16) char smem[];
     __shared__ float sm_m[4][16];
@@ -594,8 +611,8 @@ struct DecodeGroupKernel {
     const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(start0) + a.chunk, L));
     // first visible key under a sliding window / local chunks; tiles start on
     // a multiple of TT (splits do), keys below lo are masked
-    const int lo = (WINDOW && L > 0) ? key_lower_bound(L - 1, a.window_left, a.attn_chunk) : 0;
-    const int start = WINDOW ? max(start0, lo / TT * TT) : start0;
+    const int lo = (EXT && L > 0) ? key_lower_bound(L - 1, a.window_left, a.attn_chunk) : 0;
+    const int start = EXT ? max(start0, lo / TT * TT) : start0;
     const bool single = (a.num_splits == 1);
 
     if (max(start0, lo) >= end) {   // empty split: (0, -inf)
@@ -622,9 +639,20 @@ struct DecodeGroupKernel {
     u32x4 qop[8];
     {
       const int head = h0 + min(c, ncol - 1);
-      const char* qrow = static_cast<const char*>(a.q) + (static_cast<int64_t>(b) * a.hq + head) * D * 2;
+      const void* qsrc = EXT ? split_query(a, start0, L) : a.q;
+      const char* qrow = static_cast<const char*>(qsrc) + (static_cast<int64_t>(b) * a.hq + head) * D * 2;
 #pragma unroll
       for (int j = 0; j < 8; ++j) qop[j] = *reinterpret_cast<const u32x4*>(qrow + ((32 * j + 8 * g) % D) * 2);
+      if (EXT && a.q_scale != nullptr) {   // q * factor, rounded back to bf16
+        const float f = a.q_scale[b];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          qop[j].x = pack_bf16x2(bf16lo(qop[j].x) * f, bf16hi(qop[j].x) * f);
+          qop[j].y = pack_bf16x2(bf16lo(qop[j].y) * f, bf16hi(qop[j].y) * f);
+          qop[j].z = pack_bf16x2(bf16lo(qop[j].z) * f, bf16hi(qop[j].z) * f);
+          qop[j].w = pack_bf16x2(bf16lo(qop[j].w) * f, bf16hi(qop[j].w) * f);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const bool mine = (c < ncol) && ((32 * j + 8 * g) / D == kk);
@@ -666,7 +694,7 @@ struct DecodeGroupKernel {
         if (more)
           load<UNIFORM>(a, raw_n, start + TT * (tile + 4), end, lane, row_bytes, col, st);
         __builtin_amdgcn_sched_barrier(0);   // the next tile's loads go out before the MFMAs
-        compute<WINDOW>(my, c, g, end - (start + TT * tile), lo - (start + TT * tile),
+        compute<EXT>(my, c, g, end - (start + TT * tile), lo - (start + TT * tile),
                         a.scale_log2, qop, acc, m_run, l_run);
         if (!more) break;
         tile += 4;
@@ -748,9 +776,9 @@ struct DecodeGroupKernel {
   }
 };
 
-template <int D, bool UNIFORM, bool WINDOW>
+template <int D, bool UNIFORM, bool EXT>
 __global__ __launch_bounds__(256, 2) void decode_group_kernel(DecodeArgs a) {
-  DecodeGroupKernel<D>::template run<UNIFORM, WINDOW>(a);
+  DecodeGroupKernel<D>::template run<UNIFORM, EXT>(a);
 }
 
 // bf16 tiles fit two workgroups per CU (<= 256 VGPRs); fp32 tiles are twice
@@ -794,8 +822,10 @@ static hipError_t launch_decode_group(const pkv::DecodeArgs& a, hipStream_t stre
   const dim3 grid(static_cast<unsigned>(a.hkv / HPW) * a.batch * a.num_splits);
   constexpr unsigned lds = pkv::DecodeGroupKernel<D>::LDS_BYTES;
   // whole 16-token tiles on one page: page_size % 16 == 0 (splits start on pages)
-  // (a sliding window or local chunks take the variant with the lower key mask)
-  const bool window = a.window_left >= 0 || a.attn_chunk > 0;
+  // (a sliding window, local chunks or dual chunk attention take the variant
+  // with the lower key mask and the per-split query choice)
+  const bool window = a.window_left >= 0 || a.attn_chunk > 0 || a.dca_chunk > 0 ||
+                      a.q_scale != nullptr;
   if (a.page_size % 16 == 0) {
     if (window)
       hipLaunchKernelGGL((pkv::decode_group_kernel<D, true, true>), grid, dim3(256), lds, stream, a);

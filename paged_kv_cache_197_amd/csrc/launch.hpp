@@ -12,6 +12,7 @@ struct PrefillArgs;
 struct SparseArgs;
 struct CascadeExpandArgs;
 struct ExpandMergeArgs;
+struct DcaTableArgs;
 }  // namespace pkv
 
 namespace pkv_launch {
@@ -27,4 +28,5 @@ size_t sparse_workspace_bytes(int batch, int topk, int num_q_heads, int head_dim
 hipError_t sparse_topk(const pkv::SparseArgs& a, hipStream_t stream);
 hipError_t cascade_expand(const pkv::CascadeExpandArgs& a, hipStream_t stream);
 hipError_t expand_merge(const pkv::ExpandMergeArgs& a, int head_dim, hipStream_t stream);
+hipError_t dca_tables(const pkv::DcaTableArgs& a, hipStream_t stream);
 }  // namespace pkv_launch

@@ -21,7 +21,8 @@ def test_header_declares_the_entry_points():
                "merge_state", "sparse_topk_decode", "paged_attn_varlen_prefill_workspace_size",
                "sparse_topk_decode_workspace_size", "paged_kv_append",
                "paged_attn_varlen_prefill_append", "build_cascade_expand_table",
-               "paged_attn_expand_merge", "paged_attn_cascade"]:
+               "paged_attn_expand_merge", "paged_attn_cascade", "build_dca_decode_tables",
+               "paged_attn_dca_decode"]:
         assert fn in names
 
 
@@ -202,3 +203,23 @@ def test_cascade_argument_errors():
     bad = list(base)
     bad[15] = 96
     assert cz(*bad, fake, 8, fake, None, 0, fake, fake, None) == EUNSUP
+
+
+def test_dca_argument_errors():
+    lib = pkv.load_library()
+    fake = ctypes.c_void_p(256)
+    tb = lib.build_dca_decode_tables
+    # bt stride sl B C P omp t_intra l_intra t_succ l_succ l_inter sf stream
+    assert tb(None, 8, None, 0, 64, 16, 0, None, None, None, None, None, None, None) == 0
+    assert tb(fake, 8, fake, 2, 60, 16, 0, fake, fake, None, fake, fake, None, None) == EINVAL
+    assert tb(fake, 8, fake, 2, 64, 16, -1, fake, fake, None, fake, fake, None, None) == EINVAL
+    assert tb(fake, 8, fake, 2, 64, 16, 0, None, fake, None, fake, fake, None, None) == EINVAL
+    dd = lib.paged_attn_dca_decode
+    # q qs qi dtype k v pages pt stride kl B Hq Hkv D P scale C qscale kvchunk S op lp out lse st
+    base = [fake, fake, fake, 1, fake, fake, 64, fake, 8, fake, 2, 32, 8, 128, 16, 0.1]
+    assert dd(*base, 96, None, 64, 4, fake, fake, None, None, None) == EINVAL    # 96 % 64
+    assert dd(*base, 0, None, 64, 4, fake, fake, None, None, None) == EINVAL     # chunk_len < 1
+    nul = list(base)
+    nul[1] = None
+    assert dd(*nul, 64, None, 64, 4, fake, fake, None, None, None) == EINVAL     # q_succ NULL
+    assert b"q_succ" in lib.pkv_last_error()

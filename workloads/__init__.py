@@ -32,7 +32,7 @@ import torch
 __all__ = [
     "DecodeCase", "PrefillCase", "SwaCase", "SparseCase", "CascadeCase",
     "make_decode_case", "make_prefill_case", "make_swa_case", "make_sparse_case",
-    "make_cascade_case", "cascade_verify",
+    "make_cascade_case", "cascade_verify", "DcaCase", "make_dca_case", "dca_decode",
     "config1", "config2", "config3", "config4", "config5",
     "small_config3", "small_config4", "small_config5",
 ]
@@ -118,6 +118,17 @@ class CascadeCase:
     page_size: int
     scale: float
     table_width: int                # pages per row of the committed-token page table
+    name: str = ""
+
+
+@dataclass
+class DcaCase:
+    base: "DecodeCase"              # q (the intra query), caches, tables, lengths
+    q_succ: torch.Tensor            # [B, Hq, D] query of the previous chunk's keys
+    q_inter: torch.Tensor           # [B, Hq, D] query of all earlier keys
+    chunk_size: int
+    local_size: int
+    original_max_position_embeddings: int
     name: str = ""
 
 
@@ -418,6 +429,38 @@ def cascade_verify(value_device="cpu"):
     return make_cascade_case(6, prefix_lens=(64, 1024, 16384), num_draft=8, num_q_heads=32,
                              num_kv_heads=8, head_dim=128, page_size=64, num_pages=20000,
                              value_device=value_device, name="cascade_verify")
+
+
+def make_dca_case(seed, *, seq_lens, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                  chunk_size, local_size, original_max_position_embeddings=0,
+                  dtype=torch.bfloat16, kv_chunk=0, ctx=None, value_device="cpu",
+                  name="") -> DcaCase:
+    """Dual chunk attention decode: a decode case (its q is the intra query)
+    plus the succ and inter queries, N(0, 1), drawn after it from a generator
+    seeded with seed + 1 (on ``value_device``). The three queries stand for
+    the model's three rotary projections of one token."""
+    base = make_decode_case(seed, seq_lens=seq_lens, num_q_heads=num_q_heads,
+                            num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=page_size,
+                            num_pages=num_pages, dtype=dtype, kv_chunk=kv_chunk, ctx=ctx,
+                            value_device=value_device, name=name)
+    gv, dev = _value_generator(seed + 1, value_device)
+    shape = tuple(base.q.shape)
+    q_succ = _normal(gv, dev, shape, dtype)
+    q_inter = _normal(gv, dev, shape, dtype)
+    return DcaCase(base=base, q_succ=q_succ, q_inter=q_inter, chunk_size=chunk_size,
+                   local_size=local_size,
+                   original_max_position_embeddings=original_max_position_embeddings, name=name)
+
+
+def dca_decode(value_device="cpu"):
+    """Dual chunk attention decode, bf16: B 32, L ~ U[4096, 65536], 32 q / 8 kv
+    heads, D 128, page 64 over a 40000-page pool; chunk_size 8192, local_size
+    1024 (chunks of 7168 keys, one split each); queries scaled against
+    original_max_position_embeddings 32768."""
+    return make_dca_case(7, seq_lens=(32, 4096, 65536), num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, page_size=64, num_pages=40000, chunk_size=8192,
+                         local_size=1024, original_max_position_embeddings=32768,
+                         kv_chunk=7168, ctx=65536, value_device=value_device, name="dca_decode")
 
 
 def config1(value_device="cpu"):
