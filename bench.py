@@ -34,7 +34,7 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--only", choices=["all", "decode", "decode_window", "prefill",
                                       "prefill_long", "prefill_window", "prefill_append", "swa",
-                                      "sparse", "cascade", "copy"],
+                                      "sparse", "cascade", "dca", "copy"],
                    default="all", help="restrict to one workload (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -361,6 +361,42 @@ def run_cascade(torch, pkv, workloads, args):
     flops = 4 * d * hq * (n * sum_l + vis)
     return dict(ms=ms, kernel_ms=kern_ms, build_ms=build_t.kernel_ms(), bytes=nbytes, flops=flops,
                 sum_l=sum_l, batch=B, n=n, ws=ws_bytes)
+
+
+def run_dca(torch, pkv, workloads, args):
+    """Dual chunk attention decode: metadata build, the one-pass split-KV decode
+    with per-chunk queries (one split per chunk), merge_state."""
+    dev = torch.device("cuda:0")
+    c = workloads.dca_decode(value_device=dev)
+    b = c.base
+    r2t, rpi, sl = (b.req_to_token.to(dev), b.req_pool_indices.to(dev), b.seq_lens.to(dev))
+    B, hq, d = b.q.shape
+    _, P, hkv, _ = b.k_cache.shape
+    C = c.chunk_size - c.local_size
+    S = -(-int(b.seq_lens.max()) // C)
+    pt = torch.empty((B, b.table_width), dtype=torch.int32, device=dev)
+    kl = torch.empty((B,), dtype=torch.int32, device=dev)
+    op = torch.empty((S, B, hq, d), dtype=torch.float32, device=dev)
+    lp = torch.empty((S, B, hq), dtype=torch.float32, device=dev)
+    out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+
+    def step(timer):
+        pkv.build_page_table(r2t, rpi, sl, P, b.table_width, page_table=pt, kv_lens=kl,
+                             with_cu_seqlens=False)
+        meta = pkv.build_dca_decode_tables(pt, kl, C, P, c.original_max_position_embeddings)
+        e0 = timer.mark() if timer else None
+        pkv.paged_attn_dca_decode(b.q, c.q_succ, c.q_inter, b.k_cache, b.v_cache, pt, kl,
+                                  b.scale, C, kv_chunk=C, num_splits=S,
+                                  q_scale=meta["scaling_factor"], o_partial=op, lse_partial=lp)
+        if timer:
+            timer.pairs.append((e0, timer.mark()))
+        pkv.merge_state(op, lp, out=out, lse_out=lse)
+
+    ms, kern_ms = timed_loop(torch, step, args.steps, args.warmup)
+    nbytes, sum_l = decode_bytes(b.seq_lens.long(), B, hq, hkv, d, P)
+    nbytes += 2 * B * hq * d * 2                   # the succ and inter queries
+    return dict(ms=ms, kernel_ms=kern_ms, bytes=nbytes, sum_l=sum_l, splits=S)
 
 
 def run_sparse(torch, pkv, workloads, args):
@@ -748,6 +784,24 @@ def main(argv=None):
                 "sum_committed_len": r["sum_l"], "prefill_workspace_bytes": r["ws"]}
         except Exception as e:
             extra["cascade_verify"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "dca"):
+        try:
+            r = run_dca(torch, pkv, workloads, args)
+            extra["dca_decode"] = {
+                "workload": "dual chunk attention decode: B=32, L~U[4096,65536], 32 q / 8 kv "
+                            "heads, D=128, page 64, chunk_size 8192 / local 1024 (7168-key "
+                            "chunks, one split each), scaled queries; tables + decode + merge",
+                "ms_per_step": round(r["ms"], 4), "decode_kernel_ms": round(r["kernel_ms"], 4),
+                "kernel_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
+                "kernel_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4),
+                "step_GB/s": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 2),
+                "sum_kv_len": r["sum_l"], "num_splits": r["splits"],
+                "algorithmic_bytes": r["bytes"]}
+        except Exception as e:
+            extra["dca_decode"] = {"error": repr(e)}
         torch.cuda.empty_cache()
 
     if args.only in ("all", "sparse"):
