@@ -87,8 +87,10 @@ static PrefillPlan prefill_plan(int64_t batch, int64_t total_q, int64_t max_seql
   }
   const int64_t n_hb = (hq / hkv + 3) / 4;
   p.counter_bytes = round_up256(static_cast<size_t>(p.qtile_slots * hkv * n_hb) * 4);
-  p.lse_bytes = round_up256(static_cast<size_t>(p.max_splits) * total_q * hq * 4);
-  p.o_bytes = static_cast<size_t>(p.max_splits) * total_q * hq * head_dim * 4;
+  // one block of 32 rows per (split, q-tile slot, head)
+  const size_t blocks = static_cast<size_t>(p.max_splits) * p.qtile_slots * hq;
+  p.lse_bytes = round_up256(blocks * 32 * 4);
+  p.o_bytes = blocks * 32 * head_dim * 4;
   p.bytes = p.counter_bytes + p.lse_bytes + p.o_bytes;
   return p;
 }

@@ -147,29 +147,42 @@ __global__ __launch_bounds__(256) void expand_merge_kernel(ExpandMergeArgs a) {
   const uint16_t* kb = static_cast<const uint16_t*>(a.k);
   const uint16_t* vb = static_cast<const uint16_t*>(a.v);
   const int32_t* row_keys = a.table + static_cast<int64_t>(r) * a.stride;
-  for (int t = 0; t < cnt; ++t) {
-    const int64_t slot = clamp_index(row_keys[t], a.num_slots);
-    const int64_t off = (slot * a.hkv + kvh) * D + lane * DPL;
-    float kf[DPL], vf[DPL];
+  // keys in batches of KB: every batch's K and V rows are requested before
+  // the first score, so the row reads overlap instead of forming a chain
+  constexpr int KB = 8;
+  for (int t0 = 0; t0 < cnt; t0 += KB) {
+    float kf[KB][DPL], vf[KB][DPL];
 #pragma unroll
-    for (int d = 0; d < DPL; ++d) {
-      kf[d] = bf16_to_f32(kb[off + d]);
-      vf[d] = bf16_to_f32(vb[off + d]);
+    for (int u = 0; u < KB; ++u) {
+      const int t = min(t0 + u, cnt - 1);
+      const int64_t slot = clamp_index(row_keys[t], a.num_slots);
+      const int64_t off = (slot * a.hkv + kvh) * D + lane * DPL;
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) {
+        kf[u][d] = bf16_to_f32(kb[off + d]);
+        vf[u][d] = bf16_to_f32(vb[off + d]);
+      }
     }
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if (g < G) {
-        float part = 0.f;
+    for (int u = 0; u < KB; ++u) {
+      if (t0 + u < cnt) {
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) part = __builtin_fmaf(qf[g][d], kf[d], part);
-        const float s = wave_sum(part) * a.scale_log2;
-        const float m_new = fmaxf(m[g], s);
-        const float alpha = fast_exp2(m[g] - m_new);   // 0 while m is -inf
-        const float p = fast_exp2(s - m_new);
-        l[g] = __builtin_fmaf(l[g], alpha, p);
+        for (int g = 0; g < GMAX; ++g) {
+          if (g < G) {
+            float part = 0.f;
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[g][d] = __builtin_fmaf(acc[g][d], alpha, p * vf[d]);
-        m[g] = m_new;
+            for (int d = 0; d < DPL; ++d) part = __builtin_fmaf(qf[g][d], kf[u][d], part);
+            const float sc = wave_sum(part) * a.scale_log2;
+            const float m_new = fmaxf(m[g], sc);
+            const float alpha = fast_exp2(m[g] - m_new);   // 0 while m is -inf
+            const float p = fast_exp2(sc - m_new);
+            l[g] = __builtin_fmaf(l[g], alpha, p);
+#pragma unroll
+            for (int d = 0; d < DPL; ++d)
+              acc[g][d] = __builtin_fmaf(acc[g][d], alpha, p * vf[u][d]);
+            m[g] = m_new;
+          }
+        }
       }
     }
   }

@@ -556,26 +556,29 @@ struct PrefillKernel {
         continue;
       }
 
-      // partial of this split: o [split][row][head][D], lse [split][row][head],
-      // stored at device scope (see coherent_rsrc); a wave's rows of one head
-      // are a uniform base plus per-lane offsets
-      const int64_t part = static_cast<int64_t>(a.total_q) * a.hq;
-      const int64_t tile_row0 = static_cast<int64_t>(q0 + j0) * a.hq + head;
-      const uint32_t o_bytes = static_cast<uint32_t>(QT * a.hq * D * 4);
-      const uint32_t l_bytes = static_cast<uint32_t>(QT * a.hq * 4);
-      const uint32_t o_lane = static_cast<uint32_t>(q * a.hq * D * 4);
-      const uint32_t l_lane = static_cast<uint32_t>(q * a.hq * 4);
-      if (grp == 0 && head_ok && row_ok) {
-        const auto ro = coherent_rsrc(a.ws_o + (split * part + tile_row0) * D, o_bytes);
+      // partial of this split, one block per (split, q-tile slot, head): the
+      // wave's 32 rows x D floats as 16-byte pieces p = 2 (4n + a4) + h, each
+      // piece's 32 rows consecutive, so every store (and the merge's loads)
+      // covers 1 KB of contiguous memory; the LSEs of the 32 rows follow
+      // each other. Stored at device scope (see coherent_rsrc).
+      const uint32_t o_bytes = static_cast<uint32_t>(QT * D * 4);
+      const uint32_t l_bytes = static_cast<uint32_t>(QT * 4);
+      const uint32_t o_lane = static_cast<uint32_t>((h * QT + q) * 16);
+      const uint32_t l_lane = static_cast<uint32_t>(q * 4);
+      auto block_of = [&](int sp) {
+        return (static_cast<int64_t>(sp) * a.qtile_slots + slot) * a.hq + head;
+      };
+      if (grp == 0 && head_ok) {
+        const int64_t blk = block_of(split);
+        const auto ro = coherent_rsrc(a.ws_o + blk * QT * D, o_bytes);
 #pragma unroll
         for (int n = 0; n < NB; ++n)
 #pragma unroll
           for (int a4 = 0; a4 < 4; ++a4)
-            store_coherent(ro, o_lane + out_dim(h, n, a4) * 4,
+            store_coherent(ro, o_lane + (8 * n + 2 * a4) * QT * 16,
                            f32x4{acc[n][4 * a4] * inv, acc[n][4 * a4 + 1] * inv,
                                  acc[n][4 * a4 + 2] * inv, acc[n][4 * a4 + 3] * inv});
-        if (h == 0) store_coherent(coherent_rsrc(a.ws_lse + split * part + tile_row0, l_bytes),
-                                   l_lane, lse_val);
+        if (h == 0) store_coherent(coherent_rsrc(a.ws_lse + blk * QT, l_bytes), l_lane, lse_val);
       }
       wait_all_vmem();
       __syncthreads();   // every wave's partial has been written through
@@ -590,7 +593,7 @@ struct PrefillKernel {
 #pragma unroll
         for (int s2 = 0; s2 < 16; ++s2)
           ls[s2] = s2 < n_split ? load_coherent1(
-                                      coherent_rsrc(a.ws_lse + s2 * part + tile_row0, l_bytes),
+                                      coherent_rsrc(a.ws_lse + block_of(s2) * QT, l_bytes),
                                       l_lane)
                                 : neg_inf();
         float mx = ls[0];
@@ -606,12 +609,13 @@ struct PrefillKernel {
           for (int s2 = 0; s2 < n_split; ++s2) {
             const float wgt = fast_exp2((ls[s2] - mx) * kLog2e);
             wsum += wgt;
-            const auto ro = coherent_rsrc(a.ws_o + (s2 * part + tile_row0) * D, o_bytes);
+            const auto ro = coherent_rsrc(a.ws_o + block_of(s2) * QT * D, o_bytes);
             f32x4 v[NB][4];   // all loads in flight before the first use
 #pragma unroll
             for (int n = 0; n < NB; ++n)
 #pragma unroll
-              for (int a4 = 0; a4 < 4; ++a4) v[n][a4] = load_coherent4(ro, o_lane + out_dim(h, n, a4) * 4);
+              for (int a4 = 0; a4 < 4; ++a4)
+                v[n][a4] = load_coherent4(ro, o_lane + (8 * n + 2 * a4) * QT * 16);
 #pragma unroll
             for (int n = 0; n < NB; ++n)
 #pragma unroll
