@@ -31,6 +31,8 @@
 // shuffles are needed.
 // LDS rows are D*2 bytes with their 16-byte chunks XOR-swizzled by the row
 // index, so that the K operand reads (16 rows, one chunk) hit distinct banks.
+#include <climits>
+
 #include "args.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -308,7 +310,10 @@ struct PrefillKernel {
     // flat grid: kv head fastest, then split, then q-tile slot. Slots number
     // the q tiles request by request (each request's from its last, longest
     // one); a request with M rows has ceil(M / 32) of them, so
-    // ceil(total_q / 32) + batch slots cover all and few stay empty.
+    // ceil(total_q / 32) + batch slots cover all and few stay empty. Within
+    // each chunk of 64 requests the longer ones (more keys) take the lower
+    // slots: workgroups start in slot order, so the longest chains start
+    // first and the short ones fill in behind them.
     const int kvh = blockIdx.x % a.hkv;
     const int rest = blockIdx.x / a.hkv;
     const int split = rest % a.max_splits;
@@ -323,13 +328,21 @@ struct PrefillKernel {
         const int qe = in ? a.cu_q[bi + 1] : 0;
         const int kl = in ? a.kv_lens[bi] : 0;
         const int nt = in ? max(qe - qs + QT - 1, 0) / QT : 0;
-        int incl = nt;   // inclusive prefix sum over the wave
-#pragma unroll
-        for (int d = 1; d < 64; d *= 2) {
-          const int v = __shfl_up(incl, d);
-          if (lane >= d) incl += v;
+        // place of this request in the chunk: more keys first, ties by index
+        const int nb = min(64, a.batch - c0);   // requests in this chunk (uniform)
+        const int key = in ? kl : INT_MIN;
+        int rank = 0;
+#pragma unroll 4
+        for (int j = 0; j < nb; ++j) {
+          const int kj = __builtin_amdgcn_readlane(key, j);
+          rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
         }
-        const int first = base + incl - nt;   // slot of request bi's last q tile
+        int first = base;   // slot of request bi's last q tile
+#pragma unroll 4
+        for (int j = 0; j < nb; ++j) {
+          const int rj = __builtin_amdgcn_readlane(rank, j);
+          first += rj < rank ? __builtin_amdgcn_readlane(nt, j) : 0;
+        }
         const unsigned long long hit = __ballot(nt > 0 && slot >= first && slot < first + nt);
         if (hit) {
           const int l = __builtin_ctzll(hit);
@@ -340,7 +353,10 @@ struct PrefillKernel {
           Lraw = __shfl(kl, l);
           break;
         }
-        base += __shfl(incl, 63);
+        int chunk_tiles = nt;   // q tiles of the whole chunk
+#pragma unroll
+        for (int d = 1; d < 64; d *= 2) chunk_tiles += __shfl_xor(chunk_tiles, d);
+        base += chunk_tiles;
       }
     }
     // (wave-uniform; made explicit so that everything derived stays scalar)
