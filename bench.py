@@ -360,7 +360,7 @@ def run_cascade(torch, pkv, workloads, args):
     nbytes = (sum_l + B * n) * row_bytes + 2 * B * n * hq * d * 2 + B * n * hq * 4
     flops = 4 * d * hq * (n * sum_l + vis)
     return dict(ms=ms, kernel_ms=kern_ms, build_ms=build_t.kernel_ms(), bytes=nbytes, flops=flops,
-                sum_l=sum_l, batch=B, n=n, ws=ws_bytes)
+                sum_l=sum_l, batch=B, n=n, ws=ws_bytes, case=c)
 
 
 def run_dca(torch, pkv, workloads, args):
@@ -396,7 +396,7 @@ def run_dca(torch, pkv, workloads, args):
     ms, kern_ms = timed_loop(torch, step, args.steps, args.warmup)
     nbytes, sum_l = decode_bytes(b.seq_lens.long(), B, hq, hkv, d, P)
     nbytes += 2 * B * hq * d * 2                   # the succ and inter queries
-    return dict(ms=ms, kernel_ms=kern_ms, bytes=nbytes, sum_l=sum_l, splits=S)
+    return dict(ms=ms, kernel_ms=kern_ms, bytes=nbytes, sum_l=sum_l, splits=S, case=c, pt=pt, kl=kl)
 
 
 def run_sparse(torch, pkv, workloads, args):
@@ -554,6 +554,76 @@ def cpu_oracle_swa(torch, r, budget_s):
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
             "kind": "oracle", "sample": f"config4 requests 0..{n - 1} ({n} of {len(kl)}), float64 "
                                         f"numpy; {spent:.1f} s"}
+
+
+def cpu_oracle_cascade(torch, r, budget_s):
+    """The oracle's plain tree attention over the draft-tree workload's requests
+    in order (each request's committed and draft tokens gathered first)."""
+    import numpy as np
+    import oracle
+    c = r["case"]
+    n = c.num_draft
+    sl = c.seq_lens.cpu().numpy().astype(np.int64)
+    r2t, rpi = c.req_to_token.cpu().numpy(), c.req_pool_indices.cpu().numpy()
+    mask = c.custom_mask.cpu().numpy()
+    starts = np.concatenate([[0], np.cumsum(n * (sl + n))])
+    kflat = c.k_cache.reshape(-1, 1, *c.k_cache.shape[2:])
+    vflat = c.v_cache.reshape(-1, 1, *c.v_cache.shape[2:])
+    hq, d = c.q.shape[1], c.q.shape[2]
+    hkv = c.k_cache.shape[2]
+    spent, nbytes, done = 0.0, 0, 0
+    for b in range(len(sl)):
+        L = int(sl[b])
+        slots = torch.as_tensor(r2t[rpi[b], :L + n].astype(np.int64), device=c.k_cache.device)
+        k = kflat[slots].to(torch.float64).cpu().numpy()      # host copies: not timed
+        v = vflat[slots].to(torch.float64).cpu().numpy()
+        q = c.q[b * n:(b + 1) * n].to(torch.float64).cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.tree_verify_attention(q, k, v, np.arange(L + n)[None, :], [0], [L],
+                                     mask[starts[b]:starts[b + 1]], n, c.scale)
+        spent += time.perf_counter() - t0
+        nbytes += (L + n) * 2 * hkv * d * 2 + 2 * n * hq * d * 2 + n * hq * 4
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+            "kind": "oracle", "sample": f"draft-tree workload requests 0..{done - 1} ({done} of "
+                                        f"{len(sl)}), plain tree attention, float64 numpy; "
+                                        f"{spent:.1f} s"}
+
+
+def cpu_oracle_dca(torch, r, budget_s):
+    """The oracle's three-stage dual chunk decode over the workload's requests
+    in order (each request's pages gathered first)."""
+    import numpy as np
+    import oracle
+    c = r["case"]
+    b0 = c.base
+    pt, kl = r["pt"].cpu().numpy(), r["kl"].cpu().numpy()
+    P = b0.page_size
+    hq, d = b0.q.shape[1], b0.q.shape[2]
+    hkv = b0.k_cache.shape[2]
+    spent, nbytes, done = 0.0, 0, 0
+    for b in range(len(kl)):
+        L = int(kl[b])
+        npg = -(-L // P)
+        pages = torch.as_tensor(pt[b, :npg].astype(np.int64), device=b0.k_cache.device)
+        k = b0.k_cache[pages].to(torch.float64).cpu().numpy()
+        v = b0.v_cache[pages].to(torch.float64).cpu().numpy()
+        qs = [x[b:b + 1].to(torch.float64).cpu().numpy() for x in (b0.q, c.q_succ, c.q_inter)]
+        t0 = time.perf_counter()
+        oracle.dca_decode(*qs, k, v, np.arange(npg)[None, :], np.array([L]), P, b0.scale,
+                          c.chunk_size, c.local_size,
+                          original_max_position_embeddings=c.original_max_position_embeddings)
+        spent += time.perf_counter() - t0
+        nbytes += 2 * L * hkv * d * 2 + 4 * hq * d * 2 + 4 * npg
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+            "kind": "oracle", "sample": f"dual chunk decode requests 0..{done - 1} ({done} of "
+                                        f"{len(kl)}), three stages + merge, float64 numpy; "
+                                        f"{spent:.1f} s"}
 
 
 def cpu_oracle_sparse(torch, r, budget_s):
@@ -782,6 +852,8 @@ def main(argv=None):
                 "TFLOP/s": round(r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12, 2),
                 "algorithmic_bytes": r["bytes"], "flops": r["flops"],
                 "sum_committed_len": r["sum_l"], "prefill_workspace_bytes": r["ws"]}
+            if not args.no_cpu_baseline:
+                extra["cascade_verify"]["cpu_oracle"] = cpu_oracle_cascade(torch, r, 4.0)
         except Exception as e:
             extra["cascade_verify"] = {"error": repr(e)}
         torch.cuda.empty_cache()
@@ -800,6 +872,8 @@ def main(argv=None):
                 "step_GB/s": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 2),
                 "sum_kv_len": r["sum_l"], "num_splits": r["splits"],
                 "algorithmic_bytes": r["bytes"]}
+            if not args.no_cpu_baseline:
+                extra["dca_decode"]["cpu_oracle"] = cpu_oracle_dca(torch, r, 4.0)
         except Exception as e:
             extra["dca_decode"] = {"error": repr(e)}
         torch.cuda.empty_cache()
