@@ -223,3 +223,11 @@ def test_dca_argument_errors():
     nul[1] = None
     assert dd(*nul, 64, None, 64, 4, fake, fake, None, None, None) == EINVAL     # q_succ NULL
     assert b"q_succ" in lib.pkv_last_error()
+
+
+def test_binding_declares_every_entry_point():
+    """Every function the header declares has a ctypes signature in the binding
+    (so a changed argument list cannot go unnoticed)."""
+    declared = set(pkv.declared_symbols())
+    missing = sorted(declared - set(pkv._SIGNATURES))
+    assert not missing, missing
