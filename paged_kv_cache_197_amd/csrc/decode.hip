@@ -509,9 +509,13 @@ struct DecodeGroupKernel {
     } else {
       const int t = min(ts + (lane & 15), end - 1);
       const int slot = static_cast<int>(clamp_index(raw, a.num_pages)) * a.page_size + t % a.page_size;
+      // row 2i + half's slot: read from lanes 2i and 2i + 1 into scalar
+      // registers (no LDS permute on the way to the loads)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int64_t off = static_cast<int64_t>(__shfl(slot, 2 * i + half)) * row_bytes;
+        const int s0 = __builtin_amdgcn_readlane(slot, 2 * i);
+        const int s1 = __builtin_amdgcn_readlane(slot, 2 * i + 1);
+        const int64_t off = static_cast<int64_t>(half ? s1 : s0) * row_bytes;
         st.k[i] = ld_nt(kb + off);
         st.v[i] = ld_nt(vb + off);
       }
