@@ -500,7 +500,13 @@ struct PrefillKernel {
           s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[j]), as_bf16x8(qop[j]),
                                                           s_cur, 0, 0, 0);
       }
-      for (int it = 0; it < n_iter; ++it) {
+      // unrolled by the ring depth, so every stage offset below is a constant
+      // (folded into the LDS instructions' offsets instead of added per read)
+      for (int it0 = 0; it0 < n_iter; it0 += NSTAGE) {
+#pragma unroll
+      for (int u = 0; u < NSTAGE; ++u) {
+        const int it = it0 + u;
+        if (it >= n_iter) break;
         if (it + 1 < n_g) {
           if (it + 2 < n_g) wait_vmem<2 * IPW>();
           else wait_vmem<0>();
@@ -513,16 +519,17 @@ struct PrefillKernel {
                         entry_lds + (((it + 4) / SEG) & 1) * 256);
         if (it + 3 < n_g)
           copy_tile(a, L, gb + it + 3, (it + 3) % SEG, gw, lane, entries_of(it + 3), row_bytes,
-                    kb, vb, chunk_off, ring0 + ((it + 3) % NSTAGE) * STAGE);
+                    kb, vb, chunk_off, ring0 + ((u + 3) % NSTAGE) * STAGE);
         if (it < n_g) {
           const int kt = gb + it;
           u32x4 kw[NKS];
-          read_k(smem + ((it + 1) % NSTAGE) * STAGE, kbase, q, h, kw);
-          s_cur = softmax_pv(s_cur, smem + (it % NSTAGE) * STAGE + TILE, vofs,
+          read_k(smem + ((u + 1) % NSTAGE) * STAGE, kbase, q, h, kw);
+          s_cur = softmax_pv(s_cur, smem + u * STAGE + TILE, vofs,
                              kt >= full_tiles || kt < low_full, limit - kt * KT - 4 * h,
                              row_lo - kt * KT - 4 * h, h, a.scale_log2, kw, qop, acc, m_run,
                              l_run);
         }
+      }
       }
       __syncthreads();   // every wave is done with the rings
 
