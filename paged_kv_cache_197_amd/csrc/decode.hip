@@ -544,9 +544,13 @@ struct DecodeGroupKernel {
     }
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      x[i] = (4 * g + i < valid && (!EXT || 4 * g + i >= first)) ? s[i] * scale_log2
-                                                                     : neg_inf();
+    for (int i = 0; i < 4; ++i) {
+      // keys [first, valid) of the tile: one unsigned range test
+      const bool in = EXT ? static_cast<unsigned>(4 * g + i - first) <
+                                static_cast<unsigned>(valid - first)
+                          : 4 * g + i < valid;
+      x[i] = in ? s[i] * scale_log2 : neg_inf();
+    }
     float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mt = max_over_groups16(mt);
     const float m_new = fmaxf(m_run, mt);
