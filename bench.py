@@ -191,7 +191,7 @@ def run_decode(torch, pkv, workloads, args, window_left=-1, kv_chunk=None):
         ms, kern_ms = timed_loop(torch, step, args.steps, args.warmup)
         nbytes, sum_l = decode_bytes(c.seq_lens.long(), B, hq, hkv, d, P)
     res = dict(ms=ms, kernel_ms=kern_ms, bytes=nbytes, sum_l=sum_l, batch=B, splits=S,
-               case=c)
+               case=c, chunk=chunk)
     return res
 
 
@@ -315,7 +315,8 @@ def run_prefill_append(torch, pkv, workloads, args):
     flops, _ = prefill_flops(c.extend_lens.tolist(), c.seq_lens.tolist(), c.q.shape[1],
                              c.q.shape[2])
     append_bytes = 2 * 2 * kn.numel() * kn.element_size() + 4 * loc.numel()
-    return dict(ms=ms, call_ms=call_ms, flops=flops, append_bytes=append_bytes)
+    return dict(ms=ms, call_ms=call_ms, flops=flops, append_bytes=append_bytes, case=c, pt=pt,
+                kl=kl, k_new=kn, v_new=vn)
 
 
 def run_cascade(torch, pkv, workloads, args):
@@ -556,6 +557,92 @@ def cpu_oracle_swa(torch, r, budget_s):
                                         f"numpy; {spent:.1f} s"}
 
 
+def cpu_oracle_decode_window(torch, r, window_left, budget_s):
+    """The oracle's windowed split-KV decode (+ merge) over config3's requests in
+    order, each request's pages gathered first."""
+    import numpy as np
+    import oracle
+    c = r["case"]
+    pt_all, kl_all, _ = oracle.page_table_strided(
+        c.req_to_token.cpu().numpy(), c.req_pool_indices.cpu().numpy(),
+        c.seq_lens.cpu().numpy(), c.page_size, c.table_width)
+    P = c.page_size
+    hq, d = c.q.shape[1], c.q.shape[2]
+    hkv = c.k_cache.shape[2]
+    spent, nbytes, done = 0.0, 0, 0
+    for b in range(len(kl_all)):
+        L = int(kl_all[b])
+        npg = -(-L // P)
+        pages = torch.as_tensor(pt_all[b, :npg].astype(np.int64), device=c.k_cache.device)
+        k = c.k_cache[pages].to(torch.float64).cpu().numpy()
+        v = c.v_cache[pages].to(torch.float64).cpu().numpy()
+        q = c.q[b:b + 1].to(torch.float64).cpu().numpy()
+        t0 = time.perf_counter()
+        op, lp = oracle.paged_decode_splitkv(q, k, v, np.arange(npg)[None, :], np.array([L]), P,
+                                             c.scale, r["chunk"], r["splits"],
+                                             window_left=window_left)
+        oracle.merge_state(op, lp)
+        spent += time.perf_counter() - t0
+        vis = min(L, window_left + 1)
+        nbytes += 2 * vis * hkv * d * 2 + 2 * hq * d * 2
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+            "kind": "oracle", "sample": f"config3 requests 0..{done - 1} ({done} of "
+                                        f"{len(kl_all)}) under the window, float64 numpy; "
+                                        f"{spent:.1f} s"}
+
+
+def cpu_oracle_prefill_window(torch, r, window_left, rows):
+    """The oracle's windowed causal extend on the last `rows` new tokens of the
+    first long prompt (its keys gathered first)."""
+    import numpy as np
+    import oracle
+    c, pt, kl = r["case"], r["pt"].cpu().numpy(), r["kl"].cpu().numpy()
+    cu = c.cu_seqlens_q.cpu().numpy()
+    L, q1 = int(kl[0]), int(cu[1])
+    slots = torch.as_tensor(pt[0, :L].astype(np.int64), device=c.k_cache.device)
+    k = c.k_cache[slots].to(torch.float64).cpu().numpy()
+    v = c.v_cache[slots].to(torch.float64).cpu().numpy()
+    q = c.q[q1 - rows:q1].to(torch.float64).cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.paged_prefill(q, k, v, np.arange(L)[None, :], np.array([0, rows]), np.array([L]), 1,
+                         c.scale, causal=True, window_left=window_left)
+    spent = time.perf_counter() - t0
+    flops = 4 * c.q.shape[2] * c.q.shape[1] * sum(min(L - rows + j + 1, window_left + 1)
+                                                  for j in range(rows))
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(),
+            "kind": "oracle", "sample": f"the last {rows} new tokens of prompt 0 ({L} keys) under "
+                                        f"the window, float64 numpy; {spent:.1f} s"}
+
+
+def cpu_oracle_prefill_append(torch, r):
+    """The oracle's append-then-extend over every request of config2 (each
+    request's cache rows gathered first; the append writes the new rows)."""
+    import numpy as np
+    import oracle
+    c, pt, kl = r["case"], r["pt"].cpu().numpy(), r["kl"].cpu().numpy()
+    cu = c.cu_seqlens_q.cpu().numpy()
+    kn, vn = r["k_new"].to(torch.float64).cpu().numpy(), r["v_new"].to(torch.float64).cpu().numpy()
+    spent = 0.0
+    for b in range(len(kl)):
+        L, q0, q1 = int(kl[b]), int(cu[b]), int(cu[b + 1])
+        slots = torch.as_tensor(pt[b, :L].astype(np.int64), device=c.k_cache.device)
+        k = c.k_cache[slots].to(torch.float64).cpu().numpy()
+        v = c.v_cache[slots].to(torch.float64).cpu().numpy()
+        q = c.q[q0:q1].to(torch.float64).cpu().numpy()
+        loc = np.arange(L - (q1 - q0), L)          # the new tokens' rows of the gathered cache
+        t0 = time.perf_counter()
+        oracle.paged_prefill_append(q, k, v, np.arange(L)[None, :], np.array([0, q1 - q0]),
+                                    np.array([L]), 1, c.scale, loc, kn[q0:q1], vn[q0:q1])
+        spent += time.perf_counter() - t0
+    return {"value": round(r["flops"] / spent / 1e12, 6), "unit": "TFLOP/s",
+            "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"all {len(kl)} requests of config2 (append + extend), float64 numpy; "
+                      f"{spent:.1f} s"}
+
+
 def cpu_oracle_cascade(torch, r, budget_s):
     """The oracle's plain tree attention over the draft-tree workload's requests
     in order (each request's committed and draft tokens gathered first)."""
@@ -749,6 +836,8 @@ def main(argv=None):
                                          / HBM_PEAK_GBS, 4),
                 "visible_keys": r["sum_l"], "algorithmic_bytes": r["bytes"],
                 "num_splits": r["splits"]}
+            if not args.no_cpu_baseline:
+                extra["decode_window"]["cpu_oracle"] = cpu_oracle_decode_window(torch, r, W, 4.0)
         except Exception as e:
             extra["decode_window"] = {"error": repr(e)}
         torch.cuda.empty_cache()
@@ -818,6 +907,8 @@ def main(argv=None):
                 "kernel_ms": round(r["kernel_ms"], 5), "device_ms_per_step": round(r["ms"], 5),
                 "TFLOP/s": round(tf, 2), "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS,
                 "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": r["flops"]}
+            if not args.no_cpu_baseline:
+                extra["prefill_window"]["cpu_oracle"] = cpu_oracle_prefill_window(torch, r, W, 512)
         except Exception as e:
             extra["prefill_window"] = {"error": repr(e)}
         torch.cuda.empty_cache()
@@ -832,6 +923,8 @@ def main(argv=None):
                 "call_ms": round(r["call_ms"], 5), "device_ms_per_step": round(r["ms"], 5),
                 "append_bytes": r["append_bytes"],
                 "attention_TFLOP/s_over_call": round(r["flops"] / (r["call_ms"] * 1e-3) / 1e12, 2)}
+            if not args.no_cpu_baseline:
+                extra["prefill_append"]["cpu_oracle"] = cpu_oracle_prefill_append(torch, r)
         except Exception as e:
             extra["prefill_append"] = {"error": repr(e)}
         torch.cuda.empty_cache()
