@@ -17,10 +17,11 @@
 // wave per (draft row, kv head) holds the G query heads of that kv head with
 // D/64 dims per lane, streams the row's listed keys (a few, one coalesced
 // row read each for K and V), keeps an online softmax per head (scores
-// summed across the wave), then merges with the prefix pass's (O, LSE) that
+// summed across the wave with DPP and permlane swaps), then merges with the prefix pass's (O, LSE) that
 // the caller's out / lse hold, and writes the result over them.
 #include "args.hpp"
 #include "common.hpp"
+#include "lanes.hpp"
 #include "launch.hpp"
 
 namespace pkv {
@@ -110,52 +111,52 @@ __global__ __launch_bounds__(1024) void expand_cu_kernel(const int32_t* __restri
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
-  return v;
-}
-
-template <int D>
+// GMAX >= the GQA group (4, 8 or 16): the per-head arrays are sized by it, so
+// small groups keep few registers and many waves per SIMD.
+template <int D, int GMAX>
 __global__ __launch_bounds__(256) void expand_merge_kernel(ExpandMergeArgs a) {
   constexpr int DPL = D / 64;   // dims per lane
-  constexpr int GMAX = 16;
+  constexpr int KB = 4;         // keys whose rows are requested together
   const int lane = threadIdx.x & 63;
   const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (item >= static_cast<int64_t>(a.rows) * a.hkv) return;   // wave-uniform
   const int r = static_cast<int>(item / a.hkv);
   const int kvh = static_cast<int>(item - static_cast<int64_t>(r) * a.hkv);
   const int G = a.hq / a.hkv;
-  const int cnt = min(max(a.lens[r], 0), a.stride);
 
-  const uint16_t* qb = static_cast<const uint16_t*>(a.q) +
-                       (static_cast<int64_t>(r) * a.hq + static_cast<int64_t>(kvh) * G) * D +
-                       lane * DPL;
-  float qf[GMAX][DPL];
+  // Everything that does not depend on the key list is requested up front,
+  // together with the list itself (lane t holds entry t): the row's query
+  // heads, and the prefix pass's output and LSE that the merge reads.
+  const int32_t* row_keys = a.table + static_cast<int64_t>(r) * a.stride;
+  const int cnt = min(max(a.lens[r], 0), a.stride);
+  const int32_t lane_slot = lane < a.stride ? row_keys[lane] : 0;
+  const int64_t row0 = static_cast<int64_t>(r) * a.hq + static_cast<int64_t>(kvh) * G;
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + row0 * D + lane * DPL;
+  uint16_t* ob = static_cast<uint16_t*>(a.out) + row0 * D + lane * DPL;
+  float qf[GMAX][DPL], o1[GMAX][DPL], lse1[GMAX];
   float m[GMAX], l[GMAX], acc[GMAX][DPL];
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
     m[g] = neg_inf();
     l[g] = 0.f;
+    lse1[g] = g < G ? a.lse[row0 + g] : neg_inf();
 #pragma unroll
     for (int d = 0; d < DPL; ++d) {
       acc[g][d] = 0.f;
       qf[g][d] = g < G ? bf16_to_f32(qb[g * D + d]) : 0.f;
+      o1[g][d] = g < G ? bf16_to_f32(ob[g * D + d]) : 0.f;
     }
   }
 
   const uint16_t* kb = static_cast<const uint16_t*>(a.k);
   const uint16_t* vb = static_cast<const uint16_t*>(a.v);
-  const int32_t* row_keys = a.table + static_cast<int64_t>(r) * a.stride;
-  // keys in batches of KB: every batch's K and V rows are requested before
-  // the first score, so the row reads overlap instead of forming a chain
-  constexpr int KB = 8;
   for (int t0 = 0; t0 < cnt; t0 += KB) {
     float kf[KB][DPL], vf[KB][DPL];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int t = min(t0 + u, cnt - 1);
-      const int64_t slot = clamp_index(row_keys[t], a.num_slots);
+      const int32_t raw = t < 64 ? __builtin_amdgcn_readlane(lane_slot, t) : row_keys[t];
+      const int64_t slot = clamp_index(raw, a.num_slots);
       const int64_t off = (slot * a.hkv + kvh) * D + lane * DPL;
 #pragma unroll
       for (int d = 0; d < DPL; ++d) {
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(256) void expand_merge_kernel(ExpandMergeArgs a) {
             float part = 0.f;
 #pragma unroll
             for (int d = 0; d < DPL; ++d) part = __builtin_fmaf(qf[g][d], kf[u][d], part);
-            const float sc = wave_sum(part) * a.scale_log2;
+            const float sc = wave_sum64(part) * a.scale_log2;
             const float m_new = fmaxf(m[g], sc);
             const float alpha = fast_exp2(m[g] - m_new);   // 0 while m is -inf
             const float p = fast_exp2(sc - m_new);
@@ -187,37 +188,30 @@ __global__ __launch_bounds__(256) void expand_merge_kernel(ExpandMergeArgs a) {
     }
   }
 
-  // merge with the prefix pass's state held in out / lse
-  uint16_t* ob = static_cast<uint16_t*>(a.out);
+  // merge with the prefix pass's state and write over it
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
     if (g < G) {
-      const int64_t row = static_cast<int64_t>(r) * a.hq + static_cast<int64_t>(kvh) * G + g;
-      const float lse1 = a.lse[row];
       const float lse2 = cnt > 0 ? (m[g] + fast_log2(l[g])) * kLn2 : neg_inf();
-      const float mx = fmaxf(lse1, lse2);
+      const float mx = fmaxf(lse1[g], lse2);
       float w1 = 0.f, w2 = 0.f;
       if (mx != neg_inf()) {
-        w1 = fast_exp2((lse1 - mx) * kLog2e);
+        w1 = fast_exp2((lse1[g] - mx) * kLog2e);
         w2 = fast_exp2((lse2 - mx) * kLog2e);
       }
       const float total = w1 + w2;
       const float inv = total > 0.f ? 1.f / total : 0.f;
       const float inv_l = cnt > 0 ? 1.f / l[g] : 0.f;
-      uint16_t* dst = ob + row * D + lane * DPL;
       float res[DPL];
 #pragma unroll
-      for (int d = 0; d < DPL; ++d) {
-        const float o1 = bf16_to_f32(dst[d]);
-        const float o2 = acc[g][d] * inv_l;
-        res[d] = (w1 * o1 + w2 * o2) * inv;
-      }
+      for (int d = 0; d < DPL; ++d) res[d] = (w1 * o1[g][d] + w2 * (acc[g][d] * inv_l)) * inv;
+      uint16_t* dst = ob + g * D;
       if constexpr (DPL == 2) {
         *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(res[0], res[1]);
       } else {
         dst[0] = f32_to_bf16(res[0]);
       }
-      if (lane == 0) a.lse[row] = mx == neg_inf() ? neg_inf() : mx + fast_log2(total) * kLn2;
+      if (lane == 0) a.lse[row0 + g] = mx == neg_inf() ? neg_inf() : mx + fast_log2(total) * kLn2;
     }
   }
 }
@@ -235,13 +229,22 @@ hipError_t cascade_expand(const pkv::CascadeExpandArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+static void launch_expand_merge(const pkv::ExpandMergeArgs& a, dim3 grid, hipStream_t stream) {
+  const int G = a.hq / a.hkv;
+  if (G <= 4)
+    hipLaunchKernelGGL((pkv::expand_merge_kernel<D, 4>), grid, dim3(256), 0, stream, a);
+  else if (G <= 8)
+    hipLaunchKernelGGL((pkv::expand_merge_kernel<D, 8>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((pkv::expand_merge_kernel<D, 16>), grid, dim3(256), 0, stream, a);
+}
+
 hipError_t expand_merge(const pkv::ExpandMergeArgs& a, int head_dim, hipStream_t stream) {
   const int64_t items = static_cast<int64_t>(a.rows) * a.hkv;
   const dim3 grid(static_cast<unsigned>((items + 3) / 4));
-  if (head_dim == 128)
-    hipLaunchKernelGGL(pkv::expand_merge_kernel<128>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(pkv::expand_merge_kernel<64>, grid, dim3(256), 0, stream, a);
+  if (head_dim == 128) launch_expand_merge<128>(a, grid, stream);
+  else launch_expand_merge<64>(a, grid, stream);
   return hipGetLastError();
 }
 
