@@ -133,3 +133,23 @@ def test_long_prompt_sampled_rows():
                                       np.array([0, 1]), np.array([L]), 1, c.scale, causal=True)
         assert_close(f"out row {b},{j}", np_f(out[r:r + 1]), ro, O_TOL)
         assert_close(f"lse row {b},{j}", np_f(lse[r:r + 1]), rl, LSE_TOL)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_many_requests_ordered_by_length(causal):
+    """130 requests (three chunks of the longest-first slot order, ties
+    included, empty requests among them), every row against the oracle."""
+    g = np.random.default_rng(5)
+    B = 130
+    prefix = g.integers(0, 300, B).tolist()
+    extend = g.integers(0, 70, B).tolist()
+    prefix[10:14] = [100, 100, 100, 100]          # equal lengths: ties by index
+    extend[10:14] = [20, 20, 20, 20]
+    extend[20] = 0
+    total = sum(p + e for p, e in zip(prefix, extend))
+    c = workloads.make_prefill_case(131, prefix_lens=prefix, extend_lens=extend, num_q_heads=8,
+                                    num_kv_heads=2, head_dim=128, page_size=16,
+                                    num_pages=total // 16 + 2 * B)
+    c = to_device(c, DEV)
+    say(f"prefill {B} requests causal={causal}")
+    run_case(c, causal)
