@@ -457,9 +457,9 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
   // The normalised partial is staged in LDS as [HB][DV + 4] fp32 (the ring and
   // exchange buffers are free now), so that it is written, and read back, in
   // contiguous runs: device-coherent stores go through to memory as they are
-  // issued, and scattered pieces would each cost a memory write. Other splits'
-  // partials travel as bf16 (the output precision); the merging split keeps
-  // its own in fp32.
+  // issued, and scattered pieces would each cost a memory write. Partials
+  // travel as bf16 (the output precision); the merging split rounds its own
+  // the same way, so the result does not depend on which split ends last.
   char* wsb = static_cast<char*>(a.workspace);
   const int64_t n_parts = static_cast<int64_t>(units) * splits;
   bf16_t* ws_o = reinterpret_cast<bf16_t*>(wsb);
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
 
   // ---- last split: merge all splits of this (request, head block) ----
   // weights w_s(head) = exp(lse_s - max_s lse_s), kept in LDS; this split's
-  // own partial is read from the staging area
+  // own partial is read from the staging area (rounded as the others were)
   {
     const auto rl = coherent_rsrc(ws_lse + part0 * C::HB, static_cast<uint32_t>(splits * C::HB * 4));
     for (int i = threadIdx.x; i < splits * C::HB; i += C::THREADS)
@@ -538,7 +538,9 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
 #pragma unroll
       for (int k = 0; k < PASSES; ++k) {
         const int e = k * C::THREADS + static_cast<int>(threadIdx.x);
-        v[k] = *reinterpret_cast<const f32x4*>(st_o + (e / F4_ROW) * SROW + 4 * (e % F4_ROW));
+        const f32x4 f = *reinterpret_cast<const f32x4*>(st_o + (e / F4_ROW) * SROW + 4 * (e % F4_ROW));
+        const uint32_t lo = pack_bf16x2(f[0], f[1]), hi = pack_bf16x2(f[2], f[3]);
+        v[k] = f32x4{bf16lo(lo), bf16hi(lo), bf16lo(hi), bf16hi(hi)};
       }
     } else {
       const auto ro = coherent_rsrc(ws_o + (part0 + s2) * C::HB * C::DV, kPartBytes);
