@@ -30,7 +30,7 @@ def _replay_and_check(step, outs, n=4):
     torch.cuda.synchronize()
     for i in range(n):
         for o in outs:
-            o.fill_(float("nan"))
+            o.fill_(float("nan") if o.is_floating_point() else -7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -104,5 +104,62 @@ def test_sparse_graph():
                                s.scale, head_dim_v=s.head_dim_v, workspace=ws, out=out, lse=lse)
 
     say("graph: sparse MLA decode")
+    step()
+    _replay_and_check(step, [out, lse])
+
+
+def test_cascade_step_graph():
+    c = workloads.make_cascade_case(151, prefix_lens=[300, 40, 1029], num_draft=6,
+                                    num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16,
+                                    num_pages=120)
+    c = to_device(c, DEV)
+    B, n = c.seq_lens.numel(), c.num_draft
+    pt, kl, _ = pkv.build_page_table(c.req_to_token, c.req_pool_indices, c.seq_lens, 16,
+                                     c.table_width)
+    tab = torch.empty((B * n, n), dtype=torch.int32, device=DEV)
+    lens = torch.empty((B * n,), dtype=torch.int32, device=DEV)
+    cu_q = torch.arange(0, B * n + 1, n, dtype=torch.int32, device=DEV)
+    need = pkv.paged_attn_varlen_prefill_workspace_size(B, B * n, n, c.table_width * 16, 16, 4,
+                                                        128)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(c.q)
+    lse = torch.empty((B * n, 16), dtype=torch.float32, device=DEV)
+
+    def step():
+        pkv.build_cascade_expand_table(c.custom_mask, c.req_to_token, c.req_pool_indices,
+                                       c.seq_lens, n, expand_table=tab, expand_lens=lens,
+                                       with_cu=False)
+        pkv.paged_attn_cascade(c.q, c.k_cache, c.v_cache, pt, cu_q, kl, n, c.scale, tab, lens,
+                               workspace=ws, out=out, lse=lse)
+
+    say("graph: cascade (expand table + prefix pass + expand pass)")
+    step()
+    _replay_and_check(step, [out, lse, tab, lens])
+
+
+def test_dca_step_graph():
+    c = workloads.make_dca_case(161, seq_lens=[10, 200, 700], num_q_heads=16, num_kv_heads=8,
+                                head_dim=128, page_size=16, num_pages=80, chunk_size=160,
+                                local_size=32, original_max_position_embeddings=100,
+                                value_device=DEV)
+    b = to_device(c.base, DEV)
+    C = c.chunk_size - c.local_size
+    pt, kl, _ = pkv.build_page_table(b.req_to_token, b.req_pool_indices, b.seq_lens, 16,
+                                     b.table_width)
+    S = -(-700 // C)
+    B, hq, d = b.q.shape
+    op = torch.empty((S, B, hq, d), dtype=torch.float32, device=DEV)
+    lp = torch.empty((S, B, hq), dtype=torch.float32, device=DEV)
+    out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, hq), dtype=torch.float32, device=DEV)
+    meta = pkv.build_dca_decode_tables(pt, kl, C, 16, c.original_max_position_embeddings)
+
+    def step():
+        pkv.paged_attn_dca_decode(b.q, c.q_succ, c.q_inter, b.k_cache, b.v_cache, pt, kl,
+                                  b.scale, C, kv_chunk=C, num_splits=S,
+                                  q_scale=meta["scaling_factor"], o_partial=op, lse_partial=lp)
+        pkv.merge_state(op, lp, out=out, lse_out=lse)
+
+    say("graph: dual chunk decode + merge")
     step()
     _replay_and_check(step, [out, lse])
