@@ -488,7 +488,7 @@ def config3(value_device="cpu", with_values=True):
                             name="config3")
 
 
-def config4(value_device="cpu", kv_chunk=1024, with_values=True):
+def config4(value_device="cpu", kv_chunk=1536, with_values=True):
     """Sliding-window decode over the prefill-aware table, bf16: B 32,
     prefill ~ U[2048, 8192], seq = prefill + U[1, 8192], window 4096,
     64 q / 8 kv heads, D 128, page 1 over 32*16384 slots."""
