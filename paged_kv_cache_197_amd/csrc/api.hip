@@ -44,7 +44,7 @@ static float scale_log2(float softmax_scale) {
   return static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
 }
 
-// Key-split plan of paged_attn_varlen_prefill. A workgroup (8 waves) handles
+// Key-split plan of paged_attn_varlen_prefill. A workgroup handles
 // one (q tile, kv head); when there are fewer such units than half the CUs,
 // the 32-key tiles a q tile sees are cut into splits of split_tiles tiles so
 // that about kPrefillWorkgroups workgroups run, never below kMinSplitTiles
@@ -56,9 +56,14 @@ constexpr int32_t kMaxDraft = 256;
 
 constexpr int64_t kPrefillWorkgroups = 256;
 constexpr int64_t kMinSplitTiles = 4;
+// (q tile, kv head) units from which workgroups of one group of four waves
+// (two per CU) are used: at least two rounds of the 512 workgroup slots, so
+// that the longer per-workgroup chains (no key halving inside) are hidden by
+// the second workgroup per CU; below it two groups per workgroup halve them.
+constexpr int64_t kOneGroupUnits = 1024;
 
 struct PrefillPlan {
-  int32_t split_tiles, max_splits, qtile_slots;
+  int32_t split_tiles, max_splits, qtile_slots, groups;
   size_t counter_bytes, lse_bytes, o_bytes, bytes;
 };
 
@@ -81,8 +86,10 @@ static PrefillPlan prefill_plan(int64_t batch, int64_t total_q, int64_t max_seql
   p.split_tiles = static_cast<int32_t>(std::min<int64_t>(tiles, 1 << 30));
   p.max_splits = static_cast<int32_t>((n_kt + p.split_tiles - 1) / p.split_tiles);
   p.counter_bytes = p.lse_bytes = p.o_bytes = p.bytes = 0;
+  p.groups = 2;
   if (p.max_splits <= 1) {
     p.max_splits = 1;
+    if (units >= kOneGroupUnits) p.groups = 1;
     return p;
   }
   const int64_t n_hb = (hq / hkv + 3) / 4;
@@ -383,6 +390,7 @@ static pkv_status_t prefill_prepare(const void* q, int32_t dtype, const void* k_
   a.split_tiles = plan.split_tiles;
   a.max_splits = plan.max_splits;
   a.qtile_slots = plan.qtile_slots;
+  a.groups = plan.groups;
   char* ws = static_cast<char*>(workspace);
   a.counters = plan.bytes ? reinterpret_cast<int32_t*>(ws) : nullptr;
   a.ws_lse = plan.bytes ? reinterpret_cast<float*>(ws + plan.counter_bytes) : nullptr;

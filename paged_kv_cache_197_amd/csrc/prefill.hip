@@ -3,15 +3,21 @@
 // new, cu_seqlens_q over the new tokens, causal=True). New row j of request b
 // sits at position L_b - M_b + j and sees keys [0, L_b - M_b + j].
 //
-// Work decomposition. One workgroup of 8 waves per (32-row q tile, kv head,
-// request, key split). A q tile's visible 32-key tiles are cut into splits of
+// Work decomposition. One workgroup per (32-row q tile, kv head, request, key
+// split), of GROUPS groups of four waves: two groups (one workgroup per CU)
+// for launches with few q tiles, one group (two workgroups per CU) for large
+// ones. A q tile's visible 32-key tiles are cut into splits of
 // `split_tiles` tiles when the tiles are long enough to leave CUs idle
 // otherwise; each split writes its normalised partial output and LSE to the
 // workspace at device scope, and the last split of the tile to finish (device-
 // scope counter) merges them. A q tile with one split writes the output
-// directly. Inside a workgroup the split's key tiles are halved between two
-// groups of four waves, whose softmax states are merged through LDS at the end;
-// the two waves sharing a SIMD (one per group) hide each other's latencies.
+// directly. With two groups the split's key tiles are halved between them and
+// their softmax states are merged through LDS at the end; the two waves
+// sharing a SIMD (one per group) hide each other's latencies, but the per-tile
+// workgroup barrier keeps them in step. With one group per workgroup, the two
+// waves sharing a SIMD belong to different workgroups and drift apart, so one
+// issues MFMAs while the other runs its softmax (11% faster in steady state);
+// short launches keep two groups, whose halved key range is the shorter chain.
 // Within a group wave w owns q heads w, w+4, ... of the GQA group and all four
 // share 32-key K/V tiles, copied into the group's four-stage LDS ring by
 // direct global-to-LDS loads three tiles ahead of their use. The page-table
@@ -47,8 +53,10 @@ enum PageMode : int {
   kPageAny = 2,     // anything else: division
 };
 
-template <int D, int PM>
+template <int D, int PM, int GROUPS>
 struct PrefillKernel {
+  static_assert(GROUPS == 1 || GROUPS == 2, "one or two groups of four waves");
+  static constexpr int WAVES = 4 * GROUPS;
   static constexpr int KT = 32;               // keys per tile
   static constexpr int QT = 32;               // q rows per tile
   static constexpr int NKS = D / 16;          // 16-wide k-steps of S^T
@@ -59,8 +67,8 @@ struct PrefillKernel {
   static constexpr int STAGE = 2 * TILE;      // K and V
   static constexpr int NSTAGE = 4;
   static constexpr int GROUP_LDS = NSTAGE * STAGE;
-  static constexpr int ENTRY_BYTES = 8 * 2 * 256;     // 8 waves x 2 segments x 64 words
-  static constexpr int LDS_BYTES = 2 * GROUP_LDS + ENTRY_BYTES;
+  static constexpr int ENTRY_BYTES = WAVES * 2 * 256; // waves x 2 segments x 64 words
+  static constexpr int LDS_BYTES = GROUPS * GROUP_LDS + ENTRY_BYTES;
   static constexpr int RPB = 1024 / ROW;      // key rows per 1 KB copy block
   static constexpr int IPW = TILE / 1024 / 4; // copy blocks per wave and tensor
   static constexpr int KPW = IPW * RPB;       // keys per wave per tile
@@ -69,7 +77,7 @@ struct PrefillKernel {
   static constexpr int QPW = TILE / 2048;             // Q copies per wave (4 heads / 8 waves)
   static constexpr float kRescaleLog2 = 8.f;          // see softmax_pv
   static_assert(KPW == 8, "a wave copies 8 keys of each tile");
-  static_assert(4 * MERGE_F4 * 64 * 16 <= 2 * GROUP_LDS, "merge buffer fits the rings");
+  static_assert(GROUPS == 1 || 4 * MERGE_F4 * 64 * 16 <= 2 * GROUP_LDS, "merge buffer fits the rings");
   static_assert(4 * TILE / 1024 == 8 * QPW, "Q copies split evenly over the waves");
 
   // key of S^T accumulator register r for lane half h
@@ -394,7 +402,7 @@ struct PrefillKernel {
     const int t_begin = kt_lo + split * a.split_tiles;
     const int t_end = (split == n_split - 1) ? n_ktiles : t_begin + a.split_tiles;
     const int n_all = max(t_end - t_begin, 0);
-    const int n_iter = (n_all + 1) / 2;           // group 0 takes the first half
+    const int n_iter = GROUPS == 2 ? (n_all + 1) / 2 : n_all;   // group 0 takes the first half
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int grp = wave >> 2;
@@ -447,13 +455,34 @@ struct PrefillKernel {
       const bool head_ok = hg < G;
       const int head = kvh * G + min(hg, G - 1);
 
-      // the first segment's page entries, then the workgroup's Q tile (once,
-      // into LDS): only the entries are waited for before the first copies;
-      // Q lands together with tile 0
-      const uint32_t entry_lds = lds0 + 2 * GROUP_LDS + wave * 512;
+      // the first segment's page entries, then the workgroup's Q tile. With
+      // two groups Q is copied once into LDS: only the entries are waited for
+      // before the first copies, and Q lands together with tile 0. With one
+      // group (no free stage for four heads' Q) each wave loads its Q^T operand
+      // (row q, dims 16j + 8h + [0, 8)) from memory, 16 bytes of the row per
+      // lane and k-step, in the same round trip as the entries.
+      const uint32_t entry_lds = lds0 + GROUPS * GROUP_LDS + wave * 512;
       if (n_g > 0) fetch_entries(a, pt_row, L, gb, gw, lane, entry_lds);
-      copy_q(a, wave, lane, hb, kvh, G, q0 + j0, rows, lds0);
-      if (n_g > 0) wait_vmem<QPW>();
+      u32x4 qop[NKS];
+      if constexpr (GROUPS == 2) {
+        copy_q(a, wave, lane, hb, kvh, G, q0 + j0, rows, lds0);
+        if (n_g > 0) wait_vmem<QPW>();
+      } else {
+        const int tok = min(q0 + j0 + min(q, rows - 1), a.total_q - 1);
+        const char* qrow = static_cast<const char*>(a.q) +
+                           (static_cast<int64_t>(tok) * a.hq + head) * ROW;
+#pragma unroll
+        for (int j = 0; j < NKS; ++j)
+          qop[j] = *reinterpret_cast<const u32x4*>(qrow + (16 * j + 8 * h) * 2);
+        wait_vmem<0>();   // the entries and Q
+#pragma unroll
+        for (int j = 0; j < NKS; ++j) {
+          retire(qop[j].x);
+          retire(qop[j].y);
+          retire(qop[j].z);
+          retire(qop[j].w);
+        }
+      }
       f32x16 acc[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n)
@@ -466,7 +495,8 @@ struct PrefillKernel {
       // Before tile i is read, every copy issued before tile i+1's must have
       // landed: at most the 2*IPW copies of tile i+1 stay in flight.
       // entry slots of segment m: entry_lds + (m % 2) * 256 (LDS address / pointer)
-      const int32_t* entry_ptr = reinterpret_cast<const int32_t*>(smem + 2 * GROUP_LDS + wave * 512);
+      const int32_t* entry_ptr =
+          reinterpret_cast<const int32_t*>(smem + GROUPS * GROUP_LDS + wave * 512);
       auto entries_of = [&](int it) { return entry_ptr + ((it / SEG) & 1) * 64; };
       // Tile i's K and V land in stage i % 4, copied three tiles ahead; tile
       // i's softmax and O^T update run together with tile i+1's S^T, so at the
@@ -486,10 +516,10 @@ struct PrefillKernel {
         wait_vmem<0>();   // this wave's Q copies
       }
       __syncthreads();   // tile 0 and Q are in LDS
-      // Q^T operand (row q, dims 16j + 8h + [0, 8)) of this wave's head, read
-      // before the loop's first barrier (after which stage 3 takes tile 3)
-      u32x4 qop[NKS];
-      read_k(smem + q_lds(gw) - grp * GROUP_LDS, kbase, q, h, qop);
+      // two groups: the Q^T operand (row q, dims 16j + 8h + [0, 8)) of this
+      // wave's head, read before the loop's first barrier (after which stage 3
+      // takes tile 3)
+      if constexpr (GROUPS == 2) read_k(smem + q_lds(gw) - grp * GROUP_LDS, kbase, q, h, qop);
       if (n_g > 0) {
         u32x4 kw[NKS];
         read_k(smem, kbase, q, h, kw);
@@ -536,30 +566,33 @@ struct PrefillKernel {
       // ---- merge the two key halves (group 1 -> group 0) through LDS ----
       // wave gw's region: [float4 k][lane], k < 4 NB: acc[k/4][4(k%4) .. +3], then (m, l)
       f32x4* mbuf = reinterpret_cast<f32x4*>(smem) + gw * MERGE_F4 * 64 + lane;
-      if (grp == 1) {
+      if (GROUPS == 2 && grp == 1) {
 #pragma unroll
         for (int k = 0; k < 4 * NB; ++k)
           mbuf[64 * k] = f32x4{acc[k >> 2][4 * (k & 3)], acc[k >> 2][4 * (k & 3) + 1],
                                acc[k >> 2][4 * (k & 3) + 2], acc[k >> 2][4 * (k & 3) + 3]};
         mbuf[64 * 4 * NB] = f32x4{m_run, l_run, 0.f, 0.f};
       }
-      __syncthreads();
+      if constexpr (GROUPS == 2) __syncthreads();
       float lse_val = 0.f, inv = 0.f;
       if (grp == 0) {
-        const f32x4 ml = mbuf[64 * 4 * NB];
-        const float m1 = ml[0];
-        const float l1 = ml[1];
-        const float mm = fmaxf(m_run, m1);
-        const float f0 = (m_run == neg_inf()) ? 0.f : fast_exp2((m_run - mm) * a.scale_log2);
-        const float f1 = (m1 == neg_inf()) ? 0.f : fast_exp2((m1 - mm) * a.scale_log2);
+        float mm = m_run, l_m = l_run;
+        if constexpr (GROUPS == 2) {
+          const f32x4 ml = mbuf[64 * 4 * NB];
+          const float m1 = ml[0];
+          const float l1 = ml[1];
+          mm = fmaxf(m_run, m1);
+          const float f0 = (m_run == neg_inf()) ? 0.f : fast_exp2((m_run - mm) * a.scale_log2);
+          const float f1 = (m1 == neg_inf()) ? 0.f : fast_exp2((m1 - mm) * a.scale_log2);
 #pragma unroll
-        for (int k = 0; k < 4 * NB; ++k) {
-          const f32x4 o1 = mbuf[64 * k];
+          for (int k = 0; k < 4 * NB; ++k) {
+            const f32x4 o1 = mbuf[64 * k];
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            acc[k >> 2][4 * (k & 3) + c] = f0 * acc[k >> 2][4 * (k & 3) + c] + f1 * o1[c];
+            for (int c = 0; c < 4; ++c)
+              acc[k >> 2][4 * (k & 3) + c] = f0 * acc[k >> 2][4 * (k & 3) + c] + f1 * o1[c];
+          }
+          l_m = f0 * l_run + f1 * l1;
         }
-        const float l_m = f0 * l_run + f1 * l1;
         const float l_tot = l_m + __shfl_xor(l_m, 32);
         inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         lse_val = l_tot > 0.f ? (mm * a.scale_log2 + fast_log2(l_tot)) * kLn2 : neg_inf();
@@ -657,9 +690,9 @@ struct PrefillKernel {
   }
 };
 
-template <int D, int PM>
-__global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a) {
-  PrefillKernel<D, PM>::run(a);
+template <int D, int PM, int GROUPS>
+__global__ __launch_bounds__(256 * GROUPS, 2 / GROUPS) void prefill_kernel(PrefillArgs a) {
+  PrefillKernel<D, PM, GROUPS>::run(a);
 }
 
 }  // namespace pkv
@@ -668,8 +701,12 @@ namespace pkv_launch {
 
 template <int D, int PM>
 static void launch_prefill_t(const pkv::PrefillArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((pkv::prefill_kernel<D, PM>), grid, dim3(512),
-                     (pkv::PrefillKernel<D, PM>::LDS_BYTES), stream, a);
+  if (a.groups == 1)
+    hipLaunchKernelGGL((pkv::prefill_kernel<D, PM, 1>), grid, dim3(256),
+                       (pkv::PrefillKernel<D, PM, 1>::LDS_BYTES), stream, a);
+  else
+    hipLaunchKernelGGL((pkv::prefill_kernel<D, PM, 2>), grid, dim3(512),
+                       (pkv::PrefillKernel<D, PM, 2>::LDS_BYTES), stream, a);
 }
 
 template <int D>

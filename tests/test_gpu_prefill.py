@@ -153,3 +153,29 @@ def test_many_requests_ordered_by_length(causal):
     c = to_device(c, DEV)
     say(f"prefill {B} requests causal={causal}")
     run_case(c, causal)
+
+
+@pytest.mark.parametrize("D,P,group,causal", [
+    (128, 1, 4, True), (128, 16, 2, True), (64, 1, 4, False), (64, 8, 1, True),
+])
+def test_one_group_workgroups(D, P, group, causal):
+    """Launches with at least 1024 (q tile, kv head) units run workgroups of
+    one group of four waves, each walking its q tile's whole key range (the
+    smaller launches above halve it between two groups): ten requests with
+    ragged extends past 370 rows and prefixes, 8 kv heads, every row."""
+    g = np.random.default_rng(17 + D + P + group)
+    B, hkv = 10, 8
+    prefix = g.integers(0, 300, B).tolist()
+    extend = g.integers(370, 520, B).tolist()
+    prefix[3] = 0
+    extend[7] = 513                                   # one row past 16 q tiles
+    total_q = sum(extend)
+    qtiles = min(-(-total_q // 32) + B, B * -(-max(extend) // 32))
+    assert qtiles * hkv >= 1024, "the launch must be large enough for one-group workgroups"
+    total = sum(p + e for p, e in zip(prefix, extend))
+    c = workloads.make_prefill_case(300 + D + P + group, prefix_lens=prefix, extend_lens=extend,
+                                    num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=D,
+                                    page_size=P, num_pages=total // P + 2 * B)
+    c = to_device(c, DEV)
+    say(f"prefill one-group launch D={D} P={P} group={group} causal={causal}")
+    run_case(c, causal)
