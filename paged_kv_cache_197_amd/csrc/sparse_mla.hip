@@ -454,12 +454,15 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
   }
 
   // ---- hand-off through the workspace ----
-  // The normalised partial is staged in LDS as [HB][DV + 4] fp32 (the ring and
-  // exchange buffers are free now), so that it is written, and read back, in
-  // contiguous runs: device-coherent stores go through to memory as they are
-  // issued, and scattered pieces would each cost a memory write. Partials
-  // travel as bf16 (the output precision); the merging split rounds its own
-  // the same way, so the result does not depend on which split ends last.
+  // A split's partial travels in register order: for wave w, register index
+  // i and lane l, the four value dims 128 w4 + 4 rho(h, i) + [0, 4) of head
+  // 32 quad + col as bf16 (8 bytes), so that every store instruction writes
+  // 512 contiguous bytes (device-coherent stores go through to memory as they
+  // are issued) and the merging split reads them back in the same lanes, with
+  // no LDS staging on either side. Partials travel as bf16 (the output
+  // precision) and the merging split uses its own rounded the same way; the
+  // weights, their sum and the weighted sum run in split order, so the result
+  // does not depend on which split ends last.
   char* wsb = static_cast<char*>(a.workspace);
   const int64_t n_parts = static_cast<int64_t>(units) * splits;
   bf16_t* ws_o = reinterpret_cast<bf16_t*>(wsb);
@@ -467,36 +470,22 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
   int* counter = reinterpret_cast<int*>(wsb + n_parts * C::HB * C::DV * 2 + n_parts * C::HB * 4);
   const int64_t part0 = static_cast<int64_t>(unit) * splits;   // this unit's first partial
   constexpr uint32_t kPartBytes = C::HB * C::DV * 2;
-  constexpr int SROW = C::DV + 4;                  // staging row, padded (floats)
-  constexpr int F4_ROW = C::DV / 4;                // float4s per head row
-  constexpr int PASSES = C::HB * F4_ROW / C::THREADS;
-  static_assert(PASSES * C::THREADS == C::HB * F4_ROW, "whole rows per pass");
-  static_assert((C::HB * SROW + C::HB + 64 * C::HB) * 4 <= C::LDS_BYTES, "staging fits");
-  float* st_o = reinterpret_cast<float*>(smem);    // [HB][SROW]
-  float* st_lse = st_o + C::HB * SROW;             // [HB]
-  float* st_w = st_lse + C::HB;                    // [splits][HB], splits <= 64
-  __syncthreads();   // m_buf / l_buf lie in the staging area
-  {
-    float* row = st_o + (32 * quad + col) * SROW + C::DV_SLICE * w4;
+  const uint32_t lane_off = static_cast<uint32_t>((wave * 16 * 64 + lane) * 8);   // + 512 i
+  const int hd = 32 * quad + col;                  // head within the block
+  u32x2 own[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      *reinterpret_cast<f32x4*>(row + 4 * rho32(h, i)) =
-          f32x4{acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
-    if (w4 == 0 && h == 0) st_lse[32 * quad + col] = lse_val;
+  for (int i = 0; i < 16; ++i) {
+    own[i].x = pack_bf16x2(acc[0][i] * inv, acc[1][i] * inv);
+    own[i].y = pack_bf16x2(acc[2][i] * inv, acc[3][i] * inv);
   }
-  __syncthreads();
   {
     const auto ro = coherent_rsrc(ws_o + (part0 + ks) * C::HB * C::DV, kPartBytes);
 #pragma unroll
-    for (int k = 0; k < PASSES; ++k) {
-      const int e = k * C::THREADS + static_cast<int>(threadIdx.x);   // 4-dim group in [HB][DV]
-      const f32x4 v = *reinterpret_cast<const f32x4*>(st_o + (e / F4_ROW) * SROW + 4 * (e % F4_ROW));
-      const u32x2 w2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      store_coherent(ro, static_cast<uint32_t>(e * 8), __builtin_bit_cast(f32x2_t, w2));
-    }
-    if (threadIdx.x < C::HB)
-      store_coherent(coherent_rsrc(ws_lse + (part0 + ks) * C::HB, C::HB * 4), threadIdx.x * 4,
-                     st_lse[threadIdx.x]);
+    for (int i = 0; i < 16; ++i)
+      store_coherent(ro, lane_off + 512u * i, __builtin_bit_cast(f32x2_t, own[i]));
+    if (w4 == 0 && h == 0)
+      store_coherent(coherent_rsrc(ws_lse + (part0 + ks) * C::HB, C::HB * 4),
+                     static_cast<uint32_t>(hd * 4), lse_val);
   }
   wait_all_vmem();
   __syncthreads();   // every wave's part has been written through
@@ -505,70 +494,65 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
   if (!is_last) return;
 
   // ---- last split: merge all splits of this (request, head block) ----
-  // weights w_s(head) = exp(lse_s - max_s lse_s), kept in LDS; this split's
-  // own partial is read from the staging area (rounded as the others were)
+  // Other splits' partials are loaded two splits at a time, the first two in
+  // flight together with the LSEs (gathered into LDS: [split][head]).
+  constexpr int BATCH = 2;
+  u32x2 part[BATCH][16];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int s2 = s0 + q;
+      if (s2 < splits && s2 != ks) {
+        const auto ro = coherent_rsrc(ws_o + (part0 + s2) * C::HB * C::DV, kPartBytes);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          part[q][i] = __builtin_bit_cast(u32x2, load_coherent2(ro, lane_off + 512u * i));
+      }
+    }
+  };
+  load_batch(0);
+  float* st_w = reinterpret_cast<float*>(smem);   // [splits][HB] (the ring is free now)
   {
     const auto rl = coherent_rsrc(ws_lse + part0 * C::HB, static_cast<uint32_t>(splits * C::HB * 4));
     for (int i = threadIdx.x; i < splits * C::HB; i += C::THREADS)
-      st_w[i] = (i / C::HB == ks) ? st_lse[i % C::HB] : load_coherent1(rl, static_cast<uint32_t>(i * 4));
+      st_w[i] = (i / C::HB == ks) ? 0.f : load_coherent1(rl, static_cast<uint32_t>(i * 4));
   }
   __syncthreads();
-  if (threadIdx.x < C::HB) {
-    const int hd = threadIdx.x;
-    float m = neg_inf();
-    for (int s2 = 0; s2 < splits; ++s2) m = fmaxf(m, st_w[s2 * C::HB + hd]);
-    float wsum = 0.f;
-    for (int s2 = 0; s2 < splits; ++s2) {
-      const float w = (m == neg_inf()) ? 0.f : fast_exp2((st_w[s2 * C::HB + hd] - m) * kLog2e);
-      st_w[s2 * C::HB + hd] = w;
-      wsum += w;
-    }
-    if (a.lse != nullptr)
-      a.lse[static_cast<int64_t>(b) * a.hq + hb * C::HB + hd] =
-          (m == neg_inf()) ? neg_inf() : m + fast_log2(wsum) * kLn2;
-    st_lse[hd] = wsum > 0.f ? 1.f / wsum : 0.f;   // now the normaliser
-  }
-  __syncthreads();
-  f32x4 o[PASSES];
+  float M = neg_inf();
+  for (int s2 = 0; s2 < splits; ++s2) M = fmaxf(M, s2 == ks ? lse_val : st_w[s2 * C::HB + hd]);
+  float wsum = 0.f;
+  f32x4 o[16];
 #pragma unroll
-  for (int k = 0; k < PASSES; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s2 = 0; s2 < splits; ++s2) {
-    f32x4 v[PASSES];   // all loads in flight before the first use
-    if (s2 == ks) {
+  for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += BATCH) {
+    if (s0 > 0) load_batch(s0);
 #pragma unroll
-      for (int k = 0; k < PASSES; ++k) {
-        const int e = k * C::THREADS + static_cast<int>(threadIdx.x);
-        const f32x4 f = *reinterpret_cast<const f32x4*>(st_o + (e / F4_ROW) * SROW + 4 * (e % F4_ROW));
-        const uint32_t lo = pack_bf16x2(f[0], f[1]), hi = pack_bf16x2(f[2], f[3]);
-        v[k] = f32x4{bf16lo(lo), bf16hi(lo), bf16lo(hi), bf16hi(hi)};
+    for (int q = 0; q < BATCH; ++q) {
+      const int s2 = s0 + q;
+      if (s2 >= splits) break;
+      const float ls = s2 == ks ? lse_val : st_w[s2 * C::HB + hd];
+      const float wgt = (M == neg_inf()) ? 0.f : fast_exp2((ls - M) * kLog2e);
+      wsum += wgt;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const u32x2 v = (s2 == ks) ? own[i] : part[q][i];
+        o[i] += wgt * f32x4{bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y)};
       }
-    } else {
-      const auto ro = coherent_rsrc(ws_o + (part0 + s2) * C::HB * C::DV, kPartBytes);
-      u32x2 w2[PASSES];
-#pragma unroll
-      for (int k = 0; k < PASSES; ++k)
-        w2[k] = __builtin_bit_cast(u32x2,
-                                   load_coherent2(ro, static_cast<uint32_t>((k * C::THREADS + threadIdx.x) * 8)));
-#pragma unroll
-      for (int k = 0; k < PASSES; ++k)
-        v[k] = f32x4{bf16lo(w2[k].x), bf16hi(w2[k].x), bf16lo(w2[k].y), bf16hi(w2[k].y)};
-    }
-#pragma unroll
-    for (int k = 0; k < PASSES; ++k) {
-      const int e = k * C::THREADS + static_cast<int>(threadIdx.x);
-      o[k] += st_w[s2 * C::HB + e / F4_ROW] * v[k];
     }
   }
-  bf16_t* dst = static_cast<bf16_t*>(a.out) + (static_cast<int64_t>(b) * a.hq + hb * C::HB) * C::DV;
+  const float nrm = wsum > 0.f ? 1.f / wsum : 0.f;
+  bf16_t* dst = static_cast<bf16_t*>(a.out) + (static_cast<int64_t>(b) * a.hq + head) * C::DV +
+                C::DV_SLICE * w4;
 #pragma unroll
-  for (int k = 0; k < PASSES; ++k) {
-    const int e = k * C::THREADS + static_cast<int>(threadIdx.x);
-    const float nrm = st_lse[e / F4_ROW];
+  for (int i = 0; i < 16; ++i) {
     u32x2 w2;
-    w2.x = pack_bf16x2(o[k][0] * nrm, o[k][1] * nrm);
-    w2.y = pack_bf16x2(o[k][2] * nrm, o[k][3] * nrm);
-    *reinterpret_cast<u32x2*>(dst + 4 * e) = w2;
+    w2.x = pack_bf16x2(o[i][0] * nrm, o[i][1] * nrm);
+    w2.y = pack_bf16x2(o[i][2] * nrm, o[i][3] * nrm);
+    *reinterpret_cast<u32x2*>(dst + 4 * rho32(h, i)) = w2;
   }
+  if (a.lse != nullptr && w4 == 0 && h == 0)
+    a.lse[static_cast<int64_t>(b) * a.hq + head] =
+        (M == neg_inf()) ? neg_inf() : M + fast_log2(wsum) * kLn2;
   if (threadIdx.x == 0) counter_reset(&counter[unit]);   // ready for the next call
 }
 
