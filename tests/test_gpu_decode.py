@@ -201,3 +201,28 @@ def test_decode_is_deterministic_and_page_permutation_invariant():
     pt2, kl2 = gpu_strided_table(c2)
     d = gpu_decode(c2, pt2, kl2, c.kv_chunk, c.num_splits)
     assert torch.equal(a[0], d[0]) and torch.equal(a[1], d[1])
+
+
+@pytest.mark.parametrize("batch,dtype", [(63, torch.bfloat16), (64, torch.bfloat16),
+                                         (65, torch.bfloat16), (130, torch.bfloat16),
+                                         (64, torch.float32), (65, torch.float32)])
+def test_decode_split_order(batch, dtype):
+    """Workgroups take the (request, split) pairs longest first up to 64
+    requests (one per lane of the ordering wave) and in split-major order
+    above: lengths with empty requests, exact multiples of the chunk and
+    one spare split (empty for every request) must leave every partial
+    written and every value right on both sides of that bound."""
+    g = np.random.default_rng(batch)
+    chunk = 256
+    lens = g.integers(1, 3000, batch)
+    lens[::7] = 0
+    lens[3::11] = chunk * g.integers(1, 11, len(lens[3::11]))
+    lens = lens.tolist()
+    c = workloads.make_decode_case(900 + batch, seq_lens=lens, num_q_heads=8, num_kv_heads=2,
+                                   head_dim=128, page_size=16,
+                                   num_pages=sum(-(-s // 16) for s in lens) + batch + 3,
+                                   dtype=dtype, kv_chunk=chunk, ctx=max(lens))
+    c = to_device(c, DEV)
+    S = -(-max(lens) // chunk) + 1
+    say(f"split order batch={batch} {dtype} S={S}")
+    check_case(c, chunk, S, fp32=(dtype == torch.float32))
