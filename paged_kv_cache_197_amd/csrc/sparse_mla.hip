@@ -70,7 +70,8 @@ struct SparseCfg : SparseGeom {
   static constexpr int W = 4 * QUADS;            // waves
   static constexpr int THREADS = 64 * W;
   static constexpr int HB = 32 * QUADS;          // heads per workgroup
-  static constexpr int COPIES = (DMAS + 3) / 4;   // copies per tile of each copying wave
+  static constexpr int COPIES = (DMAS + W - 1) / W;   // most copies per tile of one wave
+  static constexpr int FULL_COPIERS = DMAS - (COPIES - 1) * W;   // waves issuing COPIES of them
   static constexpr int LDS_BYTES = NS * TILE + QUADS * QUAD_BYTES + MAX_KEYS_PER_SPLIT * 4;
   static_assert(LDS_BYTES <= 160 * 1024, "fits the CU's LDS");
 };
@@ -197,43 +198,40 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
   // ---- tile copies: copy i of a tile fills LDS bytes [1024 i, +1024) of the
   // stage, lane l the 16 bytes at o = 1024 i + 16 l: row o / 1168, chunk
   // (o % 1168) / 16 of the cache row. Lanes that land in a row's 16-byte pad
-  // or past the last row copy chunk 0 of row 31, which nothing reads. The
-  // copies are issued by the waves of the last quad (copy i by its wave i % 4),
-  // which spend the interval in which they are issued on the softmax. Skipped
-  // keys copy row 0 and are masked in the softmax / PV.
+  // or past the last row copy chunk 0 of row 31, which nothing reads. Every
+  // wave issues copies (copy i by wave i % W), so that the issue work, which
+  // sits between the two barriers of a tile, is spread over all of them; each
+  // wave's rows and row offsets are fixed and computed once. Skipped keys copy
+  // row 0 and are masked in the softmax / PV.
   const char* kvb = static_cast<const char*>(a.kv);
-  const bool copier = (quad == QUADS - 1);
+  uint32_t rowoff[C::COPIES];   // row (bits 16..) and byte offset in the cache row
+#pragma unroll
+  for (int k = 0; k < C::COPIES; ++k) {
+    const int i = min(wave + C::W * k, C::DMAS - 1);
+    const int o = 1024 * i + 16 * lane;
+    const int row = min(o / C::LROW, C::KT - 1);
+    const int cb = o - row * C::LROW;
+    rowoff[k] = (static_cast<uint32_t>(row) << 16) | static_cast<uint32_t>(cb < C::ROW ? cb : 0);
+  }
   auto issue_tile = [&](int t) {
     const uint32_t stage = lds0 + static_cast<uint32_t>((t % C::NS) * C::TILE);
-    // the addresses are cheap to recompute; an opaque lane offset keeps the
-    // compiler from hoisting all of them out of the loop into registers
-    int l16 = 16 * lane;
-    asm volatile("" : "+v"(l16));
     int32_t sl[C::COPIES];
-    uint32_t off[C::COPIES];
+#pragma unroll
+    for (int k = 0; k < C::COPIES; ++k) sl[k] = slots[t * C::KT + (rowoff[k] >> 16)];
 #pragma unroll
     for (int k = 0; k < C::COPIES; ++k) {
-      const int i = min(w4 + 4 * k, C::DMAS - 1);
-      const int o = 1024 * i + l16;
-      const int row = min(o / C::LROW, C::KT - 1);
-      const int cb = o - row * C::LROW;
-      off[k] = static_cast<uint32_t>(cb < C::ROW ? cb : 0);
-      sl[k] = slots[t * C::KT + row];
-    }
-#pragma unroll
-    for (int k = 0; k < C::COPIES; ++k) {
-      const int i = w4 + 4 * k;
+      const int i = wave + C::W * k;
       if (i < C::DMAS) {
         const uint32_t s = static_cast<uint32_t>(max(sl[k], 0));
-        lds_dma16(kvb + static_cast<uint64_t>(s) * C::ROW + off[k], stage + i * 1024);
+        lds_dma16(kvb + static_cast<uint64_t>(s) * C::ROW + (rowoff[k] & 0xffffu),
+                  stage + i * 1024);
       }
     }
   };
-  // copier waves: wait until only the newest tile's copies are in flight
+  // wait until only the newest tile's copies are in flight
   auto wait_newest_tile = [&]() {
-    static_assert(C::COPIES == 10 && C::DMAS == 37, "copy counts below");
-    if (w4 == 0) wait_vmem<10>();
-    else wait_vmem<9>();
+    if (wave < C::FULL_COPIERS) wait_vmem<C::COPIES>();
+    else wait_vmem<C::COPIES - 1>();
   };
   // bit k set: key k of tile t has a slot (the same mask in every wave)
   auto tile_valid = [&](int t) -> uint32_t {
@@ -386,14 +384,12 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
     }
   };
 
-  if (copier) {
-    if (n_tiles > 0) issue_tile(0);
-    if (n_tiles > 1) {
-      issue_tile(1);
-      wait_newest_tile();
-    } else {
-      wait_vmem<0>();
-    }
+  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 1) {
+    issue_tile(1);
+    wait_newest_tile();
+  } else {
+    wait_vmem<0>();
   }
   __syncthreads();   // tile 0 landed
   uint32_t valid_cur = 0xffffffffu;   // key mask of tile t
@@ -406,12 +402,10 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
     qk();
     __syncthreads();   // A: partials visible; every wave is done with tile t - 1
     const bool more = t + 2 < n_tiles;
-    if (copier && more) issue_tile(t + 2);
+    if (more) issue_tile(t + 2);
     softmax(valid_cur);
-    if (copier) {
-      if (more) wait_newest_tile();
-      else wait_vmem<0>();
-    }
+    if (more) wait_newest_tile();
+    else wait_vmem<0>();
     __syncthreads();   // B: P^T and rescale factors visible; tile t + 1 landed
     const uint32_t valid_pv = valid_cur;
     pv(t, valid_pv, t + 1 < n_tiles);
