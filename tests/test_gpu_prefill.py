@@ -157,12 +157,15 @@ def test_many_requests_ordered_by_length(causal):
 
 @pytest.mark.parametrize("D,P,group,causal", [
     (128, 1, 4, True), (128, 16, 2, True), (64, 1, 4, False), (64, 8, 1, True),
+    (128, 1, 8, True), (64, 4, 16, False),
 ])
 def test_one_group_workgroups(D, P, group, causal):
     """Launches with at least 1024 (q tile, kv head) units run workgroups of
     one group of four waves, each walking its q tile's whole key range (the
     smaller launches above halve it between two groups): ten requests with
-    ragged extends past 370 rows and prefixes, 8 kv heads, every row."""
+    ragged extends past 370 rows and prefixes, 8 kv heads, GQA groups of 1 to
+    16 (above 4 a workgroup runs its head blocks one after another), every
+    row."""
     g = np.random.default_rng(17 + D + P + group)
     B, hkv = 10, 8
     prefix = g.integers(0, 300, B).tolist()
