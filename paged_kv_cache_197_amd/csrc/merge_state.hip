@@ -41,6 +41,29 @@ __global__ __launch_bounds__(256) void merge_state_kernel(const float* __restric
   const int64_t row = idx / vecs_per_row;
   const int col = static_cast<int>(idx - row * vecs_per_row) * VEC;
 
+  // The parts' pieces are requested eight at a time, all in flight before
+  // the first is used, and the first eight go out before the LSEs, so that
+  // both arrive in one round trip. A part of zero weight (an empty split, or
+  // one far below the max) adds nothing, whatever its output holds.
+  constexpr int BATCH = 8;
+  float v[BATCH][VEC];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int s = min(s0 + k, num_parts - 1);
+      const float* src = o_parts + (s * rows + row) * dv + col;
+      if (VEC == 4) {
+        const float4 q = *reinterpret_cast<const float4*>(src);
+        v[k][0] = q.x;
+        v[k][1 % VEC] = q.y;
+        v[k][2 % VEC] = q.z;
+        v[k][3 % VEC] = q.w;
+      } else {
+        v[k][0] = src[0];
+      }
+    }
+  };
+  load_batch(0);
   float m = neg_inf();
   for (int s = 0; s < num_parts; ++s) m = fmaxf(m, lse_parts[s * rows + row]);
 
@@ -49,19 +72,17 @@ __global__ __launch_bounds__(256) void merge_state_kernel(const float* __restric
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
   float total = 0.f;
   if (m != neg_inf()) {
-    for (int s = 0; s < num_parts; ++s) {
-      const float w = fast_exp2((lse_parts[s * rows + row] - m) * kLog2e);
-      if (w == 0.f) continue;  // a part with no weight contributes nothing
-      total += w;
-      const float* src = o_parts + (s * rows + row) * dv + col;
-      if (VEC == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src);
-        acc[0] += w * v.x;
-        acc[1 % VEC] += w * v.y;
-        acc[2 % VEC] += w * v.z;
-        acc[3 % VEC] += w * v.w;
-      } else {
-        acc[0] += w * src[0];
+    for (int s0 = 0; s0 < num_parts; s0 += BATCH) {
+      if (s0 > 0) load_batch(s0);
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const int s = min(s0 + k, num_parts - 1);
+        const float w =
+            (s0 + k < num_parts) ? fast_exp2((lse_parts[s * rows + row] - m) * kLog2e) : 0.f;
+        if (w == 0.f) continue;
+        total += w;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] += w * v[k][i];
       }
     }
   }
