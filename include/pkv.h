@@ -234,7 +234,8 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
  * (this is its S-way form):
  *   m = max_s lse[s], w_s = exp(lse[s] - m),
  *   out = sum_s w_s o[s] / sum_s w_s, lse_out = m + ln(sum_s w_s);
- *   m == -inf gives (0, -inf).
+ *   m == -inf gives (0, -inf). A part with lse -inf (an empty split) adds
+ *   nothing, whatever its o holds (NaN included).
  * o_parts [num_parts, n_tokens, num_heads, head_dim_v] fp32;
  * lse_parts [num_parts, n_tokens, num_heads] fp32;
  * out [n_tokens, num_heads, head_dim_v] of out_dtype (out);

@@ -58,3 +58,19 @@ def test_merge_two_way_matches_page_formula():
     l0, l1 = lse[0].double(), lse[1].double()
     ref = torch.maximum(l0, l1) + torch.log1p(torch.exp(-(l0 - l1).abs()))
     assert_close("lse", np_f(lse_out), ref.numpy(), 1e-5)
+
+
+def test_merge_ignores_output_of_empty_parts():
+    """Parts with LSE -inf add nothing, whatever their output holds: NaN there
+    must not reach the result (11 parts: a batch of eight loads and a partial
+    one)."""
+    say("merge empty parts holding NaN")
+    S, N, H, Dv = 11, 9, 4, 64
+    o, lse = random_parts(4242, S, N, H, Dv, p_neg_inf=0.4)
+    o_gpu = o.clone()
+    o_gpu[torch.isneginf(lse)] = float("nan")
+    out, lse_out = pkv.merge_state(o_gpu.to(DEV), lse.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge_state(o.double().numpy(), lse.double().numpy())
+    assert_close("out", np_f(out), ro, 1e-5)
+    assert_close("lse", np_f(lse_out), rl, 1e-5)
