@@ -79,6 +79,26 @@ class Timer:
     def kernel_ms(self):
         return sum(a.elapsed_time(b) for a, b in self.pairs) / max(len(self.pairs), 1)
 
+    def kernel_ms_median(self):
+        t = sorted(a.elapsed_time(b) for a, b in self.pairs)
+        if not t:
+            return 0.0
+        n = len(t)
+        return t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+
+
+def kernel_median(torch, step, launches=50, warmup=10):
+    """Median HIP-event duration of the event-bracketed kernel over `launches`
+    launches after `warmup` untimed steps (steps enqueued back to back)."""
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    for _ in range(launches):
+        step(timer)
+    torch.cuda.synchronize()
+    return timer.kernel_ms_median(), len(timer.pairs)
+
 
 def timed_loop(torch, step, steps, warmup):
     """W untimed steps, then exactly K timed steps between synchronisations.
@@ -190,8 +210,9 @@ def run_decode(torch, pkv, workloads, args, window_left=-1, kv_chunk=None):
     else:
         ms, kern_ms = timed_loop(torch, step, args.steps, args.warmup)
         nbytes, sum_l = decode_bytes(c.seq_lens.long(), B, hq, hkv, d, P)
-    res = dict(ms=ms, kernel_ms=kern_ms, bytes=nbytes, sum_l=sum_l, batch=B, splits=S,
-               case=c, chunk=chunk)
+    med_ms, n_med = kernel_median(torch, step)
+    res = dict(ms=ms, kernel_ms=kern_ms, kernel_ms_median=med_ms, median_launches=n_med,
+               bytes=nbytes, sum_l=sum_l, batch=B, splits=S, case=c, chunk=chunk)
     return res
 
 
@@ -491,10 +512,15 @@ def cpu_baseline_decode(torch, res, budget_s):
             break
     cores = len(os.sched_getaffinity(0))
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s",
-            "cores": blas_threads, "kind": "oracle",
+            "cores": cores, "blas_threads": blas_threads, "kind": "oracle",
             "sample": f"config3 requests 0..{n_req - 1} ({n_req} of {B}, {sum_l} keys, all "
-                      f"{hq} heads, {c.num_splits} splits + merge), float64 numpy; "
-                      f"{spent:.1f} s on a host with {cores} cores available"}
+                      f"{hq} heads, {c.num_splits} splits + merge), float64 numpy with "
+                      f"{blas_threads} BLAS threads; {spent:.1f} s"}
+
+
+def _core_fields():
+    """Host cores this process may run on, and the BLAS threads the oracle used."""
+    return {"cores": len(os.sched_getaffinity(0)), "blas_threads": _blas_threads()}
 
 
 def _blas_threads():
@@ -524,7 +550,7 @@ def cpu_oracle_prefill(torch, r):
         spent += time.perf_counter() - t0
         M = q1 - q0
         flops += 4 * c.q.shape[2] * c.q.shape[1] * sum(L - M + j + 1 for j in range(M))
-    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(),
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", **_core_fields(),
             "kind": "oracle", "sample": f"all {len(kl)} requests of config2, float64 numpy; "
                                         f"{spent:.1f} s"}
 
@@ -552,7 +578,7 @@ def cpu_oracle_swa(torch, r, budget_s):
         n += 1
         if spent >= budget_s:
             break
-    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", **_core_fields(),
             "kind": "oracle", "sample": f"config4 requests 0..{n - 1} ({n} of {len(kl)}), float64 "
                                         f"numpy; {spent:.1f} s"}
 
@@ -588,7 +614,7 @@ def cpu_oracle_decode_window(torch, r, window_left, budget_s):
         done += 1
         if spent >= budget_s:
             break
-    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", **_core_fields(),
             "kind": "oracle", "sample": f"config3 requests 0..{done - 1} ({done} of "
                                         f"{len(kl_all)}) under the window, float64 numpy; "
                                         f"{spent:.1f} s"}
@@ -612,7 +638,7 @@ def cpu_oracle_prefill_window(torch, r, window_left, rows):
     spent = time.perf_counter() - t0
     flops = 4 * c.q.shape[2] * c.q.shape[1] * sum(min(L - rows + j + 1, window_left + 1)
                                                   for j in range(rows))
-    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(),
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", **_core_fields(),
             "kind": "oracle", "sample": f"the last {rows} new tokens of prompt 0 ({L} keys) under "
                                         f"the window, float64 numpy; {spent:.1f} s"}
 
@@ -638,7 +664,7 @@ def cpu_oracle_prefill_append(torch, r):
                                     np.array([L]), 1, c.scale, loc, kn[q0:q1], vn[q0:q1])
         spent += time.perf_counter() - t0
     return {"value": round(r["flops"] / spent / 1e12, 6), "unit": "TFLOP/s",
-            "cores": _blas_threads(), "kind": "oracle",
+            **_core_fields(), "kind": "oracle",
             "sample": f"all {len(kl)} requests of config2 (append + extend), float64 numpy; "
                       f"{spent:.1f} s"}
 
@@ -673,7 +699,7 @@ def cpu_oracle_cascade(torch, r, budget_s):
         done += 1
         if spent >= budget_s:
             break
-    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", **_core_fields(),
             "kind": "oracle", "sample": f"draft-tree workload requests 0..{done - 1} ({done} of "
                                         f"{len(sl)}), plain tree attention, float64 numpy; "
                                         f"{spent:.1f} s"}
@@ -707,7 +733,7 @@ def cpu_oracle_dca(torch, r, budget_s):
         done += 1
         if spent >= budget_s:
             break
-    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", **_core_fields(),
             "kind": "oracle", "sample": f"dual chunk decode requests 0..{done - 1} ({done} of "
                                         f"{len(kl)}), three stages + merge, float64 numpy; "
                                         f"{spent:.1f} s"}
@@ -738,7 +764,7 @@ def cpu_oracle_sparse(torch, r, budget_s):
         n += 1
         if spent >= budget_s:
             break
-    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", **_core_fields(),
             "kind": "oracle", "sample": f"config5 requests 0..{n - 1} ({n} of {idx.shape[0]}), "
                                         f"float64 numpy; {spent:.1f} s"}
 
@@ -813,6 +839,8 @@ def main(argv=None):
                 "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "kernel_ms": round(r["kernel_ms"], 4),
+                "kernel_ms_median": round(r["kernel_ms_median"], 4),
+                "median_launches": r["median_launches"],
                 "traffic": stored_traffic("decode_config3", src),
                 "source_hash": src,
             },

@@ -31,6 +31,8 @@
  *     O = 0 and LSE = -inf ([DCA] _dual_chunk_flash_attn_decoding_with_exp_sums).
  *   - LSE arrays are token-major [tokens, heads] ([FA] forward_extend passes
  *     softmax_lse.T.contiguous() to merge_state_v2).
+ *   - softmax_scale must be finite and > 0 (the pages pass 1/sqrt(head dim));
+ *     every attention entry point returns PKV_EINVAL otherwise.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -51,6 +53,20 @@ typedef enum {
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype_t;
 
+/*
+ * Workspaces (paged_attn_varlen_prefill[_append], paged_attn_cascade,
+ * sparse_topk_decode). A workspace starts with PKV_WORKSPACE_COUNTER_BYTES
+ * bytes of completion counters at a fixed place that does not depend on the
+ * call's shape; the per-split partial results follow them. Hence one buffer,
+ * at least as large as the size function returns for each shape, serves
+ * calls of any shape in any order. Before its first use the counter region
+ * must be zero (any fill on the stream: hipMemsetAsync, torch.zero_); every
+ * launch that runs to completion leaves it zero again. A call that returns an
+ * error has enqueued nothing and has left it as it was. Calls that share a
+ * workspace must be ordered (one stream, or synchronised).
+ */
+#define PKV_WORKSPACE_COUNTER_BYTES 65536
+
 /* Static string naming a status code. */
 const char* pkv_status_string(int status);
 
@@ -61,7 +77,7 @@ const char* pkv_last_error(void);
  * build_page_table -- integer metadata for one forward pass.
  *
  * Strided mode (prefill_lens == NULL), [FA] init_forward_metadata (decode and
- * extend branches, "strided format" conversion); [DCA] init_forward_metadata:
+ * extend branches, token slots reduced to page ids); [DCA] init_forward_metadata:
  *   page_table[b, p] = req_to_token[r, p * page_size] / page_size
  *       for p < ceil(L_b / page_size), else 0,   r = req_pool_indices[b],
  *   kv_lens[b] = L_b = seq_lens[b].
@@ -119,9 +135,8 @@ pkv_status_t build_page_table(const int32_t* req_to_token, int64_t req_to_token_
  *          (A max_seqlen_k below some L_b is still correct, only slower.)
  * workspace caller-owned device memory of at least
  *          paged_attn_varlen_prefill_workspace_size(...) bytes (0 when no q
- *          tile is split: NULL allowed). Its first bytes are counters that
- *          must be zero before the first call; every call leaves them zero.
- *          Calls sharing a workspace must not overlap in time.
+ *          tile is split: NULL allowed); layout and zeroing rule as stated at
+ *          PKV_WORKSPACE_COUNTER_BYTES.
  * out      [total_q, num_q_heads, head_dim] dtype (out); lse [total_q, num_q_heads]
  *          fp32 (out) or NULL.
  * Supported: dtype PKV_BF16, head_dim 64 or 128, Hq % Hkv == 0,
@@ -263,12 +278,10 @@ pkv_status_t merge_state(const float* o_parts, const float* lse_parts, int32_t n
  * req_to_token [req_to_token_rows, req_to_token_stride] int32
  * topk_idx [batch, topk] int32 logical indices in [0, stride) or -1
  * workspace: device scratch of at least sparse_topk_decode_workspace_size(...)
- *          bytes (may be NULL when that size is 0). It holds per-split partial
- *          results and one completion counter per (request, head block; a head
- *          block is 64 heads when num_q_heads is a multiple of 64, else 32): it
- *          must be zero-filled before its first use, and every call that
- *          returns PKV_OK leaves the counters zero again. Calls sharing one
- *          workspace must not overlap in time (same stream, or synchronised).
+ *          bytes (may be NULL when that size is 0): one completion counter
+ *          per (request, head block) in the counter region, then per-split
+ *          partial results; layout and zeroing rule as stated at
+ *          PKV_WORKSPACE_COUNTER_BYTES.
  * out      [batch, num_q_heads, head_dim_v] bf16 (out); lse [batch, num_q_heads]
  *          fp32 (out) or NULL.
  * Supported: head_dim_qk 576, head_dim_v 512, num_q_heads a multiple of 32,
@@ -293,12 +306,12 @@ pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num
  *   lens_intra = L - c * chunk_len, table_intra row = block_tables row from
  *     page c * chunk_len / page_size;
  *   lens_succ = chunk_len if c >= 1 else 0, table_succ row from page
- *     max(c - 1, 0) * chunk_len / page_size;
+ *     (c - 1) * chunk_len / page_size (all 0 when c = 0);
  *   lens_inter = max(c - 1, 0) * chunk_len (read through the request's own row);
  *   scaling_factor = max(0.1 * ln(L / original_max_position_embeddings) + 1, 1)
  *     when original_max_position_embeddings > 0, else 1.
  * Table rows hold chunk_len / page_size entries (the widest the pages' tables
- * can be); entries past the request's last page, (L - 1) / page_size, are 0.
+ * can be): the pages that hold their stage's keys, in order, then 0.
  *
  * block_tables [batch, bt_stride] int32 page ids (the strided page table)
  * table_intra, table_succ [batch, chunk_len / page_size] int32 (out; table_succ

@@ -40,7 +40,6 @@ from .reference import (  # noqa: F401
     kv_head_of,
     merge_state,
     page_table_pa_swa,
-    page_table_pa_swa_bruteforce,
     page_table_strided,
     paged_decode_splitkv,
     paged_prefill,

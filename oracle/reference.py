@@ -45,10 +45,10 @@ def cu_seqlens(lens) -> np.ndarray:
 def page_table_strided(req_to_token, req_pool_indices, seq_lens, page_size, width):
     """Token-level ``req_to_token`` rows -> page table of page ids.
 
-    [FA] ``init_forward_metadata``: the row ``req_to_token[req_pool_indices[b]]``
-    is taken, then "converted to a strided format": every ``page_size``-th
-    column, integer-divided by ``page_size``. [DCA] ``init_forward_metadata``
-    does the same for ``block_tables``. Columns past ``ceil(L_b / page_size)``
+    [FA] ``init_forward_metadata``: the request's ``req_to_token`` row is
+    reduced to one entry per page -- the slot of the page's first token,
+    integer-divided by ``page_size``, which is the page id. [DCA]
+    ``init_forward_metadata`` builds ``block_tables`` the same way. Columns past ``ceil(L_b / page_size)``
     are 0. ``kv_lens`` is ``seq_lens`` as int32 and ``cu_seqlens_k`` its
     zero-led prefix sum (``cache_seqlens_int32`` / ``cu_seqlens_k``).
     """
@@ -67,45 +67,16 @@ def page_table_strided(req_to_token, req_pool_indices, seq_lens, page_size, widt
 
 
 def page_table_pa_swa(req_to_token, req_pool_indices, seq_lens, prefill_lens, window, width):
-    """Prefill-aware sliding-window token table, by the formula on the page.
+    """Prefill-aware sliding-window token table, by set construction.
 
-    [FA] ``_build_pa_page_table_kernel`` and its wrapper ``_build_pa_page_table``:
-    per request, ``pf`` is read from the pool-sized ``prefill_lens`` through the
-    request's pool row; ``decode_start = max(pf, sl - window)``;
-    ``gap = decode_start - pf`` if positive, else 0; ``kv_len = sl - gap``;
-    destination column ``j < kv_len`` takes ``req_to_token[row, j]`` when
-    ``j < pf`` and ``req_to_token[row, j + gap]`` otherwise. The destination
-    buffer starts zeroed, so columns ``>= kv_len`` are 0.
-    """
-    req_to_token = np.asarray(req_to_token)
-    rpi = np.asarray(req_pool_indices)
-    seq_lens = np.asarray(seq_lens)
-    prefill_lens = np.asarray(prefill_lens)
-    batch = len(rpi)
-    pt = np.zeros((batch, width), dtype=np.int32)
-    kv_lens = np.zeros(batch, dtype=np.int32)
-    for b in range(batch):
-        r = int(rpi[b])
-        sl = int(seq_lens[b])
-        pf = int(prefill_lens[r])
-        decode_start = max(pf, sl - window)
-        gap = decode_start - pf if decode_start > pf else 0
-        kv_len = sl - gap
-        kv_lens[b] = kv_len
-        for j in range(kv_len):
-            pos = j if j < pf else j + gap
-            pt[b, j] = int(req_to_token[r, pos])
-    return pt, kv_lens, cu_seqlens(kv_lens)
-
-
-def page_table_pa_swa_bruteforce(req_to_token, req_pool_indices, seq_lens, prefill_lens,
-                                 window, width):
-    """The same table by set construction, from the kernel's docstring alone.
-
-    [FA] ``_build_pa_page_table_kernel`` docstring: the row is the tokens of
-    ``[0, prefill_len)`` together with ``[decode_start, seq_len)``, in increasing
-    order, ``decode_start = max(prefill_len, seq_len - window)``. Tokens are
-    limited to the ``seq_len`` tokens that exist.
+    [FA] ``_build_pa_page_table_kernel`` / ``_build_pa_page_table`` (the
+    kernel's description of what it keeps): request b keeps its prompt
+    positions ``[0, pf)`` and the newest decoded positions
+    ``[max(pf, sl - window), sl)``, where ``pf`` is read from the pool-sized
+    ``prefill_lens`` at the request's pool row and ``sl = seq_lens[b]``. Only
+    positions below ``sl`` exist. The kept positions, in increasing order,
+    are mapped through the request's ``req_to_token`` row; ``kv_lens`` is
+    their count and the rest of the row is 0 (the destination starts zeroed).
     """
     req_to_token = np.asarray(req_to_token)
     batch = len(req_pool_indices)
@@ -115,9 +86,9 @@ def page_table_pa_swa_bruteforce(req_to_token, req_pool_indices, seq_lens, prefi
         r = int(req_pool_indices[b])
         sl = int(seq_lens[b])
         pf = int(prefill_lens[r])
-        decode_start = max(pf, sl - window)
-        keep = set(range(0, pf)) | set(range(decode_start, sl))
-        keep = sorted(t for t in keep if t < sl)
+        prompt = set(range(0, pf))
+        recent = set(range(max(pf, sl - window), sl))
+        keep = sorted(t for t in prompt | recent if t < sl)
         kv_lens[b] = len(keep)
         for j, t in enumerate(keep):
             pt[b, j] = int(req_to_token[r, t])
@@ -542,45 +513,52 @@ def dca_query_chunk(seq_lens, chunk_len) -> np.ndarray:
 
 
 def dca_decode_tables(block_tables, seq_lens, chunk_size, local_size, page_size):
-    """Per-request key ranges and page tables of the three decode stages.
+    """Per-request key ranges of the three decode stages and the page tables
+    that read them.
 
-    [DCA] ``init_forward_metadata`` (decode): ``chunk_len = chunk_size -
-    local_size``, ``c = (L - 1) // chunk_len`` (the chunk holding the query);
-    intra: keys ``[c*chunk_len, L)``, table ``block_tables[b, st:ed]`` from
-    ``st = c*chunk_len // P`` up to ``(L - 1) // P + 1``; succ: ``chunk_len``
-    keys (0 when ``c = 0``) from page ``max(c - 1, 0)*chunk_len // P``; inter:
-    ``max(c - 1, 0)*chunk_len`` keys from key 0 through the full table. Table
-    widths follow the page: ``(max length - 1) // P + 1`` columns, zero past a
-    row's pages; the succ table exists only when some request has succ keys.
+    [DCA] ``init_forward_metadata`` (decode) and
+    ``_dual_chunk_flash_attn_decoding``: with chunk length
+    ``C = chunk_size - local_size`` and ``c = (L - 1) // C`` the chunk that
+    holds the query (a request of length 0 counts as chunk 0), the stages
+    read these key positions of the request:
+      intra -- the query's own chunk, ``[c*C, L)``;
+      succ  -- the whole chunk before it, ``[(c-1)*C, c*C)``, none when c = 0;
+      inter -- everything earlier, ``[0, (c-1)*C)``, read through the
+               request's own ``block_tables`` row.
+    A stage's table row lists the pages that hold its positions, in order,
+    taken from the request's ``block_tables`` row, and is 0 after them; rows
+    are ``C // page_size`` wide (a stage never spans more than one chunk).
+    Positions start at multiples of ``C``, a multiple of ``page_size``, so a
+    stage's first position is the first slot of its first page.
 
-    Returns dict(lens_intra, table_intra, lens_succ, table_succ or None,
-    lens_inter), int64 arrays.
+    Returns dict(lens_intra, table_intra, lens_succ, table_succ, lens_inter),
+    int64 arrays.
     """
     bt = np.asarray(block_tables, dtype=np.int64)
-    L = np.asarray(seq_lens, dtype=np.int64)
-    batch = len(L)
-    chunk_len = int(chunk_size) - int(local_size)
+    L_all = np.asarray(seq_lens, dtype=np.int64)
+    batch = len(L_all)
+    C = int(chunk_size) - int(local_size)
     P = int(page_size)
-    c = dca_query_chunk(L, chunk_len)
-    lens_intra = L - c * chunk_len
-    w = (int(lens_intra.max()) - 1) // P + 1
-    table_intra = np.zeros((batch, w), dtype=np.int64)
-    for i in range(batch):
-        st = int(c[i]) * chunk_len // P
-        ed = min(st + w, (int(L[i]) - 1) // P + 1)
-        table_intra[i, :ed - st] = bt[i, st:ed]
-    lens_succ = (c - np.maximum(c - 1, 0)) * chunk_len
-    table_succ = None
-    if int(lens_succ.max()) > 0:
-        ws = (int(lens_succ.max()) - 1) // P + 1
-        table_succ = np.zeros((batch, ws), dtype=np.int64)
-        for i in range(batch):
-            st = int(max(c[i] - 1, 0)) * chunk_len // P
-            ed = min(st + ws, (int(L[i]) - 1) // P + 1)
-            table_succ[i, :ed - st] = bt[i, st:ed]
-    lens_inter = np.maximum(c - 1, 0) * chunk_len
-    return dict(lens_intra=lens_intra, table_intra=table_intra, lens_succ=lens_succ,
-                table_succ=table_succ, lens_inter=lens_inter)
+    assert C % P == 0, "chunk length must be a multiple of the page size"
+    width = C // P
+    tables = {"intra": np.zeros((batch, width), dtype=np.int64),
+              "succ": np.zeros((batch, width), dtype=np.int64)}
+    lens = {k: np.zeros(batch, dtype=np.int64) for k in ("intra", "succ", "inter")}
+    for b in range(batch):
+        L = int(L_all[b])
+        c = max(int(dca_query_chunk([L], C)[0]), 0)
+        ranges = {"intra": range(c * C, L),
+                  "succ": range((c - 1) * C, c * C) if c >= 1 else range(0),
+                  "inter": range(0, max(c - 1, 0) * C)}
+        for name, positions in ranges.items():
+            lens[name][b] = len(positions)
+            if name == "inter":
+                continue
+            pages = sorted({t // P for t in positions})
+            for j, page in enumerate(pages):
+                tables[name][b, j] = bt[b, page]
+    return dict(lens_intra=lens["intra"], table_intra=tables["intra"], lens_succ=lens["succ"],
+                table_succ=tables["succ"], lens_inter=lens["inter"])
 
 
 def dca_decode(q, q_succ, q_inter, k_cache, v_cache, block_tables, seq_lens, page_size, scale,
@@ -609,7 +587,7 @@ def dca_decode(q, q_succ, q_inter, k_cache, v_cache, block_tables, seq_lens, pag
                                  page_size, scale, 0, 1)
     parts_o.append(o[0])
     parts_l.append(l_[0])
-    if t["table_succ"] is not None:
+    if int(t["lens_succ"].max()) > 0:
         o, l_ = paged_decode_splitkv(qs[1], k_cache, v_cache, t["table_succ"], t["lens_succ"],
                                      page_size, scale, 0, 1)
         parts_o.append(o[0])

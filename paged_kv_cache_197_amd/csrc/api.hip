@@ -40,6 +40,13 @@ static int32_t log2_if_pow2(int32_t v) {
   return k;
 }
 
+// softmax_scale must be finite and positive: the kernels keep their running
+// maxima in raw score units and apply the scale inside the exponent, which
+// orders scores correctly only for a positive scale
+static bool scale_ok(float softmax_scale) {
+  return softmax_scale > 0.f && softmax_scale <= 3.402823466e38f;
+}
+
 static float scale_log2(float softmax_scale) {
   return static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
 }
@@ -48,8 +55,8 @@ static float scale_log2(float softmax_scale) {
 // one (q tile, kv head); when there are fewer such units than half the CUs,
 // the 32-key tiles a q tile sees are cut into splits of split_tiles tiles so
 // that about kPrefillWorkgroups workgroups run, never below kMinSplitTiles
-// tiles per split. The workspace holds the split counters (zero between
-// calls), then the partial LSEs and outputs.
+// tiles per split. The workspace holds the split counters (in its fixed
+// counter region, zero between calls), then the partial LSEs and outputs.
 // Largest draft count per request of the cascade expand table (a wave holds a
 // request's draft columns, four per lane).
 constexpr int32_t kMaxDraft = 256;
@@ -64,6 +71,7 @@ constexpr int64_t kOneGroupUnits = 1024;
 
 struct PrefillPlan {
   int32_t split_tiles, max_splits, qtile_slots, groups;
+  int64_t counters;
   size_t counter_bytes, lse_bytes, o_bytes, bytes;
 };
 
@@ -86,6 +94,7 @@ static PrefillPlan prefill_plan(int64_t batch, int64_t total_q, int64_t max_seql
   p.split_tiles = static_cast<int32_t>(std::min<int64_t>(tiles, 1 << 30));
   p.max_splits = static_cast<int32_t>((n_kt + p.split_tiles - 1) / p.split_tiles);
   p.counter_bytes = p.lse_bytes = p.o_bytes = p.bytes = 0;
+  p.counters = 0;
   p.groups = 2;
   if (p.max_splits <= 1) {
     p.max_splits = 1;
@@ -93,7 +102,12 @@ static PrefillPlan prefill_plan(int64_t batch, int64_t total_q, int64_t max_seql
     return p;
   }
   const int64_t n_hb = (hq / hkv + 3) / 4;
-  p.counter_bytes = round_up256(static_cast<size_t>(p.qtile_slots * hkv * n_hb) * 4);
+  // counters: one per (q-tile slot, kv head, head block), in the fixed region
+  // at the start of the workspace. Splits are planned only below
+  // kPrefillWorkgroups / 2 units, which keeps them far below its capacity
+  // (at most 2 * 127 slot-heads x 4 head blocks); prefill_prepare checks it.
+  p.counters = p.qtile_slots * hkv * n_hb;
+  p.counter_bytes = PKV_WORKSPACE_COUNTER_BYTES;
   // one block of 32 rows per (split, q-tile slot, head)
   const size_t blocks = static_cast<size_t>(p.max_splits) * p.qtile_slots * hq;
   p.lse_bytes = round_up256(blocks * 32 * 4);
@@ -137,6 +151,8 @@ static pkv_status_t decode_impl(const void* q, const void* q_succ, const void* q
   PKV_REQUIRE(window_left >= -1 && attn_chunk >= 0 && !(window_left >= 0 && attn_chunk > 0),
               PKV_EINVAL, "decode: window_left %d / attn_chunk %d (at most one of them)",
               window_left, attn_chunk);
+  PKV_REQUIRE(pkv_host::scale_ok(softmax_scale), PKV_EINVAL,
+              "decode: softmax_scale %g is not finite and positive", softmax_scale);
   PKV_REQUIRE(kv_chunk >= 0, PKV_EINVAL, "decode: kv_chunk %d < 0", kv_chunk);
   PKV_REQUIRE(kv_chunk % page_size == 0, PKV_EINVAL,
               "decode: kv_chunk %d is not a multiple of page_size %d", kv_chunk, page_size);
@@ -359,6 +375,8 @@ static pkv_status_t prefill_prepare(const void* q, int32_t dtype, const void* k_
               "prefill: a sliding window or local chunks need causal rows");
   PKV_REQUIRE(max_seqlen_q <= total_q, PKV_EINVAL, "prefill: max_seqlen_q %d > total_q %d",
               max_seqlen_q, total_q);
+  PKV_REQUIRE(pkv_host::scale_ok(softmax_scale), PKV_EINVAL,
+              "prefill: softmax_scale %g is not finite and positive", softmax_scale);
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) {
     *nothing = true;
     return pkv_host::ok();
@@ -367,6 +385,9 @@ static pkv_status_t prefill_prepare(const void* q, int32_t dtype, const void* k_
               PKV_EINVAL, "prefill: NULL required pointer");
   const pkv_host::PrefillPlan plan = pkv_host::prefill_plan(
       batch, total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim);
+  PKV_REQUIRE(plan.counters * 4 <= PKV_WORKSPACE_COUNTER_BYTES, PKV_EUNSUPPORTED,
+              "prefill: %lld split counters exceed the workspace's counter region",
+              (long long)plan.counters);
   PKV_REQUIRE(plan.bytes == 0 || (workspace != nullptr && workspace_bytes >= plan.bytes),
               PKV_EINVAL, "prefill: workspace of %zu bytes, need %zu", workspace_bytes,
               plan.bytes);
@@ -515,12 +536,19 @@ pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num
               "sparse_topk_decode: num_q_heads %d not a multiple of 32", num_q_heads);
   PKV_REQUIRE(topk <= 131072, PKV_EUNSUPPORTED,
               "sparse_topk_decode: topk %d above 131072 (64 key splits of 2048)", topk);
+  PKV_REQUIRE(pkv_host::scale_ok(softmax_scale), PKV_EINVAL,
+              "sparse_topk_decode: softmax_scale %g is not finite and positive", softmax_scale);
   if (batch == 0) return pkv_host::ok();
   PKV_REQUIRE(q && kv_cache && req_to_token && req_pool_indices && out, PKV_EINVAL,
               "sparse_topk_decode: NULL required pointer");
   PKV_REQUIRE(topk == 0 || topk_idx != nullptr, PKV_EINVAL, "sparse_topk_decode: NULL topk_idx");
   PKV_REQUIRE(num_slots >= 1 && req_to_token_rows >= 1 && req_to_token_stride >= 1, PKV_EINVAL,
               "sparse_topk_decode: empty cache or token table");
+  PKV_REQUIRE(pkv_launch::sparse_counters(batch, topk, num_q_heads) * 4 <=
+                  PKV_WORKSPACE_COUNTER_BYTES,
+              PKV_EUNSUPPORTED,
+              "sparse_topk_decode: batch %d needs more split counters than the workspace's "
+              "counter region holds", batch);
   const size_t need = sparse_topk_decode_workspace_size(batch, topk, num_q_heads, head_dim_v);
   PKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr), PKV_EINVAL,
               "sparse_topk_decode: workspace of %zu bytes, need %zu", workspace_bytes, need);
@@ -642,6 +670,8 @@ static pkv_status_t expand_merge_prepare(const char* who, const void* q, int32_t
                               lse),
               PKV_EINVAL, "%s: NULL required pointer (out and lse are both needed)", who);
   PKV_REQUIRE(n_rows == 0 || num_slots >= 1, PKV_EINVAL, "%s: empty cache", who);
+  PKV_REQUIRE(pkv_host::scale_ok(softmax_scale), PKV_EINVAL,
+              "%s: softmax_scale %g is not finite and positive", who, softmax_scale);
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;

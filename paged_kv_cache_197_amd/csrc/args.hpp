@@ -82,7 +82,7 @@ struct PrefillArgs {
   int32_t groups;       // groups of four waves per workgroup (1 or 2)
   float* ws_o;          // [max_splits, qtile_slots, Hq] blocks of 32 rows x D partial outputs
   float* ws_lse;        // [max_splits, qtile_slots, Hq, 32] partial LSEs (max_splits > 1)
-  int32_t* counters;    // [qtile_slots, Hkv, ceil(G / 4)], zero between calls
+  int32_t* counters;    // [qtile_slots, Hkv, ceil(G / 4)] in the workspace's counter region
   void* out;
   float* lse;
   int32_t window_left;  // >= 0: sliding window (W, 0); else none (causal only)

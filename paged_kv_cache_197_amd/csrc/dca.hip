@@ -2,11 +2,11 @@
 // decode ([DCA] init_forward_metadata, decode branch). With chunk_len C and
 // the query's chunk c = (L - 1) / C:
 //   intra: keys [cC, L), table = the request's page-table row from page cC / P
-//   succ:  C keys (0 when c = 0), table from page max(c - 1, 0) C / P
+//   succ:  keys [(c - 1)C, cC) (none when c = 0), table from page (c - 1) C / P
 //   inter: max(c - 1, 0) C keys from key 0 (the request's own row)
 // and, when original_max_position_embeddings > 0, the query scaling factor
 // max(0.1 ln(L / original_max_position_embeddings) + 1, 1). Table rows are
-// C / P columns wide; entries past the request's last page are 0.
+// C / P columns wide and list the pages of their stage's keys, then 0.
 //
 // Integer gather, one thread per (request, column) for both tables.
 #include "args.hpp"
@@ -29,8 +29,9 @@ __global__ __launch_bounds__(256) void dca_tables_kernel(DcaTableArgs a) {
     const int64_t i_intra = static_cast<int64_t>(c) * C / a.page_size + col;
     a.table_intra[out] = i_intra < last_page ? row[min(i_intra, last_col)] : 0;
     if (a.table_succ != nullptr) {
-      const int64_t i_succ = static_cast<int64_t>(max(c - 1, 0)) * C / a.page_size + col;
-      a.table_succ[out] = i_succ < last_page ? row[min(i_succ, last_col)] : 0;
+      // c >= 1: the C / P pages of the chunk before the query's, all held
+      const int64_t i_succ = static_cast<int64_t>(c - 1) * C / a.page_size + col;
+      a.table_succ[out] = (c >= 1 && i_succ < last_page) ? row[min(i_succ, last_col)] : 0;
     }
   }
   if (blockIdx.y == 0 && threadIdx.x == 0) {

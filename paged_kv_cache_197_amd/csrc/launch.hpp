@@ -25,6 +25,8 @@ hipError_t kv_append(const void* k_new, const void* v_new, const int32_t* loc, i
                      int64_t row_bytes, void* k_cache, void* v_cache, int64_t num_slots,
                      hipStream_t stream);
 size_t sparse_workspace_bytes(int batch, int topk, int num_q_heads, int head_dim_v);
+// completion counters a split sparse launch uses (0 when it does not split)
+int64_t sparse_counters(int batch, int topk, int num_q_heads);
 hipError_t sparse_topk(const pkv::SparseArgs& a, hipStream_t stream);
 hipError_t cascade_expand(const pkv::CascadeExpandArgs& a, hipStream_t stream);
 hipError_t expand_merge(const pkv::ExpandMergeArgs& a, int head_dim, hipStream_t stream);

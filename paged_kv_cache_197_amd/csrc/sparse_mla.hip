@@ -98,13 +98,13 @@ __host__ __device__ inline int sparse_keys_per_split(int topk, int splits) {
   return (k + SparseGeom::KT - 1) / SparseGeom::KT * SparseGeom::KT;
 }
 
-// workspace: o [units][S][HB][DV] bf16, lse [units][S][HB] fp32, counter [units]
+// workspace: counter [units] in the fixed counter region at its start, then
+// o [units][S][HB][DV] bf16 and lse [units][S][HB] fp32
 __host__ __device__ inline size_t sparse_ws_bytes(int units, int splits, int hb) {
   if (splits <= 1) return 0;
   const size_t o = static_cast<size_t>(units) * splits * hb * SparseGeom::DV * 2;
   const size_t l = static_cast<size_t>(units) * splits * hb * 4;
-  const size_t c = static_cast<size_t>(units) * 4;
-  return o + l + c;
+  return PKV_WORKSPACE_COUNTER_BYTES + o + l;
 }
 
 __device__ __forceinline__ int rho32(int h, int r) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -459,9 +459,10 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
   // does not depend on which split ends last.
   char* wsb = static_cast<char*>(a.workspace);
   const int64_t n_parts = static_cast<int64_t>(units) * splits;
-  bf16_t* ws_o = reinterpret_cast<bf16_t*>(wsb);
-  float* ws_lse = reinterpret_cast<float*>(wsb + n_parts * C::HB * C::DV * 2);
-  int* counter = reinterpret_cast<int*>(wsb + n_parts * C::HB * C::DV * 2 + n_parts * C::HB * 4);
+  int* counter = reinterpret_cast<int*>(wsb);
+  bf16_t* ws_o = reinterpret_cast<bf16_t*>(wsb + PKV_WORKSPACE_COUNTER_BYTES);
+  float* ws_lse = reinterpret_cast<float*>(wsb + PKV_WORKSPACE_COUNTER_BYTES +
+                                           n_parts * C::HB * C::DV * 2);
   const int64_t part0 = static_cast<int64_t>(unit) * splits;   // this unit's first partial
   constexpr uint32_t kPartBytes = C::HB * C::DV * 2;
   const uint32_t lane_off = static_cast<uint32_t>((wave * 16 * 64 + lane) * 8);   // + 512 i
@@ -553,6 +554,12 @@ __global__ __launch_bounds__(256 * QUADS, 1) void sparse_mla_kernel(SparseArgs a
 }  // namespace pkv
 
 namespace pkv_launch {
+
+int64_t sparse_counters(int batch, int topk, int num_q_heads) {
+  if (batch <= 0 || topk <= 0 || num_q_heads <= 0) return 0;
+  if (pkv::sparse_num_splits(batch, topk, num_q_heads) <= 1) return 0;
+  return static_cast<int64_t>(batch) * (num_q_heads / pkv::sparse_head_block(num_q_heads));
+}
 
 size_t sparse_workspace_bytes(int batch, int topk, int num_q_heads, int head_dim_v) {
   (void)head_dim_v;

@@ -13,6 +13,7 @@ LIB = pkv.library_path()
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libpkv.so not built")
 
 EINVAL, EUNSUP = 1, 2
+COUNTER_BYTES = 65536   # PKV_WORKSPACE_COUNTER_BYTES
 
 
 def test_header_declares_the_entry_points():
@@ -104,10 +105,12 @@ def test_sparse_workspace_plan():
     size = lib.sparse_topk_decode_workspace_size
     # 32 requests x 128 heads: 64-head blocks, 64 units, 4 key splits of 512
     units, splits, hb = 64, 4, 64
-    # partials: bf16 [HB][512] + fp32 LSE [HB] per (unit, split); one counter per unit
-    assert size(32, 2048, 128, 512) == units * splits * hb * (512 * 2 + 4) + units * 4
+    # the fixed counter region, then per (unit, split) partials: bf16 [HB][512]
+    # and fp32 LSE [HB]
+    region = COUNTER_BYTES
+    assert size(32, 2048, 128, 512) == region + units * splits * hb * (512 * 2 + 4)
     # one request, 32 heads: one 32-head block, 8 splits of 256 keys
-    assert size(1, 2048, 32, 512) == 8 * 32 * (512 * 2 + 4) + 4
+    assert size(1, 2048, 32, 512) == region + 8 * 32 * (512 * 2 + 4)
     # 96 heads are three 32-head blocks; enough units for one split: no workspace
     assert size(96, 2048, 96, 512) == 0
     pf = lib.paged_attn_varlen_prefill
@@ -136,7 +139,7 @@ def test_prefill_workspace_plan():
     assert size(4, 849, 512, 96, 32, 8, 128) == 0
     # two q tiles against 8192 cached keys: split, workspace scales with total_q
     small = size(1, 64, 64, 8192, 32, 8, 128)
-    assert small > 0
+    assert small > COUNTER_BYTES
     assert size(1, 128, 64, 8192, 32, 8, 128) > small
     # a call that needs a workspace rejects a missing or short one before any
     # launch (fake non-NULL pointers: validation never touches them)
@@ -231,3 +234,36 @@ def test_binding_declares_every_entry_point():
     declared = set(pkv.declared_symbols())
     missing = sorted(declared - set(pkv._SIGNATURES))
     assert not missing, missing
+
+
+def test_header_counter_region_constant():
+    text = open(os.path.join(os.path.dirname(LIB), "..", "include", "pkv.h")).read()
+    assert f"#define PKV_WORKSPACE_COUNTER_BYTES {COUNTER_BYTES}" in text
+
+
+def test_softmax_scale_must_be_finite_and_positive():
+    """Every attention entry point rejects a scale that is zero, negative or not
+    finite before anything is enqueued (fake non-NULL device pointers)."""
+    lib = pkv.load_library()
+    fake = ctypes.c_void_p(256)
+    bad = [0.0, -0.125, float("nan"), float("inf"), -float("inf")]
+    for sc in bad:
+        assert _decode(lib, q=fake, k=fake, v=fake, pt=fake, kv_lens=fake, op=fake, lp=fake,
+                       scale=sc) == EINVAL, sc
+        assert b"softmax_scale" in lib.pkv_last_error()
+        pf = lib.paged_attn_varlen_prefill
+        assert pf(fake, 1, fake, fake, 8, fake, 4, fake, fake, 2, 10, 5, 40, 8, 2, 128, 1, sc, 1,
+                  -1, 0, fake, 1 << 30, fake, None, None) == EINVAL, sc
+        sp = lib.sparse_topk_decode
+        assert sp(fake, fake, 10, fake, 2, 10, fake, fake, 4, 1, 128, 576, 512, sc, fake, 1 << 30,
+                  fake, None, None) == EINVAL, sc
+        em = lib.paged_attn_expand_merge
+        assert em(fake, 1, fake, fake, 9, fake, 8, fake, 4, 32, 8, 128, sc, fake, fake,
+                  None) == EINVAL, sc
+        dd = lib.paged_attn_dca_decode
+        assert dd(fake, fake, fake, 1, fake, fake, 64, fake, 8, fake, 2, 32, 8, 128, 16, sc, 64,
+                  None, 64, 4, fake, fake, None, None, None) == EINVAL, sc
+    # a positive scale passes the check (these calls then fail on other grounds
+    # only when an argument is wrong; here everything else is valid but the
+    # device pointers are fake, so stop at the decode's host checks)
+    assert _decode(lib, scale=0.125, batch=0) == 0

@@ -151,3 +151,26 @@ def test_cascade_verify_workload_sampled():
             mask_all[starts[b]:starts[b + 1]], n, c.scale)
         assert_close(f"out[{b}]", np_f(out[b * n:(b + 1) * n]), ro, O_TOL)
         assert_close(f"lse[{b}]", np_f(lse[b * n:(b + 1) * n]), rl, LSE_TOL)
+
+
+def test_cascade_page_permutation_bit_identical():
+    """Moving every cache page elsewhere (token table rewritten to match, tables
+    rebuilt on the GPU) leaves the cascade result bit-identical."""
+    c = make_case(761, [70, 300, 5, 1100], 8, hq=16, hkv=4, D=128, P=16)
+    say("cascade page permutation")
+    pt, kl, tab, lens, _ = gpu_tables(c)
+    a = gpu_cascade(c, pt, kl, tab, lens)
+    P = c.page_size
+    n = c.k_cache.shape[0]
+    assert 0 <= int(c.req_to_token.min()) and int(c.req_to_token.max()) < n * P
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(8)).to(DEV)
+    k = torch.empty_like(c.k_cache)
+    v = torch.empty_like(c.v_cache)
+    k[perm] = c.k_cache
+    v[perm] = c.v_cache
+    r2t = c.req_to_token.long()
+    r2t = (perm[r2t // P] * P + r2t % P).to(torch.int32)
+    c2 = workloads.CascadeCase(**{**c.__dict__, "k_cache": k, "v_cache": v, "req_to_token": r2t})
+    pt2, kl2, tab2, lens2, _ = gpu_tables(c2)
+    d = gpu_cascade(c2, pt2, kl2, tab2, lens2)
+    assert torch.equal(a[0], d[0]) and torch.equal(a[1], d[1])

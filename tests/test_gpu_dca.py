@@ -48,13 +48,7 @@ def test_dca_tables(P, chunk_size, local_size, omp):
     for name in ("lens_intra", "lens_succ", "lens_inter"):
         assert np.array_equal(np_i(r[name]), t[name]), name
     for name in ("table_intra", "table_succ"):
-        ref = t[name]
-        if ref is None:
-            continue
-        got = np_i(r[name])
-        w = ref.shape[1]
-        assert np.array_equal(got[:, :w], ref), name
-        assert not got[:, w:].any(), name
+        assert np.array_equal(np_i(r[name]), t[name]), name
     sf = oracle.dca_scaling_factor(lens, omp) if omp > 0 else np.ones(len(lens))
     assert np.allclose(np_f(r["scaling_factor"]), sf, rtol=1e-6, atol=0)
 

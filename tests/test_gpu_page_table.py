@@ -67,19 +67,6 @@ def test_sliding_window_tables_match_oracle(make):
               np_i(c.prefill_lens), c.window, c.table_width)
 
 
-def test_sliding_window_table_is_brute_force_set():
-    """The GPU table also equals the set-construction reading of the docstring."""
-    c = workloads.config4(with_values=False)
-    say("pa-swa vs set construction")
-    got = gpu_table(np_i(c.req_to_token), np_i(c.req_pool_indices), np_i(c.seq_lens),
-                    1, c.table_width, prefill_lens=np_i(c.prefill_lens), window=c.window)
-    ref = oracle.page_table_pa_swa_bruteforce(np_i(c.req_to_token), np_i(c.req_pool_indices),
-                                              np_i(c.seq_lens), np_i(c.prefill_lens), c.window,
-                                              c.table_width)
-    for g, r in zip(got, ref):
-        assert np.array_equal(g, r)
-
-
 def test_sliding_window_edge_cases():
     rng = np.random.default_rng(11)
     say("pa-swa edge cases")

@@ -100,3 +100,35 @@ def test_sparse_repeat_calls_and_order_invariance():
     d = run_case(c2)
     assert_close("shuffled out", np_f(d[0]), np_f(a[0]), 1e-2)
     assert_close("shuffled lse", np_f(d[1]), np_f(a[1]), 1e-4)
+
+
+# Many key splits: the upper half of the range the entry point accepts
+# (64 splits of 2048 keys at most). One request of 32 heads is one unit, so the
+# plan cuts the top-k list into 64 splits; eight requests give 32 splits.
+@pytest.mark.parametrize("batch,topk,pad,rows", [(8, 65536, 1500, [0, 5]),
+                                                 (1, 131072, 3000, [0])])
+def test_sparse_many_key_splits(batch, topk, pad, rows):
+    c = workloads.make_sparse_case(90 + batch, batch=batch, ctx=topk, topk=topk, num_q_heads=32,
+                                   head_dim_qk=576, head_dim_v=512, num_pad=pad,
+                                   value_device=DEV)
+    c = to_device(c, DEV)
+    say(f"sparse many splits batch={batch} topk={topk} pad={pad} rows={rows}")
+    run_case(c, rows=rows)
+
+
+def test_sparse_slot_permutation_bit_identical():
+    """Moving every cache row to another slot (token table rewritten to match)
+    leaves the result bit-identical: the kernel reads the same values in the
+    same logical order."""
+    c = to_device(workloads.small_config5(seed=19, num_pad=9), DEV)
+    say("sparse slot permutation")
+    a = run_case(c)
+    n = c.kv_cache.shape[0]
+    assert 0 <= int(c.req_to_token.min()) and int(c.req_to_token.max()) < n   # indexing below
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(6)).to(DEV)
+    kv = torch.empty_like(c.kv_cache)
+    kv[perm] = c.kv_cache
+    r2t = perm[c.req_to_token.long()].to(torch.int32)
+    c2 = workloads.SparseCase(**{**c.__dict__, "kv_cache": kv, "req_to_token": r2t})
+    d = run_case(c2)
+    assert torch.equal(a[0], d[0]) and torch.equal(a[1], d[1])

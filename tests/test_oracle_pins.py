@@ -299,17 +299,27 @@ def _random_swa_inputs(rng, batch, ctx):
     return r2t, rpi, sl, pf_pool
 
 
-def test_pa_swa_formula_matches_set_construction():
+def test_pa_swa_sizes_and_order():
+    """The kept set, counted in closed form: the prompt contributes
+    ``h = min(pf, sl)`` leading positions and the window the ``min(sl, pf + W) - h``
+    newest ones, so the row is those two runs back to back, then zeros. Checked
+    on 200 random cases (prompt past the sequence, empty window, and so on)."""
     rng = np.random.default_rng(7)
     for trial in range(200):
         batch = int(rng.integers(1, 6))
         ctx = int(rng.integers(1, 60))
         r2t, rpi, sl, pf = _random_swa_inputs(rng, batch, ctx)
         window = int(rng.integers(0, 70))
-        a = oracle.page_table_pa_swa(r2t, rpi, sl, pf, window, ctx)
-        b = oracle.page_table_pa_swa_bruteforce(r2t, rpi, sl, pf, window, ctx)
-        for x, y in zip(a, b):
-            assert np.array_equal(x, y), trial
+        pt, kv, cu = oracle.page_table_pa_swa(r2t, rpi, sl, pf, window, ctx)
+        for b in range(batch):
+            r, s_, p_ = int(rpi[b]), int(sl[b]), int(pf[int(rpi[b])])
+            head = min(p_, s_)
+            total = min(s_, p_ + window)
+            assert kv[b] == total, trial
+            positions = list(range(head)) + list(range(s_ - (total - head), s_))
+            assert pt[b, :total].tolist() == [int(r2t[r, t]) for t in positions], trial
+            assert not pt[b, total:].any(), trial
+        assert cu.tolist() == [0] + np.cumsum(kv).tolist()
 
 
 def test_pa_swa_edge_cases():
@@ -406,21 +416,22 @@ def test_planted_unnormalised_merge_is_caught(monkeypatch):
         test_split_then_merge_equals_unsplit(4, 8)
 
 
-def test_planted_pa_swa_gap_mistake_is_caught(monkeypatch):
+def test_planted_pa_swa_window_mistake_is_caught(monkeypatch):
+    """A window that keeps one token too few is caught by the size pin."""
     def bad(req_to_token, rpi, seq_lens, prefill_lens, window, width):
         pt = np.zeros((len(rpi), width), dtype=np.int32)
         kv = np.zeros(len(rpi), dtype=np.int32)
         for b in range(len(rpi)):
             r, sl, pf = int(rpi[b]), int(seq_lens[b]), int(prefill_lens[int(rpi[b])])
-            ds = max(pf, sl - window)
-            gap = ds - pf
-            kv[b] = sl - gap
-            for j in range(kv[b]):
-                pt[b, j] = req_to_token[r, j if j <= pf else j + gap]   # <= instead of <
+            keep = sorted(t for t in set(range(pf)) | set(range(max(pf, sl - window + 1), sl))
+                          if t < sl)
+            kv[b] = len(keep)
+            for j, t in enumerate(keep):
+                pt[b, j] = req_to_token[r, t]
         return pt, kv, oracle.cu_seqlens(kv)
     monkeypatch.setattr(oracle, "page_table_pa_swa", bad)
     with pytest.raises(AssertionError):
-        test_pa_swa_formula_matches_set_construction()
+        test_pa_swa_sizes_and_order()
 
 
 # --- kv_append: set_kv_buffer at out_cache_loc ([FA] forward_extend) ---------
@@ -809,10 +820,14 @@ def test_dca_tables_cover_the_three_ranges():
         cc = (L - 1) // C
         got = [slot(t["table_intra"][b], p) for p in range(int(t["lens_intra"][b]))]
         assert got == full[cc * C:L]
-        if t["table_succ"] is not None:
-            got = [slot(t["table_succ"][b], p) for p in range(int(t["lens_succ"][b]))]
-            assert got == full[max(cc - 1, 0) * C:cc * C] if cc >= 1 else got == []
+        got = [slot(t["table_succ"][b], p) for p in range(int(t["lens_succ"][b]))]
+        assert got == (full[(cc - 1) * C:cc * C] if cc >= 1 else [])
         assert int(t["lens_inter"][b]) == max(cc - 1, 0) * C
+        # the three ranges tile [0, L); rows are zero past their stage's pages
+        assert t["lens_intra"][b] + t["lens_succ"][b] + t["lens_inter"][b] == L
+        n_intra = -(-int(t["lens_intra"][b]) // P)
+        assert not t["table_intra"][b, n_intra:].any()
+        assert not t["table_succ"][b, C // P if cc >= 1 else 0:].any()
 
 
 @pytest.mark.parametrize("P,chunk_size,local_size", [(4, 24, 8), (1, 9, 1), (8, 40, 8)])
