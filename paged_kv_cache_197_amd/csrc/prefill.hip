@@ -68,7 +68,11 @@ struct PrefillKernel {
   static constexpr int NSTAGE = 4;
   static constexpr int GROUP_LDS = NSTAGE * STAGE;
   static constexpr int ENTRY_BYTES = WAVES * 2 * 256; // waves x 2 segments x 64 words
-  static constexpr int LDS_BYTES = GROUPS * GROUP_LDS + ENTRY_BYTES;
+  // the split hand-off's flag sits after the entry slots, inside the dynamic
+  // LDS: with no static LDS the dynamic region starts at address 0, so every
+  // constant LDS offset folds into the instructions' offset fields
+  static constexpr int FLAG_OFF = GROUPS * GROUP_LDS + ENTRY_BYTES;
+  static constexpr int LDS_BYTES = FLAG_OFF + 16;
   static constexpr int RPB = 1024 / ROW;      // key rows per 1 KB copy block
   static constexpr int IPW = TILE / 1024 / 4; // copy blocks per wave and tensor
   static constexpr int KPW = IPW * RPB;       // keys per wave per tile
@@ -163,9 +167,10 @@ struct PrefillKernel {
       const int j = i * RPB + lane / CH;   // key 8w + j of the tile
       const int t = min(kt * KT + KPW * w + j, L - 1);
       const int32_t raw = raws[i];
-      // page in [0, num_pages) (num_pages * page_size < 2^31: slots fit 32 bits)
-      const uint32_t page = static_cast<uint32_t>(raw) < static_cast<uint32_t>(a.num_pages)
-                                ? static_cast<uint32_t>(raw) : 0u;
+      // page clamped into [0, num_pages) (num_pages * page_size < 2^31: slots
+      // fit 32 bits; a negative entry reads as a large unsigned one)
+      const uint32_t page = min(static_cast<uint32_t>(raw),
+                                static_cast<uint32_t>(a.num_pages - 1));
       uint32_t slot;
       if constexpr (PM == kPageToken) slot = page;
       else if constexpr (PM == kPagePow2) slot = (page << a.page_shift) | page_off(a, t);
@@ -186,20 +191,34 @@ struct PrefillKernel {
       kw[j] = *reinterpret_cast<const u32x4*>(stage + kbase + swz(q, 2 * j + h) * 16);
   }
 
+  // Online-softmax state of the lane's row (equal in lanes q and q + 32).
+  // m is a reference max in raw score units (-inf before the row has seen a
+  // key); the scale c = scale_log2 > 0 is applied inside the exponent,
+  // p = exp2(s c - m c). m moves only when a score exceeds thr = m +
+  // kRescaleLog2 / c, so the exponentials stay below 2^kRescaleLog2 while the
+  // accumulators are rescaled on few tiles; the sum and the output share the
+  // reference, so the result is the same for any such m. l is this lane's
+  // half-row sum of the exponentials (fp32).
+  struct RowState {
+    float m, thr, neg_mc, l;
+  };
+  static __device__ __forceinline__ RowState row_state_init() {
+    return RowState{neg_inf(), neg_inf(), 0.f, 0.f};
+  }
+
   // Softmax of S^T for this wave's row block and the O^T update with the
   // tile's V, software-pipelined with S^T of the next tile: its K operands
   // (kw, already read) go through the MFMAs while the exponentials of this
-  // tile run on the VALU. Returns the next tile's S^T.
-  // m_run is a reference max in raw score units; scale_log2 > 0 is applied
-  // inside the exponent (exp2(s * c - m * c)). Masked tiles apply the per-row
-  // key window (key kt*32 + rho(h, r) is visible iff rel_lo <= rho(h, r) - 4h
-  // < rel).
+  // tile run on the VALU. Returns the next tile's S^T. Masked tiles apply the
+  // per-row key window (key kt*32 + rho(h, r) is visible iff
+  // rel_lo <= rho(h, r) - 4h < rel).
   static __device__ __forceinline__ f32x16 softmax_pv(f32x16 s, const char* stage_v,
                                                       const int (&vofs)[2][NB], bool masked,
-                                                      int rel, int rel_lo, int h, float scale_log2,
+                                                      int rel, int rel_lo, float scale_log2,
+                                                      float rescale_step,
                                                       const u32x4 (&kw)[NKS],
                                                       const u32x4 (&qop)[NKS], f32x16 (&acc)[NB],
-                                                      float& m_run, float& l_run) {
+                                                      RowState& st) {
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = s[r];
@@ -208,26 +227,27 @@ struct PrefillKernel {
       for (int r = 0; r < 16; ++r)
         if (8 * (r >> 2) + (r & 3) >= rel || 8 * (r >> 2) + (r & 3) < rel_lo) x[r] = neg_inf();
     }
-    float mt = fmaxf(x[0], x[1]);
+    // this lane's half of the row: does any score pass the threshold?
+    // (med3(a, b, +inf) = max(a, b) without quieting the MFMA results first)
+    float mt = __builtin_amdgcn_fmed3f(x[0], x[1], __builtin_inff());
 #pragma unroll
     for (int r = 2; r < 16; ++r) mt = fmaxf(mt, x[r]);
-    mt = max_xor32(mt);
-    // m_run moves only when a row's tile max exceeds it by more than
-    // kRescaleLog2 (log2 units of the scaled score). In between, the
-    // exponentials stay below 2^kRescaleLog2 and the sum and the output share
-    // the reference, so the result is unchanged while the rescale of the
-    // accumulators is skipped on almost every tile.
-    // (-inf - -inf is NaN: a row with no visible key yet does not move.)
-    const bool grow = (mt - m_run) * scale_log2 > kRescaleLog2;
-    const float m_ref = grow ? mt : m_run;
-    const float m_use = (m_ref == neg_inf()) ? 0.f : m_ref;
-    const float alpha = grow ? fast_exp2((m_run - m_use) * scale_log2) : 1.f;
-    const float neg_mc = -m_use * scale_log2;
-    m_run = m_ref;
-    if (__any(grow)) {
+    if (__any(mt > st.thr)) {
+      // rare after a row's first tiles: move the reference of every row whose
+      // maximum (both halves) passed it, and rescale what was accumulated
+      mt = max_xor32(mt);
+      const bool grow = mt > st.thr;
+      const float m_ref = grow ? mt : st.m;
+      const float m_use = (m_ref == neg_inf()) ? 0.f : m_ref;
+      const float alpha = grow ? fast_exp2((st.m - m_use) * scale_log2) : 1.f;
+      st.m = m_ref;
+      st.neg_mc = -m_use * scale_log2;
+      st.thr = (m_ref == neg_inf()) ? neg_inf() : m_ref + rescale_step;
+      st.l *= alpha;
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[n] *= alpha;
     }
+    const float neg_mc = st.neg_mc;
 
     // V^T operands (see below) of the first 16-key step, early
     typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -265,15 +285,17 @@ struct PrefillKernel {
       for (int s2 = 0; s2 < 2; ++s2)
         vt[1][n][s2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             reinterpret_cast<lds_s16x4*>((lds_char*)stage_v + vofs[s2][n] + 16 * ROW));
-    float ps[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ps[i] = (p[4 * i] + p[4 * i + 1]) + (p[4 * i + 2] + p[4 * i + 3]);
-    l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
 
     // O^T block n row m = dim 32n + m. Its A operand for the 16-key step t is
     // V^T[32n + m][keys 16t + 8(e/4) + 4h + e%4], e = 0..7: two transposed
     // 8-byte LDS reads (ds_read_b64_tr_b16), each turning 16 lanes' row-major
     // 4-dim pieces of 4 keys into one dim's 4 keys per lane (vofs).
+    // The row sum is taken over the fp32 exponentials: bf16-rounded ones
+    // would move the LSE by up to 2^-9 on rows that one key dominates.
+    float ps[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ps[i] = (p[4 * i] + p[4 * i + 1]) + (p[4 * i + 2] + p[4 * i + 3]);
+    st.l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const u32x4 pw = {pack_bf16x2(p[8 * t + 0], p[8 * t + 1]),
@@ -310,7 +332,7 @@ struct PrefillKernel {
 
   static __device__ void run(const PrefillArgs& a) {
     extern __shared__ __align__(16) char smem[];
-    __shared__ int sh_last;
+    int& sh_last = *reinterpret_cast<int*>(smem + FLAG_OFF);
 
     const int G = a.hq / a.hkv;
     const int n_hb = (G + 3) / 4;
@@ -488,8 +510,8 @@ struct PrefillKernel {
       for (int n = 0; n < NB; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
-      float m_run = neg_inf();
-      float l_run = 0.f;
+      RowState st = row_state_init();
+      const float rescale_step = kRescaleLog2 / a.scale_log2;
 
       // ---- pipeline: tile i+2 is copied while tile i is consumed ----
       // Before tile i is read, every copy issued before tile i+1's must have
@@ -536,7 +558,7 @@ struct PrefillKernel {
 #pragma unroll
       for (int u = 0; u < NSTAGE; ++u) {
         const int it = it0 + u;
-        if (it >= n_iter) break;
+        if (it < n_iter) {
         if (it + 1 < n_g) {
           if (it + 2 < n_g) wait_vmem<2 * IPW>();
           else wait_vmem<0>();
@@ -556,8 +578,9 @@ struct PrefillKernel {
           read_k(smem + ((u + 1) % NSTAGE) * STAGE, kbase, q, h, kw);
           s_cur = softmax_pv(s_cur, smem + u * STAGE + TILE, vofs,
                              kt >= full_tiles || kt < low_full, limit - kt * KT - 4 * h,
-                             row_lo - kt * KT - 4 * h, h, a.scale_log2, kw, qop, acc, m_run,
-                             l_run);
+                             row_lo - kt * KT - 4 * h, a.scale_log2, rescale_step, kw, qop, acc,
+                             st);
+        }
         }
       }
       }
@@ -571,18 +594,18 @@ struct PrefillKernel {
         for (int k = 0; k < 4 * NB; ++k)
           mbuf[64 * k] = f32x4{acc[k >> 2][4 * (k & 3)], acc[k >> 2][4 * (k & 3) + 1],
                                acc[k >> 2][4 * (k & 3) + 2], acc[k >> 2][4 * (k & 3) + 3]};
-        mbuf[64 * 4 * NB] = f32x4{m_run, l_run, 0.f, 0.f};
+        mbuf[64 * 4 * NB] = f32x4{st.m, st.l, 0.f, 0.f};
       }
       if constexpr (GROUPS == 2) __syncthreads();
       float lse_val = 0.f, inv = 0.f;
       if (grp == 0) {
-        float mm = m_run, l_m = l_run;
+        float mm = st.m, l_m = st.l;
         if constexpr (GROUPS == 2) {
           const f32x4 ml = mbuf[64 * 4 * NB];
           const float m1 = ml[0];
           const float l1 = ml[1];
-          mm = fmaxf(m_run, m1);
-          const float f0 = (m_run == neg_inf()) ? 0.f : fast_exp2((m_run - mm) * a.scale_log2);
+          mm = fmaxf(st.m, m1);
+          const float f0 = (st.m == neg_inf()) ? 0.f : fast_exp2((st.m - mm) * a.scale_log2);
           const float f1 = (m1 == neg_inf()) ? 0.f : fast_exp2((m1 - mm) * a.scale_log2);
 #pragma unroll
           for (int k = 0; k < 4 * NB; ++k) {
@@ -591,7 +614,7 @@ struct PrefillKernel {
             for (int c = 0; c < 4; ++c)
               acc[k >> 2][4 * (k & 3) + c] = f0 * acc[k >> 2][4 * (k & 3) + c] + f1 * o1[c];
           }
-          l_m = f0 * l_run + f1 * l1;
+          l_m = f0 * st.l + f1 * l1;
         }
         const float l_tot = l_m + __shfl_xor(l_m, 32);
         inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
