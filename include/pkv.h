@@ -299,6 +299,29 @@ pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num
                                 void* out, float* lse, void* stream);
 
 /*
+ * sparse_topk_decode_noalloc -- sparse_topk_decode that allocates nothing and
+ * takes no workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid it). Its
+ * split partials and counters live in a library-owned device array of
+ * PKV_SPARSE_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held from the
+ * library's load until the process ends; the first call on each GPU looks up
+ * that GPU's copy and clears its counters with a kernel on `stream`. Calls on
+ * one GPU share the array: calls that overlap in time on one GPU race (order
+ * them on one stream). Arguments, results and errors as for
+ * sparse_topk_decode, plus PKV_EUNSUPPORTED when the shape needs more than
+ * PKV_SPARSE_NOALLOC_SCRATCH_BYTES of workspace
+ * (sparse_topk_decode_workspace_size).
+ */
+#define PKV_SPARSE_NOALLOC_SCRATCH_BYTES (32u << 20)
+pkv_status_t sparse_topk_decode_noalloc(const void* q, const void* kv_cache, int64_t num_slots,
+                                        const int32_t* req_to_token, int64_t req_to_token_rows,
+                                        int64_t req_to_token_stride,
+                                        const int32_t* req_pool_indices, const int32_t* topk_idx,
+                                        int32_t topk, int32_t batch, int32_t num_q_heads,
+                                        int32_t head_dim_qk, int32_t head_dim_v,
+                                        float softmax_scale, void* out, float* lse, void* stream);
+
+/*
  * build_dca_decode_tables -- per-request metadata of dual chunk attention
  * decode. [DCA] init_forward_metadata (decode): chunk_len = chunk_size -
  * local_size, c = (L - 1) / chunk_len for L = seq_lens[b] (the cached length

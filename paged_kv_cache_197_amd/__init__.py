@@ -22,6 +22,7 @@ __all__ = [
     "paged_kv_append",
     "paged_attn_decode_splitkv",
     "merge_state", "sparse_topk_decode", "sparse_topk_decode_workspace_size",
+    "sparse_topk_decode_noalloc",
     "PKV_F32", "PKV_BF16",
 ]
 
@@ -81,6 +82,8 @@ _SIGNATURES = {
     "sparse_topk_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "sparse_topk_decode": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _I64, _P, _P, _I32, _I32, _I32,
                                           _I32, _I32, _F, _P, _SZ, _P, _P, _P]),
+    "sparse_topk_decode_noalloc": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _I64, _P, _P, _I32,
+                                                  _I32, _I32, _I32, _I32, _F, _P, _P, _P]),
     "build_dca_decode_tables": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P,
                                                _P, _P, _P, _P, _P]),
     "paged_attn_dca_decode": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I64, _P, _I32, _P, _I32,
@@ -118,6 +121,7 @@ def declared_symbols(header: str = HEADER):
     """Function names declared in include/pkv.h."""
     text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)   # preprocessor lines (macros)
     return sorted(set(re.findall(r"\b([A-Za-z_]\w*)\s*\(", text)) - {"if", "defined"})
 
 
@@ -376,6 +380,33 @@ def sparse_topk_decode(q, kv_cache, req_to_token, req_pool_indices, topk_idx, so
                                 head_dim_v, float(softmax_scale), _ptr(workspace), ws_bytes,
                                 _ptr(out), _ptr(lse), _stream(dev))
     _check("sparse_topk_decode", st)
+    return out, lse
+
+
+def sparse_topk_decode_noalloc(q, kv_cache, req_to_token, req_pool_indices, topk_idx,
+                               softmax_scale, *, head_dim_v=512, out=None, lse=None):
+    """sparse_topk_decode with the split workspace in the library's per-GPU
+    scratch array: the C call allocates nothing (``out`` / ``lse`` are
+    allocated here only when not given). Calls on one GPU must not overlap."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    kv = kv_cache.reshape(kv_cache.shape[0], -1)
+    _need(kv, "kv_cache", torch.bfloat16, dev, 2)
+    r2t = _i32(req_to_token, "req_to_token", dev)
+    rpi = _i32(req_pool_indices, "req_pool_indices", dev)
+    idx = _i32(topk_idx, "topk_idx", dev)
+    batch, hq, dqk = q.shape
+    topk = idx.shape[1] if idx.dim() == 2 else 0
+    if out is None:
+        out = torch.empty((batch, hq, head_dim_v), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    st = lib.sparse_topk_decode_noalloc(_ptr(q), _ptr(kv), kv.shape[0], _ptr(r2t), r2t.shape[0],
+                                        r2t.shape[1], _ptr(rpi), _ptr(idx), topk, batch, hq, dqk,
+                                        head_dim_v, float(softmax_scale), _ptr(out), _ptr(lse),
+                                        _stream(dev))
+    _check("sparse_topk_decode_noalloc", st)
     return out, lse
 
 

@@ -520,39 +520,42 @@ size_t sparse_topk_decode_workspace_size(int32_t batch, int32_t topk, int32_t nu
   return pkv_launch::sparse_workspace_bytes(batch, topk, num_q_heads, head_dim_v);
 }
 
-pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num_slots,
-                                const int32_t* req_to_token, int64_t req_to_token_rows,
-                                int64_t req_to_token_stride, const int32_t* req_pool_indices,
-                                const int32_t* topk_idx, int32_t topk, int32_t batch,
-                                int32_t num_q_heads, int32_t head_dim_qk, int32_t head_dim_v,
-                                float softmax_scale, void* workspace, size_t workspace_bytes,
-                                void* out, float* lse, void* stream) {
+}  // extern "C"
+
+// Checks and argument packing shared by the sparse entry points (workspace
+// fields left for the caller); sets *nothing when there is no work.
+static pkv_status_t sparse_prepare(const char* who, const void* q, const void* kv_cache,
+                                   int64_t num_slots, const int32_t* req_to_token,
+                                   int64_t req_to_token_rows, int64_t req_to_token_stride,
+                                   const int32_t* req_pool_indices, const int32_t* topk_idx,
+                                   int32_t topk, int32_t batch, int32_t num_q_heads,
+                                   int32_t head_dim_qk, int32_t head_dim_v, float softmax_scale,
+                                   void* out, float* lse, pkv::SparseArgs& a, bool* nothing) {
+  *nothing = false;
   PKV_REQUIRE(head_dim_qk == 576 && head_dim_v == 512, PKV_EUNSUPPORTED,
-              "sparse_topk_decode: head dims %d/%d not supported (576/512)", head_dim_qk,
-              head_dim_v);
+              "%s: head dims %d/%d not supported (576/512)", who, head_dim_qk, head_dim_v);
   PKV_REQUIRE(batch >= 0 && topk >= 0 && num_q_heads >= 1, PKV_EINVAL,
-              "sparse_topk_decode: bad sizes batch %d topk %d heads %d", batch, topk, num_q_heads);
+              "%s: bad sizes batch %d topk %d heads %d", who, batch, topk, num_q_heads);
   PKV_REQUIRE(num_q_heads % 32 == 0, PKV_EUNSUPPORTED,
-              "sparse_topk_decode: num_q_heads %d not a multiple of 32", num_q_heads);
+              "%s: num_q_heads %d not a multiple of 32", who, num_q_heads);
   PKV_REQUIRE(topk <= 131072, PKV_EUNSUPPORTED,
-              "sparse_topk_decode: topk %d above 131072 (64 key splits of 2048)", topk);
+              "%s: topk %d above 131072 (64 key splits of 2048)", who, topk);
   PKV_REQUIRE(pkv_host::scale_ok(softmax_scale), PKV_EINVAL,
-              "sparse_topk_decode: softmax_scale %g is not finite and positive", softmax_scale);
-  if (batch == 0) return pkv_host::ok();
+              "%s: softmax_scale %g is not finite and positive", who, softmax_scale);
+  if (batch == 0) {
+    *nothing = true;
+    return pkv_host::ok();
+  }
   PKV_REQUIRE(q && kv_cache && req_to_token && req_pool_indices && out, PKV_EINVAL,
-              "sparse_topk_decode: NULL required pointer");
-  PKV_REQUIRE(topk == 0 || topk_idx != nullptr, PKV_EINVAL, "sparse_topk_decode: NULL topk_idx");
+              "%s: NULL required pointer", who);
+  PKV_REQUIRE(topk == 0 || topk_idx != nullptr, PKV_EINVAL, "%s: NULL topk_idx", who);
   PKV_REQUIRE(num_slots >= 1 && req_to_token_rows >= 1 && req_to_token_stride >= 1, PKV_EINVAL,
-              "sparse_topk_decode: empty cache or token table");
+              "%s: empty cache or token table", who);
   PKV_REQUIRE(pkv_launch::sparse_counters(batch, topk, num_q_heads) * 4 <=
                   PKV_WORKSPACE_COUNTER_BYTES,
               PKV_EUNSUPPORTED,
-              "sparse_topk_decode: batch %d needs more split counters than the workspace's "
-              "counter region holds", batch);
-  const size_t need = sparse_topk_decode_workspace_size(batch, topk, num_q_heads, head_dim_v);
-  PKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr), PKV_EINVAL,
-              "sparse_topk_decode: workspace of %zu bytes, need %zu", workspace_bytes, need);
-  pkv::SparseArgs a;
+              "%s: batch %d needs more split counters than the workspace's counter region holds",
+              who, batch);
   a.q = q;
   a.kv = kv_cache;
   a.num_slots = num_slots;
@@ -567,12 +570,60 @@ pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num
   a.dqk = head_dim_qk;
   a.dv = head_dim_v;
   a.scale_log2 = pkv_host::scale_log2(softmax_scale);
-  a.workspace = workspace;
-  a.workspace_bytes = workspace_bytes;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
   a.out = out;
   a.lse = lse;
+  return pkv_host::ok();
+}
+
+extern "C" {
+
+pkv_status_t sparse_topk_decode(const void* q, const void* kv_cache, int64_t num_slots,
+                                const int32_t* req_to_token, int64_t req_to_token_rows,
+                                int64_t req_to_token_stride, const int32_t* req_pool_indices,
+                                const int32_t* topk_idx, int32_t topk, int32_t batch,
+                                int32_t num_q_heads, int32_t head_dim_qk, int32_t head_dim_v,
+                                float softmax_scale, void* workspace, size_t workspace_bytes,
+                                void* out, float* lse, void* stream) {
+  pkv::SparseArgs a;
+  bool nothing = false;
+  const pkv_status_t st = sparse_prepare(
+      "sparse_topk_decode", q, kv_cache, num_slots, req_to_token, req_to_token_rows,
+      req_to_token_stride, req_pool_indices, topk_idx, topk, batch, num_q_heads, head_dim_qk,
+      head_dim_v, softmax_scale, out, lse, a, &nothing);
+  if (st != PKV_OK || nothing) return st;
+  const size_t need = sparse_topk_decode_workspace_size(batch, topk, num_q_heads, head_dim_v);
+  PKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr), PKV_EINVAL,
+              "sparse_topk_decode: workspace of %zu bytes, need %zu", workspace_bytes, need);
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   return pkv_host::from_hip(pkv_launch::sparse_topk(a, static_cast<hipStream_t>(stream)),
                             "sparse_topk_decode launch");
+}
+
+pkv_status_t sparse_topk_decode_noalloc(const void* q, const void* kv_cache, int64_t num_slots,
+                                        const int32_t* req_to_token, int64_t req_to_token_rows,
+                                        int64_t req_to_token_stride,
+                                        const int32_t* req_pool_indices, const int32_t* topk_idx,
+                                        int32_t topk, int32_t batch, int32_t num_q_heads,
+                                        int32_t head_dim_qk, int32_t head_dim_v,
+                                        float softmax_scale, void* out, float* lse, void* stream) {
+  pkv::SparseArgs a;
+  bool nothing = false;
+  const pkv_status_t st = sparse_prepare(
+      "sparse_topk_decode_noalloc", q, kv_cache, num_slots, req_to_token, req_to_token_rows,
+      req_to_token_stride, req_pool_indices, topk_idx, topk, batch, num_q_heads, head_dim_qk,
+      head_dim_v, softmax_scale, out, lse, a, &nothing);
+  if (st != PKV_OK || nothing) return st;
+  const size_t need = sparse_topk_decode_workspace_size(batch, topk, num_q_heads, head_dim_v);
+  PKV_REQUIRE(need <= PKV_SPARSE_NOALLOC_SCRATCH_BYTES, PKV_EUNSUPPORTED,
+              "sparse_topk_decode_noalloc: this shape needs %zu bytes of scratch, the library "
+              "holds %zu per GPU (use sparse_topk_decode with a workspace)",
+              need, (size_t)PKV_SPARSE_NOALLOC_SCRATCH_BYTES);
+  return pkv_host::from_hip(
+      pkv_launch::sparse_topk_noalloc(a, need > 0, static_cast<hipStream_t>(stream)),
+      "sparse_topk_decode_noalloc launch");
 }
 
 pkv_status_t build_dca_decode_tables(const int32_t* block_tables, int32_t bt_stride,

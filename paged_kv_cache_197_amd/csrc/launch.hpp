@@ -28,6 +28,9 @@ size_t sparse_workspace_bytes(int batch, int topk, int num_q_heads, int head_dim
 // completion counters a split sparse launch uses (0 when it does not split)
 int64_t sparse_counters(int batch, int topk, int num_q_heads);
 hipError_t sparse_topk(const pkv::SparseArgs& a, hipStream_t stream);
+// sparse_topk on the library's per-device scratch array instead of a caller
+// workspace (when `split`, i.e. the shape needs one); allocates nothing
+hipError_t sparse_topk_noalloc(const pkv::SparseArgs& a, bool split, hipStream_t stream);
 hipError_t cascade_expand(const pkv::CascadeExpandArgs& a, hipStream_t stream);
 hipError_t expand_merge(const pkv::ExpandMergeArgs& a, int head_dim, hipStream_t stream);
 hipError_t dca_tables(const pkv::DcaTableArgs& a, hipStream_t stream);

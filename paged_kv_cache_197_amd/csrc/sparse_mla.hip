@@ -34,6 +34,8 @@
 // to the workspace with device-coherent stores, and the last split to finish
 // (device-scope counter) reads them back the same way, merges them and writes
 // the output; the counter is reset for the next call.
+#include <mutex>
+
 #include "args.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -587,6 +589,66 @@ static hipError_t launch_sparse(const pkv::SparseArgs& a, hipStream_t stream) {
 hipError_t sparse_topk(const pkv::SparseArgs& a, hipStream_t stream) {
   if (pkv::sparse_quads(a.hq) == 2) return launch_sparse<2>(a, stream);
   return launch_sparse<1>(a, stream);
+}
+
+// ---- sparse_topk_decode_noalloc: the workspace in library-owned memory ----
+// For callers that cannot allocate (HIP graph capture, serving loops that
+// forbid it). Each GPU the library runs on holds its own copy of `scratch`
+// from module load until the process ends; calls on one GPU share it, so
+// calls that overlap in time on one GPU race. Its first
+// PKV_WORKSPACE_COUNTER_BYTES are the split counters: zeroed by a fill kernel
+// at the first call on each device, then left zero by every completed launch.
+namespace {
+
+__device__ __align__(256) unsigned char scratch[PKV_SPARSE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+// The current device's address of `scratch` (the array's name in host code is
+// a host-side stand-in, not a device address): looked up once per device with
+// that device current, and its counter region cleared on `stream` then.
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    constexpr int n = PKV_WORKSPACE_COUNTER_BYTES / 4;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(ptr), n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t sparse_topk_noalloc(const pkv::SparseArgs& a_in, bool split, hipStream_t stream) {
+  pkv::SparseArgs a = a_in;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  if (split) {
+    void* ptr = nullptr;
+    const hipError_t e = scratch_address(stream, &ptr);
+    if (e != hipSuccess) return e;
+    a.workspace = ptr;
+    a.workspace_bytes = PKV_SPARSE_NOALLOC_SCRATCH_BYTES;
+  }
+  return sparse_topk(a, stream);
 }
 
 }  // namespace pkv_launch

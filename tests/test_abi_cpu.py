@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
                "sparse_topk_decode_workspace_size", "paged_kv_append",
                "paged_attn_varlen_prefill_append", "build_cascade_expand_table",
                "paged_attn_expand_merge", "paged_attn_cascade", "build_dca_decode_tables",
-               "paged_attn_dca_decode"]:
+               "paged_attn_dca_decode", "sparse_topk_decode_noalloc"]:
         assert fn in names
 
 
@@ -267,3 +267,27 @@ def test_softmax_scale_must_be_finite_and_positive():
     # only when an argument is wrong; here everything else is valid but the
     # device pointers are fake, so stop at the decode's host checks)
     assert _decode(lib, scale=0.125, batch=0) == 0
+
+
+def test_sparse_noalloc_argument_errors():
+    """The no-alloc sparse call checks its arguments like sparse_topk_decode and
+    rejects a shape whose workspace exceeds the library's scratch array, before
+    touching the device (fake non-NULL pointers)."""
+    lib = pkv.load_library()
+    fake = ctypes.c_void_p(256)
+    na = lib.sparse_topk_decode_noalloc
+    # q kv slots r2t rows stride rpi idx topk B Hq Dqk Dv scale out lse stream
+    assert na(fake, fake, 10, fake, 2, 10, fake, fake, 4, 1, 128, 512, 512, 0.1, fake, None,
+              None) == EUNSUP
+    assert na(fake, fake, 10, fake, 2, 10, fake, fake, 4, 1, 128, 576, 512, -1.0, fake, None,
+              None) == EINVAL
+    assert na(None, None, 10, None, 2, 10, None, None, 4, 0, 128, 576, 512, 0.1, None, None,
+              None) == 0                                 # empty batch: nothing to do
+    limit = 32 << 20   # PKV_SPARSE_NOALLOC_SCRATCH_BYTES
+    big = lib.sparse_topk_decode_workspace_size(256, 131072, 128, 512)
+    assert big > limit
+    assert na(fake, fake, 10, fake, 2, 10, fake, fake, 131072, 256, 128, 576, 512, 0.1, fake,
+              None, None) == EUNSUP
+    assert b"scratch" in lib.pkv_last_error()
+    text = open(os.path.join(os.path.dirname(LIB), "..", "include", "pkv.h")).read()
+    assert "#define PKV_SPARSE_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
