@@ -32,7 +32,7 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--only", choices=["all", "decode", "decode_window", "prefill",
+    p.add_argument("--only", choices=["all", "decode", "decode_merged", "decode_window", "prefill",
                                       "prefill_long", "prefill_window", "prefill_append", "swa",
                                       "sparse", "cascade", "dca", "copy"],
                    default="all", help="restrict to one workload (for profiler runs)")
@@ -178,7 +178,7 @@ def window_decode_bytes(seq_lens, window_left, batch, hq, hkv, d, page_size, ele
 # Workloads
 # ---------------------------------------------------------------------------
 
-def run_decode(torch, pkv, workloads, args, window_left=-1, kv_chunk=None):
+def run_decode(torch, pkv, workloads, args, window_left=-1, kv_chunk=None, merged=False):
     dev = torch.device("cuda:0")
     c = workloads.config3(value_device=dev)
     r2t, rpi, sl = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev))
@@ -192,11 +192,20 @@ def run_decode(torch, pkv, workloads, args, window_left=-1, kv_chunk=None):
     lp = torch.empty((S, B, hq), dtype=torch.float32, device=dev)
     out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    ws = (torch.zeros(pkv.paged_attn_decode_merged_workspace_size(B, hq, d, 0), dtype=torch.uint8,
+                      device=dev) if merged else None)
 
     def step(timer):
         pkv.build_page_table(r2t, rpi, sl, P, c.table_width, page_table=pt, kv_lens=kl,
                              with_cu_seqlens=False)
         e0 = timer.mark() if timer else None
+        if merged:   # balanced ranges, decode and merge in one launch
+            pkv.paged_attn_decode_merged(c.q, c.k_cache, c.v_cache, pt, kl, c.scale, kv_chunk=0,
+                                         num_splits=0, window_left=window_left, workspace=ws,
+                                         out=out, lse=lse)
+            if timer:
+                timer.pairs.append((e0, timer.mark()))
+            return
         pkv.paged_attn_decode_splitkv(c.q, c.k_cache, c.v_cache, pt, kl, c.scale,
                                       kv_chunk=chunk, num_splits=S, window_left=window_left,
                                       o_partial=op, lse_partial=lp)
@@ -226,10 +235,12 @@ def run_swa(torch, pkv, workloads, args):
     S = c.num_splits
     pt = torch.empty((B, c.table_width), dtype=torch.int32, device=dev)
     kl = torch.empty((B,), dtype=torch.int32, device=dev)
-    op = torch.empty((S, B, hq, d), dtype=torch.float32, device=dev)
-    lp = torch.empty((S, B, hq), dtype=torch.float32, device=dev)
     out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    # balanced ranges (kv_chunk 0, num_splits 0): the library cuts the batch's
+    # visible keys into one round of equal shares
+    ws = torch.zeros(pkv.paged_attn_decode_merged_workspace_size(B, hq, d, 0), dtype=torch.uint8,
+                     device=dev)
     build_t = Timer(torch)
 
     def step(timer):
@@ -239,12 +250,11 @@ def run_swa(torch, pkv, workloads, args):
         e0 = timer.mark() if timer else None
         if timer:
             build_t.pairs.append((e_b, e0))
-        pkv.paged_attn_decode_splitkv(c.q, c.k_cache, c.v_cache, pt, kl, c.scale,
-                                      kv_chunk=c.kv_chunk, num_splits=S, o_partial=op,
-                                      lse_partial=lp)
+        # split decode and the merge of its parts: one launch
+        pkv.paged_attn_decode_merged(c.q, c.k_cache, c.v_cache, pt, kl, c.scale, kv_chunk=0,
+                                     num_splits=0, workspace=ws, out=out, lse=lse)
         if timer:
             timer.pairs.append((e0, timer.mark()))
-        pkv.merge_state(op, lp, out=out, lse_out=lse)
 
     ms, kern_ms = device_loop(torch, step, args.steps, args.warmup)
     torch.cuda.synchronize()
@@ -850,6 +860,25 @@ def main(argv=None):
         del r
         torch.cuda.empty_cache()
 
+    if args.only in ("all", "decode_merged"):
+        try:
+            r = run_decode(torch, pkv, workloads, args, merged=True)
+            extra["decode_merged"] = {
+                "workload": "config3's batch through the merged entry point with balanced "
+                            "ranges (instead of 4096-token chunks): page-table build, then the "
+                            "decode and the merge of its parts in one launch",
+                "device_ms_per_step": round(r["ms"], 4),
+                "decode_merge_kernel_ms": round(r["kernel_ms"], 4),
+                "decode_merge_kernel_ms_median": round(r["kernel_ms_median"], 4),
+                "step_GB/s": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 2),
+                "kernel_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
+                "kernel_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": r["bytes"], "split_mode": "balanced ranges"}
+        except Exception as e:
+            extra["decode_merged"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
     if args.only in ("all", "decode_window"):
         try:
             W = 4095
@@ -875,14 +904,17 @@ def main(argv=None):
             r = run_swa(torch, pkv, workloads, args)
             extra["swa_decode"] = {
                 "workload": "config4: prefill-aware sliding-window decode, B=32, window 4096, "
-                            "64 q / 8 kv heads, D=128, page 1 (table built on GPU)",
-                "device_ms_per_step": round(r["ms"], 4), "decode_kernel_ms": round(r["kernel_ms"], 4),
+                            "64 q / 8 kv heads, D=128, page 1 (table built on GPU); merged "
+                            "decode over balanced ranges (the batch's visible keys cut into 512 "
+                            "equal workgroup shares, parts merged in the same launch)",
+                "device_ms_per_step": round(r["ms"], 4),
+                "decode_merge_kernel_ms": round(r["kernel_ms"], 4),
                 "table_build_ms": round(r["build_ms"], 4),
                 "GB/s": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 2),
                 "kernel_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
                 "kernel_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
                                          / HBM_PEAK_GBS, 4),
-                "sum_kv_len": r["sum_kv_len"], "num_splits": r["splits"]}
+                "sum_kv_len": r["sum_kv_len"], "split_mode": "balanced ranges"}
             if not args.no_cpu_baseline:
                 extra["swa_decode"]["cpu_oracle"] = cpu_oracle_swa(torch, r, 4.0)
         except Exception as e:  # report, do not hide

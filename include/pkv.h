@@ -55,15 +55,16 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype_t;
 
 /*
  * Workspaces (paged_attn_varlen_prefill[_append], paged_attn_cascade,
- * sparse_topk_decode). A workspace starts with PKV_WORKSPACE_COUNTER_BYTES
- * bytes of completion counters at a fixed place that does not depend on the
- * call's shape; the per-split partial results follow them. Hence one buffer,
- * at least as large as the size function returns for each shape, serves
- * calls of any shape in any order. Before its first use the counter region
- * must be zero (any fill on the stream: hipMemsetAsync, torch.zero_); every
- * launch that runs to completion leaves it zero again. A call that returns an
- * error has enqueued nothing and has left it as it was. Calls that share a
- * workspace must be ordered (one stream, or synchronised).
+ * paged_attn_decode_merged, sparse_topk_decode). A workspace starts with
+ * PKV_WORKSPACE_COUNTER_BYTES bytes of completion counters at a fixed place
+ * that does not depend on the call's shape; the per-split partial results
+ * follow them. Hence one buffer, at least as large as the size function
+ * returns for each shape, serves calls of any shape in any order. Before its
+ * first use the counter region must be zero (any fill on the stream:
+ * hipMemsetAsync, torch.zero_); every launch that runs to completion leaves it
+ * zero again. A call rejected by its argument checks has enqueued nothing and
+ * has left it as it was. Calls that share a workspace must be ordered (one
+ * stream, or synchronised).
  */
 #define PKV_WORKSPACE_COUNTER_BYTES 65536
 
@@ -241,6 +242,42 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
                                        int32_t window_left, int32_t attn_chunk,
                                        int32_t kv_chunk, int32_t num_splits, float* o_partial,
                                        float* lse_partial, void* out, float* lse, void* stream);
+
+/*
+ * paged_attn_decode_merged -- paged_attn_decode_splitkv and merge_state over
+ * its num_splits parts in one call ([FA] forward_decode runs the split decode
+ * and its combine back to back; [DCA] _dual_chunk_flash_attn_decoding merges
+ * the partial decodes it has just produced). Arguments as for
+ * paged_attn_decode_splitkv, except:
+ * workspace: device scratch of at least
+ *          paged_attn_decode_merged_workspace_size(...) bytes (may be NULL when
+ *          that size is 0, i.e. num_splits == 1): completion counters (one per
+ *          request and group of 256 / head_dim kv heads, in the counter
+ *          region), then the partials
+ *          o [num_splits, batch, num_q_heads, head_dim] fp32 and lse
+ *          [num_splits, batch, num_q_heads] fp32, each 256-byte aligned; layout
+ *          and zeroing rule as stated at PKV_WORKSPACE_COUNTER_BYTES.
+ * out      [batch, num_q_heads, head_dim] dtype (out); lse [batch, num_q_heads]
+ *          fp32 (out) or NULL.
+ * The result is bit-identical to paged_attn_decode_splitkv followed by
+ * merge_state on the same arguments. On the bf16 kv-head-group kernel (bf16,
+ * 256 / head_dim kv heads whose query heads fit 16 columns) this is one launch:
+ * the last of a request's non-empty splits to finish merges them. Otherwise
+ * the two kernels run back to back. A request with no visible key gets
+ * (0, -inf). Errors as for paged_attn_decode_splitkv, plus PKV_EINVAL for a
+ * NULL out or a workspace smaller than the size function returns.
+ */
+size_t paged_attn_decode_merged_workspace_size(int32_t batch, int32_t num_q_heads,
+                                               int32_t head_dim, int32_t num_splits);
+
+pkv_status_t paged_attn_decode_merged(const void* q, int32_t dtype, const void* k_cache,
+                                      const void* v_cache, int64_t num_pages,
+                                      const int32_t* page_table, int32_t pt_stride,
+                                      const int32_t* kv_lens, int32_t batch, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                      float softmax_scale, int32_t window_left, int32_t attn_chunk,
+                                      int32_t kv_chunk, int32_t num_splits, void* workspace,
+                                      size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
  * merge_state -- combine partial attention states over disjoint key sets.

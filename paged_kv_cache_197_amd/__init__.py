@@ -20,7 +20,8 @@ __all__ = [
     "PkvError", "PkvLibraryMissing", "load_library", "library_path", "declared_symbols",
     "build_page_table", "paged_attn_varlen_prefill", "paged_attn_varlen_prefill_workspace_size",
     "paged_kv_append",
-    "paged_attn_decode_splitkv",
+    "paged_attn_decode_splitkv", "paged_attn_decode_merged",
+    "paged_attn_decode_merged_workspace_size",
     "merge_state", "sparse_topk_decode", "sparse_topk_decode_workspace_size",
     "sparse_topk_decode_noalloc",
     "PKV_F32", "PKV_BF16",
@@ -78,6 +79,10 @@ _SIGNATURES = {
     "paged_attn_decode_splitkv": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _I32,
                                                  _I32, _I32, _I32, _I32, _F, _I32, _I32, _I32,
                                                  _I32, _P, _P, _P, _P, _P]),
+    "paged_attn_decode_merged_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+    "paged_attn_decode_merged": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _I32,
+                                                _I32, _I32, _I32, _I32, _F, _I32, _I32, _I32,
+                                                _I32, _P, _SZ, _P, _P, _P]),
     "merge_state": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P, _P]),
     "sparse_topk_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "sparse_topk_decode": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _I64, _P, _P, _I32, _I32, _I32,
@@ -235,6 +240,47 @@ def paged_attn_decode_splitkv(q, k_cache, v_cache, page_table, kv_lens, softmax_
         _stream(dev))
     _check("paged_attn_decode_splitkv", st)
     return (out, lse) if num_splits == 1 else (o_partial, lse_partial)
+
+
+def paged_attn_decode_merged_workspace_size(batch, num_q_heads, head_dim, num_splits):
+    return int(load_library().paged_attn_decode_merged_workspace_size(batch, num_q_heads,
+                                                                      head_dim, num_splits))
+
+
+def paged_attn_decode_merged(q, k_cache, v_cache, page_table, kv_lens, softmax_scale, *,
+                             kv_chunk=0, num_splits=1, window_left=-1, attn_chunk=0,
+                             workspace=None, out=None, lse=None):
+    """Split-KV paged decode and the merge of its splits in one call.
+    Returns (out [B, Hq, D] q.dtype, lse [B, Hq] fp32)."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", None, dev, 3)
+    _need(k_cache, "k_cache", q.dtype, dev, 4)
+    _need(v_cache, "v_cache", q.dtype, dev, 4)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    pt = _i32(page_table, "page_table", dev)
+    kl = _i32(kv_lens, "kv_lens", dev)
+    batch, hq, d = q.shape
+    num_pages, page_size, hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head_dim of q and cache differ")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    need = paged_attn_decode_merged_workspace_size(batch, hq, d, num_splits)
+    if workspace is None and need > 0:
+        # zero-filled once: the kernel leaves its completion counters at zero
+        workspace = torch.zeros((need,), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.paged_attn_decode_merged(
+        _ptr(q), _dtype_code(q.dtype), _ptr(k_cache), _ptr(v_cache), num_pages, _ptr(pt),
+        pt.shape[1], _ptr(kl), batch, hq, hkv, d, page_size, float(softmax_scale),
+        int(window_left), int(attn_chunk), int(kv_chunk), int(num_splits), _ptr(workspace),
+        ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
+    _check("paged_attn_decode_merged", st)
+    return out, lse
 
 
 def merge_state(o_parts, lse_parts, *, out_dtype=torch.bfloat16, out=None, lse_out=None):

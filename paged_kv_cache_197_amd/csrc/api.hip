@@ -125,6 +125,28 @@ using pkv_host::fail;
     if (!(cond)) return fail(code, __VA_ARGS__); \
   } while (0)
 
+// Balanced merged decode: ranges per kv-head group so that groups x ranges
+// is one round of workgroups on a 256-CU device (two per CU), and the most
+// partial rows (ranges + batch, or 8 fixed splits x batch where the group
+// kernel does not run) its workspace must hold.
+constexpr int kBalancedSlots = 512;
+constexpr int kBalancedMaxSplits = 8;
+constexpr int64_t kBalancedMaxKeys = int64_t{1} << 24;
+
+// merged decode workspace: counters, then o [parts, Hq, D] fp32, then lse
+// [parts, Hq] fp32 with parts = S x B (fixed splits) or 512 + 8 B (balanced,
+// num_splits == 0)
+static size_t decode_merged_ws_bytes(int64_t batch, int64_t num_q_heads, int64_t head_dim,
+                                     int64_t num_splits) {
+  if (num_splits == 1 || num_splits < 0 || batch <= 0 || num_q_heads <= 0 || head_dim <= 0)
+    return 0;
+  const int64_t parts = num_splits == 0 ? kBalancedSlots + kBalancedMaxSplits * batch
+                                        : num_splits * batch;
+  const size_t rows = static_cast<size_t>(parts * num_q_heads);
+  return PKV_WORKSPACE_COUNTER_BYTES + pkv_host::round_up256(rows * head_dim * 4) +
+         pkv_host::round_up256(rows * 4);
+}
+
 static pkv_status_t decode_impl(const void* q, const void* q_succ, const void* q_inter,
                                 int32_t dca_chunk, const float* q_scale, int32_t dtype,
                                 const void* k_cache, const void* v_cache, int64_t num_pages,
@@ -133,7 +155,9 @@ static pkv_status_t decode_impl(const void* q, const void* q_succ, const void* q
                                 int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                                 float softmax_scale, int32_t window_left, int32_t attn_chunk,
                                 int32_t kv_chunk, int32_t num_splits, float* o_partial,
-                                float* lse_partial, void* out, float* lse, void* stream) {
+                                float* lse_partial, void* out, float* lse, void* stream,
+                                bool merged = false, void* workspace = nullptr,
+                                size_t workspace_bytes = 0) {
   PKV_REQUIRE(dtype == PKV_F32 || dtype == PKV_BF16, PKV_EUNSUPPORTED,
               "decode: dtype %d not supported", dtype);
   PKV_REQUIRE(head_dim == 64 || head_dim == 128, PKV_EUNSUPPORTED,
@@ -158,8 +182,10 @@ static pkv_status_t decode_impl(const void* q, const void* q_succ, const void* q
               "decode: kv_chunk %d is not a multiple of page_size %d", kv_chunk, page_size);
   PKV_REQUIRE(kv_chunk % 32 == 0, PKV_EINVAL, "decode: kv_chunk %d is not a multiple of 32",
               kv_chunk);
-  PKV_REQUIRE(num_splits >= 1, PKV_EINVAL, "decode: num_splits %d < 1", num_splits);
-  PKV_REQUIRE(kv_chunk > 0 || num_splits == 1, PKV_EINVAL,
+  // merged decode: kv_chunk 0 with num_splits 0 asks for balanced ranges
+  const bool balanced = merged && kv_chunk == 0 && num_splits == 0;
+  PKV_REQUIRE(num_splits >= 1 || balanced, PKV_EINVAL, "decode: num_splits %d < 1", num_splits);
+  PKV_REQUIRE(kv_chunk > 0 || num_splits <= 1, PKV_EINVAL,
               "decode: kv_chunk 0 (one split) needs num_splits 1, got %d", num_splits);
   PKV_REQUIRE(dca_chunk >= 0, PKV_EINVAL, "decode: chunk_len %d < 0", dca_chunk);
   if (dca_chunk > 0) {
@@ -173,13 +199,18 @@ static pkv_status_t decode_impl(const void* q, const void* q_succ, const void* q
               "decode: NULL required pointer");
   PKV_REQUIRE(dca_chunk == 0 || (q_succ && q_inter), PKV_EINVAL,
               "decode: dual chunk attention needs q_succ and q_inter");
-  if (num_splits == 1) {
-    PKV_REQUIRE(out != nullptr, PKV_EINVAL, "decode: num_splits 1 needs out");
+  if (num_splits == 1 || merged) {
+    PKV_REQUIRE(out != nullptr, PKV_EINVAL, "decode: out is NULL");
   } else {
     PKV_REQUIRE(o_partial && lse_partial, PKV_EINVAL,
                 "decode: num_splits %d needs o_partial and lse_partial", num_splits);
   }
-  const int64_t grid = static_cast<int64_t>(num_kv_heads) * batch * num_splits;
+  const size_t ws_need = decode_merged_ws_bytes(batch, num_q_heads, head_dim, num_splits);
+  if (merged && ws_need > 0) {
+    PKV_REQUIRE(workspace != nullptr && workspace_bytes >= ws_need, PKV_EINVAL,
+                "decode: workspace of %zu bytes given, %zu needed", workspace_bytes, ws_need);
+  }
+  const int64_t grid = static_cast<int64_t>(num_kv_heads) * batch * max(num_splits, 1);
   PKV_REQUIRE(grid <= 0x7fffffff, PKV_EUNSUPPORTED, "decode: grid too large");
   const int64_t cap = static_cast<int64_t>(pt_stride) * page_size;
   pkv::DecodeArgs a;
@@ -200,6 +231,7 @@ static pkv_status_t decode_impl(const void* q, const void* q_succ, const void* q
                          : static_cast<int32_t>(((cap < 0x40000000LL ? cap : 0x40000000LL) + 31) /
                                                 32 * 32);
   a.num_splits = num_splits;
+  a.units = 0;
   a.window_left = window_left;
   a.attn_chunk = attn_chunk;
   a.q_succ = q_succ;
@@ -210,9 +242,54 @@ static pkv_status_t decode_impl(const void* q, const void* q_succ, const void* q
   a.lse_part = lse_partial;
   a.out = out;
   a.lse = lse;
+  a.counters = nullptr;
+  bool merge_after = false;
+  if (merged && num_splits != 1) {
+    // partials in the workspace after its counter region; the group kernel
+    // merges them itself when its counters fit, else merge_state follows
+    char* ws = static_cast<char*>(workspace);
+    const int64_t parts = balanced ? kBalancedSlots + kBalancedMaxSplits * int64_t{batch}
+                                   : int64_t{num_splits} * batch;
+    const int64_t rows = parts * num_q_heads;
+    a.o_part = reinterpret_cast<float*>(ws + PKV_WORKSPACE_COUNTER_BYTES);
+    a.lse_part = reinterpret_cast<float*>(ws + PKV_WORKSPACE_COUNTER_BYTES +
+                                          pkv_host::round_up256(static_cast<size_t>(rows) * head_dim * 4));
+    const int groups = pkv_launch::decode_groups(a, dtype, head_dim);
+    const bool counters_fit = static_cast<int64_t>(batch) * groups * 4 <= PKV_WORKSPACE_COUNTER_BYTES;
+    if (balanced && groups > 0 && counters_fit && cap <= kBalancedMaxKeys) {
+      a.units = (kBalancedSlots + groups - 1) / groups;
+      a.num_splits = 2;   // (not read in this mode; anything but one split)
+      a.counters = reinterpret_cast<int*>(ws);
+    } else {
+      if (balanced) {
+        // fixed splits instead: at most eight, on whole pages and tiles
+        int64_t unit = page_size;
+        while (unit % 32 != 0) unit += page_size;
+        const int64_t per = (cap + kBalancedMaxSplits - 1) / kBalancedMaxSplits;
+        const int64_t chunk = (per + unit - 1) / unit * unit;
+        PKV_REQUIRE(chunk <= 0x7fffffff, PKV_EUNSUPPORTED, "decode: key capacity too large");
+        a.chunk = static_cast<int32_t>(chunk);
+        a.num_splits = static_cast<int32_t>((cap + chunk - 1) / chunk);
+        num_splits = a.num_splits;
+      }
+      if (a.num_splits == 1) {
+        a.out = out;   // one split: written directly
+      } else if (groups > 0 && counters_fit) {
+        a.counters = reinterpret_cast<int*>(ws);
+      } else {
+        merge_after = true;
+      }
+    }
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const pkv_status_t r =
+      pkv_host::from_hip(pkv_launch::decode_splitkv(a, dtype, head_dim, st), "decode launch");
+  if (r != PKV_OK || !merge_after) return r;
   return pkv_host::from_hip(
-      pkv_launch::decode_splitkv(a, dtype, head_dim, static_cast<hipStream_t>(stream)),
-      "decode launch");
+      pkv_launch::merge_state(a.o_part, a.lse_part, num_splits,
+                              static_cast<int64_t>(batch) * num_q_heads, head_dim, out, dtype,
+                              lse, st),
+      "merge_state launch");
 }
 
 extern "C" {
@@ -303,6 +380,26 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
                      page_table, pt_stride, kv_lens, batch, num_q_heads, num_kv_heads, head_dim,
                      page_size, softmax_scale, window_left, attn_chunk, kv_chunk, num_splits,
                      o_partial, lse_partial, out, lse, stream);
+}
+
+size_t paged_attn_decode_merged_workspace_size(int32_t batch, int32_t num_q_heads,
+                                               int32_t head_dim, int32_t num_splits) {
+  return decode_merged_ws_bytes(batch, num_q_heads, head_dim, num_splits);
+}
+
+pkv_status_t paged_attn_decode_merged(const void* q, int32_t dtype, const void* k_cache,
+                                      const void* v_cache, int64_t num_pages,
+                                      const int32_t* page_table, int32_t pt_stride,
+                                      const int32_t* kv_lens, int32_t batch, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                      float softmax_scale, int32_t window_left, int32_t attn_chunk,
+                                      int32_t kv_chunk, int32_t num_splits, void* workspace,
+                                      size_t workspace_bytes, void* out, float* lse,
+                                      void* stream) {
+  return decode_impl(q, nullptr, nullptr, 0, nullptr, dtype, k_cache, v_cache, num_pages,
+                     page_table, pt_stride, kv_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                     page_size, softmax_scale, window_left, attn_chunk, kv_chunk, num_splits,
+                     nullptr, nullptr, out, lse, stream, true, workspace, workspace_bytes);
 }
 
 pkv_status_t paged_attn_dca_decode(const void* q, const void* q_succ, const void* q_inter,

@@ -43,6 +43,14 @@ struct DecodeArgs {
   const void* q_inter;
   int32_t dca_chunk;
   const float* q_scale;   // [B] factors applied to the queries (rounded back), or null
+  // merged decode (num_splits > 1): completion counters, one per (request,
+  // kv-head group), in a zeroed workspace; the last non-empty split of each
+  // merges o_part / lse_part into out / lse. Null: partials only.
+  int* counters;
+  // > 0 (merged decode, bf16 kv-head groups): the visible keys of the batch
+  // are cut into this many equal ranges per group instead of fixed splits;
+  // partial rows [units + batch, Hq] in o_part / lse_part
+  int32_t units;
 };
 
 // Query a split scores its keys with: q, or under dual chunk attention the

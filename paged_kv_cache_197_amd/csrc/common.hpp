@@ -131,6 +131,26 @@ __device__ __forceinline__ void counter_reset(int* c) {
   __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// LSE-weighted combine of partial states, one part at a time in split order:
+// m = max of the parts' LSEs, w = exp(lse - m), acc += w * o, total += w,
+// out = acc / total, lse_out = m + ln(total). Parts of weight 0 (empty
+// splits: lse = -inf) are skipped. merge_state and the merged decode both go
+// through these, so the two give the same bits.
+__device__ __forceinline__ float merge_weight(float lse_part, float m) {
+  return fast_exp2((lse_part - m) * kLog2e);
+}
+template <int N>
+__device__ __forceinline__ void merge_add(float w, const float (&v)[N], float (&acc)[N],
+                                          float& total) {
+  total += w;
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = __builtin_fmaf(w, v[i], acc[i]);
+}
+__device__ __forceinline__ float merge_norm(float total) { return total > 0.f ? 1.f / total : 0.f; }
+__device__ __forceinline__ float merge_lse(float m, float total) {
+  return m == neg_inf() ? neg_inf() : __builtin_fmaf(fast_log2(total), kLn2, m);
+}
+
 // Clamp an index read from device memory into [0, n): a violated precondition
 // turns into a wrong (but in-bounds) access instead of a fault.
 __device__ __forceinline__ int64_t clamp_index(int64_t i, int64_t n) {

@@ -683,51 +683,98 @@ struct DecodeGroupKernel {
 
   // EXT: the variant with a lower key bound (sliding window, local chunks)
   // and the per-split query choice and scaling of dual chunk attention.
+  // Merge of a request's parts for the group's ncol heads, run by the last
+  // part to finish: n parts whose rows start at part_row + k * part_stride
+  // (k in order), read back at device scope from o_part / lse_part, combined
+  // in that order with the arithmetic of merge_state and written to out / lse
+  // rows out_row .. out_row + ncol. Thread t takes column t / (D / 8), dims
+  // 8 (t % (D / 8)) + [0, 8).
+  static __device__ __forceinline__ void merge_parts(const DecodeArgs& a, int64_t part_row, int64_t part_stride,
+                                     int n, int64_t out_row, int ncol) {
+    constexpr int PER_COL = D / 8;
+    constexpr int BATCH = 8;
+    const int c2 = threadIdx.x / PER_COL;
+    const int dq = (threadIdx.x % PER_COL) * 8;
+    if (c2 >= ncol) return;
+    auto lse_of = [&](int k) {
+      const auto r = coherent_rsrc(a.lse_part + part_row + k * part_stride,
+                                   static_cast<uint32_t>(ncol * 4));
+      return load_coherent1(r, static_cast<uint32_t>(c2 * 4));
+    };
+    float m = neg_inf();
+    for (int k0 = 0; k0 < n; k0 += BATCH) {
+      float ls[BATCH];
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) ls[q] = (k0 + q < n) ? lse_of(k0 + q) : neg_inf();
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) m = fmaxf(m, ls[q]);
+    }
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    float total = 0.f;
+    if (m != neg_inf()) {
+      for (int k0 = 0; k0 < n; k0 += BATCH) {
+        float ls[BATCH];
+        f32x4 v[BATCH][2];
+#pragma unroll
+        for (int q = 0; q < BATCH; ++q) {
+          if (k0 + q < n) {
+            const auto r = coherent_rsrc(a.o_part + (part_row + (k0 + q) * part_stride) * D,
+                                         static_cast<uint32_t>(ncol * D * 4));
+            const uint32_t off = static_cast<uint32_t>((c2 * D + dq) * 4);
+            v[q][0] = load_coherent4(r, off);
+            v[q][1] = load_coherent4(r, off + 16);
+            ls[q] = lse_of(k0 + q);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < BATCH; ++q) {
+          if (k0 + q >= n) break;
+          const float w = merge_weight(ls[q], m);
+          if (w == 0.f) continue;
+          const float vv[8] = {v[q][0][0], v[q][0][1], v[q][0][2], v[q][0][3],
+                               v[q][1][0], v[q][1][1], v[q][1][2], v[q][1][3]};
+          merge_add(w, vv, acc, total);
+        }
+      }
+    }
+    const float inv = merge_norm(total);
+    const u32x4 w4 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                      pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+    *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(a.out) + (out_row + c2) * D + dq) = w4;
+    if (a.lse != nullptr && dq == 0) a.lse[out_row + c2] = merge_lse(m, total);
+  }
+
+  // One lane's share of an attend() result: the normalised output of column
+  // c, dims d0 + [0, 8), and the column's LSE; each (column, dims) piece has
+  // exactly one owner lane, and lse_lane marks one owner per column.
+  struct Piece {
+    float o[8];
+    float lse;
+    int d0;
+    bool owner;
+    bool lse_lane;
+  };
+
+  // Attention of group grp's query heads over keys [start, end) of request b
+  // (start a multiple of TT; keys below lo masked; end > max(start, lo)),
+  // with query rows from qsrc. Wave w takes tiles w, w+4, ... and keeps its own
+  // state; the four states are merged through LDS. Every thread passes a
+  // workgroup barrier after the last LDS read, so LDS may be reused at once.
   template <bool UNIFORM, bool EXT>
-  static __device__ void run(const DecodeArgs& a) {
+  static __device__ __forceinline__ void attend(const DecodeArgs& a, const void* qsrc, int b, int grp, int start,
+                                int end, int lo, Piece& pc) {
     extern __shared__ __align__(16) char smem[];
     __shared__ float sm_m[4][16];
     __shared__ float sm_l[4][16];
-
     const int G = a.hq / a.hkv;
-    const int ngrp = a.hkv / HPW;
-    const int grp = blockIdx.x % ngrp;
     const int lane = threadIdx.x & 63;
-    const SplitPick pick = pick_split(a, blockIdx.x / ngrp, EXT, lane);
-    const int b = __builtin_amdgcn_readfirstlane(pick.b);
-    const int s = __builtin_amdgcn_readfirstlane(pick.s);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15;
     const int g = lane >> 4;
     const int ncol = HPW * G;                 // query heads of the group
     const int h0 = grp * ncol;                // first query head of the group
-
-    const int L = __builtin_amdgcn_readfirstlane(pick.L);
-    const int start0 = static_cast<int>(min<int64_t>(static_cast<int64_t>(s) * a.chunk, L));
-    const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(start0) + a.chunk, L));
-    // first visible key under a sliding window / local chunks; tiles start on
-    // a multiple of TT (splits do), keys below lo are masked
-    const int lo = (EXT && L > 0) ? key_lower_bound(L - 1, a.window_left, a.attn_chunk) : 0;
-    const int start = EXT ? max(start0, lo / TT * TT) : start0;
-    const bool single = (a.num_splits == 1);
-
-    if (max(start0, lo) >= end) {   // empty split: (0, -inf)
-      for (int i = threadIdx.x; i < ncol * D; i += blockDim.x) {
-        const int64_t row = static_cast<int64_t>(b) * a.hq + h0 + i / D;
-        const int d = i % D;
-        if (single) static_cast<bf16_t*>(a.out)[row * D + d].bits = 0;
-        else a.o_part[(static_cast<int64_t>(s) * a.batch * a.hq + row) * D + d] = 0.f;
-      }
-      for (int i = threadIdx.x; i < ncol; i += blockDim.x) {
-        const int64_t row = static_cast<int64_t>(b) * a.hq + h0 + i;
-        if (single) {
-          if (a.lse) a.lse[row] = neg_inf();
-        } else {
-          a.lse_part[static_cast<int64_t>(s) * a.batch * a.hq + row] = neg_inf();
-        }
-      }
-      return;
-    }
 
     // Qpad^T operand, k-step j: dims 32j + 8g + [0, 8) of the virtual row,
     // nonzero only where they belong to column c's kv head.
@@ -735,7 +782,6 @@ struct DecodeGroupKernel {
     u32x4 qop[8];
     {
       const int head = h0 + min(c, ncol - 1);
-      const void* qsrc = EXT ? split_query(a, start0, L) : a.q;
       const char* qrow = static_cast<const char*>(qsrc) + (static_cast<int64_t>(b) * a.hq + head) * D * 2;
 #pragma unroll
       for (int j = 0; j < 8; ++j) qop[j] = *reinterpret_cast<const u32x4*>(qrow + ((32 * j + 8 * g) % D) * 2);
@@ -822,59 +868,294 @@ struct DecodeGroupKernel {
     // 128 h + 32 g + 8 i + [0, 8); it is the owner when they are column c's.
     const int i = wave;
     const int hsel = (HPW == 2) ? kk : (kk >> 1);
-    const bool owner = (c < ncol) && (HPW == 2 || ((g >> 1) == (kk & 1)));
-    if (!owner) return;
-    float M = sm_m[0][c];
+    pc.owner = (c < ncol) && (HPW == 2 || ((g >> 1) == (kk & 1)));
+    pc.d0 = (32 * g + 8 * i) % D;
+    pc.lse_lane = (i == 0) && (pc.d0 == 0);
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][c]);
-    float f[4];
-    float Ltot = 0.f;
+    for (int e = 0; e < 8; ++e) pc.o[e] = 0.f;
+    pc.lse = 0.f;
+    if (pc.owner) {
+      float M = sm_m[0][c];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      f[w] = (sm_m[w][c] == neg_inf()) ? 0.f : fast_exp2(sm_m[w][c] - M);
-      Ltot += f[w] * sm_l[w][c];
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][c]);
+      float f[4];
+      float Ltot = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        f[w] = (sm_m[w][c] == neg_inf()) ? 0.f : fast_exp2(sm_m[w][c] - M);
+        Ltot += f[w] * sm_l[w][c];
+      }
+      const float inv = 1.f / Ltot;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float4* reg = reinterpret_cast<const float4*>(smem + w * WAVE_LDS) + lane * 16;
+        const float4 u0 = reg[(4 * i + 2 * hsel) ^ c];
+        const float4 u1 = reg[(4 * i + 2 * hsel + 1) ^ c];
+        pc.o[0] += f[w] * u0.x;
+        pc.o[1] += f[w] * u0.y;
+        pc.o[2] += f[w] * u0.z;
+        pc.o[3] += f[w] * u0.w;
+        pc.o[4] += f[w] * u1.x;
+        pc.o[5] += f[w] * u1.y;
+        pc.o[6] += f[w] * u1.z;
+        pc.o[7] += f[w] * u1.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pc.o[e] *= inv;
+      pc.lse = (M + fast_log2(Ltot)) * kLn2;
     }
-    const float inv = 1.f / Ltot;
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float4* reg = reinterpret_cast<const float4*>(smem + w * WAVE_LDS) + lane * 16;
-      const float4 u0 = reg[(4 * i + 2 * hsel) ^ c];
-      const float4 u1 = reg[(4 * i + 2 * hsel + 1) ^ c];
-      o[0] += f[w] * u0.x;
-      o[1] += f[w] * u0.y;
-      o[2] += f[w] * u0.z;
-      o[3] += f[w] * u0.w;
-      o[4] += f[w] * u1.x;
-      o[5] += f[w] * u1.y;
-      o[6] += f[w] * u1.z;
-      o[7] += f[w] * u1.w;
+    __syncthreads();   // LDS free for the caller
+  }
+
+  // Final output of column c of the group from a Piece (owner lanes).
+  static __device__ __forceinline__ void write_out(const DecodeArgs& a, int64_t row,
+                                                   const Piece& pc) {
+    if (!pc.owner) return;
+    const u32x4 w4 = {pack_bf16x2(pc.o[0], pc.o[1]), pack_bf16x2(pc.o[2], pc.o[3]),
+                      pack_bf16x2(pc.o[4], pc.o[5]), pack_bf16x2(pc.o[6], pc.o[7])};
+    *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(a.out) + row * D + pc.d0) = w4;
+    if (a.lse != nullptr && pc.lse_lane) a.lse[row] = pc.lse;
+  }
+
+  // (0, -inf) for the group's columns of request b (no visible key)
+  static __device__ __forceinline__ void write_empty(const DecodeArgs& a, int b, int h0, int ncol) {
+    for (int i = threadIdx.x; i < ncol * D; i += blockDim.x)
+      static_cast<bf16_t*>(a.out)[(static_cast<int64_t>(b) * a.hq + h0 + i / D) * D + i % D].bits = 0;
+    if (a.lse != nullptr)
+      for (int i = threadIdx.x; i < ncol; i += blockDim.x)
+        a.lse[static_cast<int64_t>(b) * a.hq + h0 + i] = neg_inf();
+  }
+
+  // Hand a part over at device scope (rows part_row0 + column), count it on
+  // `counter`; the part that completes the count (n parts) merges the parts
+  // [first_row + k * stride] into the output rows of request b.
+  static __device__ __forceinline__ void hand_over(const DecodeArgs& a, const Piece& pc, int64_t part_row0,
+                                   int ncol, int* counter, int n, int64_t first_row,
+                                   int64_t stride, int64_t out_row) {
+    __shared__ int sm_last;
+    const int c = threadIdx.x & 15;
+    if (pc.owner) {
+      const auto ro = coherent_rsrc(a.o_part + part_row0 * D, static_cast<uint32_t>(ncol * D * 4));
+      const uint32_t off = static_cast<uint32_t>((c * D + pc.d0) * 4);
+      store_coherent(ro, off, f32x4{pc.o[0], pc.o[1], pc.o[2], pc.o[3]});
+      store_coherent(ro, off + 16, f32x4{pc.o[4], pc.o[5], pc.o[6], pc.o[7]});
+      if (pc.lse_lane)
+        store_coherent(coherent_rsrc(a.lse_part + part_row0, static_cast<uint32_t>(ncol * 4)),
+                       static_cast<uint32_t>(c * 4), pc.lse);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] *= inv;
-    const int d0 = (32 * g + 8 * i) % D;
-    const int64_t row = static_cast<int64_t>(b) * a.hq + h0 + c;
-    const float lse_val = (M + fast_log2(Ltot)) * kLn2;
-    const bool lse_lane = (i == 0) && (d0 == 0);
+    wait_all_vmem();
+    __syncthreads();   // every wave's share has been written through
+    if (threadIdx.x == 0) sm_last = (counter_add(counter, 1) == n - 1);
+    __syncthreads();
+    if (!sm_last) return;
+    merge_parts(a, first_row, stride, n, out_row, ncol);
+    if (threadIdx.x == 0) counter_reset(counter);   // ready for the next call
+  }
+
+  // Fixed splits: workgroup (unit, group) takes split s of request b (the
+  // order of pick_split); partials to o_part / lse_part [S, B, Hq], or merged
+  // in the launch when counters are given.
+  template <bool UNIFORM, bool EXT>
+  static __device__ __forceinline__ void run_fixed(const DecodeArgs& a) {
+    const int G = a.hq / a.hkv;
+    const int ngrp = a.hkv / HPW;
+    const int grp = blockIdx.x % ngrp;
+    const int lane = threadIdx.x & 63;
+    const SplitPick pick = pick_split(a, blockIdx.x / ngrp, EXT, lane);
+    const int b = __builtin_amdgcn_readfirstlane(pick.b);
+    const int s = __builtin_amdgcn_readfirstlane(pick.s);
+    const int c = lane & 15;
+    const int ncol = HPW * G;                 // query heads of the group
+    const int h0 = grp * ncol;                // first query head of the group
+
+    const int L = __builtin_amdgcn_readfirstlane(pick.L);
+    const int start0 = static_cast<int>(min<int64_t>(static_cast<int64_t>(s) * a.chunk, L));
+    const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(start0) + a.chunk, L));
+    // first visible key under a sliding window / local chunks; tiles start on
+    // a multiple of TT (splits do), keys below lo are masked
+    const int lo = (EXT && L > 0) ? key_lower_bound(L - 1, a.window_left, a.attn_chunk) : 0;
+    const int start = EXT ? max(start0, lo / TT * TT) : start0;
+    const bool single = (a.num_splits == 1);
+    // merged decode: the request's non-empty splits are [sf, sf + n_ne)
+    const bool merged = (a.counters != nullptr) && !single;
+    const int v1 = static_cast<int>(min<int64_t>(L, static_cast<int64_t>(a.num_splits) * a.chunk));
+    const int v0 = min(lo, v1);
+    const int sf = v0 / a.chunk;
+    const int n_ne = v0 < v1 ? (v1 - 1) / a.chunk - sf + 1 : 0;
+
+    if (max(start0, lo) >= end) {   // empty split: (0, -inf)
+      if (merged) {
+        // nothing to hand over; a request with no visible key at all gets
+        // (0, -inf) from its split 0
+        if (n_ne == 0 && s == 0) write_empty(a, b, h0, ncol);
+        return;
+      }
+      for (int i = threadIdx.x; i < ncol * D; i += blockDim.x) {
+        const int64_t row = static_cast<int64_t>(b) * a.hq + h0 + i / D;
+        const int d = i % D;
+        if (single) static_cast<bf16_t*>(a.out)[row * D + d].bits = 0;
+        else a.o_part[(static_cast<int64_t>(s) * a.batch * a.hq + row) * D + d] = 0.f;
+      }
+      for (int i = threadIdx.x; i < ncol; i += blockDim.x) {
+        const int64_t row = static_cast<int64_t>(b) * a.hq + h0 + i;
+        if (single) {
+          if (a.lse) a.lse[row] = neg_inf();
+        } else {
+          a.lse_part[static_cast<int64_t>(s) * a.batch * a.hq + row] = neg_inf();
+        }
+      }
+      return;
+    }
+
+    Piece pc;
+    attend<UNIFORM, EXT>(a, EXT ? split_query(a, start0, L) : a.q, b, grp, start, end, lo, pc);
+    const int64_t out_row0 = static_cast<int64_t>(b) * a.hq + h0;
+    const int64_t split_rows = static_cast<int64_t>(a.batch) * a.hq;
+    if (merged) {
+      hand_over(a, pc, s * split_rows + out_row0, ncol, a.counters + static_cast<int64_t>(b) * ngrp + grp,
+                n_ne, sf * split_rows + out_row0, split_rows, out_row0);
+      return;
+    }
     if (single) {
-      u32x4 w4 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                  pack_bf16x2(o[6], o[7])};
-      *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(a.out) + row * D + d0) = w4;
-      if (a.lse != nullptr && lse_lane) a.lse[row] = lse_val;
-    } else {
-      float* dst = a.o_part + (static_cast<int64_t>(s) * a.batch * a.hq + row) * D + d0;
-      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
-      if (lse_lane) a.lse_part[static_cast<int64_t>(s) * a.batch * a.hq + row] = lse_val;
+      write_out(a, out_row0 + c, pc);
+    } else if (pc.owner) {
+      float* dst = a.o_part + (s * split_rows + out_row0 + c) * D + pc.d0;
+      *reinterpret_cast<float4*>(dst) = make_float4(pc.o[0], pc.o[1], pc.o[2], pc.o[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(pc.o[4], pc.o[5], pc.o[6], pc.o[7]);
+      if (pc.lse_lane) a.lse_part[s * split_rows + out_row0 + c] = pc.lse;
     }
+  }
+
+  // Balanced ranges (merged decode with a.units > 0): the visible keys of all
+  // requests, in TT-key tiles from the tile that holds each request's first
+  // visible key, are laid end to end and cut into a.units ranges of equal
+  // tile count (at least kMinRangeTiles each; later ranges may be empty).
+  // Workgroup (range r, group) walks the requests its range covers; a request
+  // covered by one range is written directly, else each range's part goes to
+  // partial row r + b (unique: ranges follow the requests' order) and the last
+  // of the request's ranges to finish merges them in range order.
+  static constexpr int kMinRangeTiles = 8;
+
+  template <bool EXT>
+  static __device__ __forceinline__ void visible(const DecodeArgs& a, int j, int& L, int& v0,
+                                                 int& nt) {
+    const int64_t cap = static_cast<int64_t>(a.pt_stride) * a.page_size;
+    L = (j < a.batch) ? static_cast<int>(min<int64_t>(max(a.kv_lens[j], 0), cap)) : 0;
+    v0 = (EXT && L > 0) ? key_lower_bound(L - 1, a.window_left, a.attn_chunk) : 0;
+    nt = (L > v0) ? (L - 1) / TT - v0 / TT + 1 : 0;
+  }
+
+  template <bool UNIFORM, bool EXT>
+  static __device__ __forceinline__ void run_balanced(const DecodeArgs& a) {
+    const int G = a.hq / a.hkv;
+    const int ngrp = a.hkv / HPW;
+    const int grp = blockIdx.x % ngrp;
+    const int r = blockIdx.x / ngrp;
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15;
+    const int ncol = HPW * G;
+    const int h0 = grp * ncol;
+
+    // total tiles; requests with no visible key get (0, -inf) from range 0
+    int64_t NT = 0;
+    for (int j0 = 0; j0 < a.batch; j0 += 64) {
+      int L, v0, nt;
+      visible<EXT>(a, j0 + lane, L, v0, nt);
+      int x = nt;
+#pragma unroll
+      for (int d = 1; d < 64; d *= 2) x += __shfl_xor(x, d);
+      NT += __builtin_amdgcn_readfirstlane(x);
+      if (r == 0) {
+        unsigned long long none = __ballot(j0 + lane < a.batch && nt == 0);
+        while (none) {
+          const int k = __builtin_ctzll(none);
+          none &= none - 1;
+          write_empty(a, j0 + k, h0, ncol);
+        }
+      }
+    }
+    const int64_t units = max<int64_t>(1, min<int64_t>(a.units, NT / kMinRangeTiles));
+    if (r >= units) return;
+    const int64_t t0 = r * NT / units;
+    const int64_t t1 = (r + 1) * NT / units;
+    // range holding global tile t: the largest q with floor(q NT / units) <= t
+    auto range_of = [&](int64_t t) { return static_cast<int>(((t + 1) * units - 1) / NT); };
+
+    // the request holding tile t0 (b) and its first global tile (pb)
+    int b = a.batch;
+    int64_t pb = 0;
+    {
+      int64_t base = 0;
+      for (int j0 = 0; j0 < a.batch; j0 += 64) {
+        int L, v0, nt;
+        visible<EXT>(a, j0 + lane, L, v0, nt);
+        int incl = nt;
+#pragma unroll
+        for (int d = 1; d < 64; d *= 2) {
+          const int y = __shfl_up(incl, d);
+          if (lane >= d) incl += y;
+        }
+        const int64_t lo_t = base + incl - nt;
+        const unsigned long long hit = __ballot(nt > 0 && lo_t <= t0 && t0 < lo_t + nt);
+        if (hit) {
+          const int k = __builtin_ctzll(hit);
+          b = j0 + k;
+          pb = base + __builtin_amdgcn_readlane(incl - nt, k);
+          break;
+        }
+        base += __builtin_amdgcn_readlane(incl, 63);
+      }
+    }
+
+    // walk the requests the range covers; only scalar state crosses a segment
+    // (each segment reads the arguments again from the kernel's argument
+    // segment, where `a` lives, through a pointer the compiler cannot follow,
+    // so that they are not all held in registers across the segments)
+    typedef const __attribute__((address_space(4))) DecodeArgs* KArgPtr;
+    int64_t pos = t0;
+    const int batch = a.batch;
+    while (pos < t1 && b < batch) {
+      KArgPtr ap = (KArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+      asm volatile("" : "+s"(ap));
+      const DecodeArgs a = *(const DecodeArgs*)ap;
+      int Lb, v0b, ntb;
+      visible<EXT>(a, b, Lb, v0b, ntb);
+      if (ntb > 0) {
+        const int lt0 = static_cast<int>(pos - pb);
+        const int lt1 = static_cast<int>(min(t1, pb + ntb) - pb);
+        const int first_key = v0b / TT * TT;
+        const int start = first_key + TT * lt0;
+        const int end = min(first_key + TT * lt1, Lb);
+        Piece pc;
+        attend<UNIFORM, EXT>(a, a.q, b, grp, start, end, v0b, pc);
+        const int r_first = range_of(pb);
+        const int r_last = range_of(pb + ntb - 1);
+        const int64_t out_row0 = static_cast<int64_t>(b) * a.hq + h0;
+        if (r_first == r_last) {
+          write_out(a, out_row0 + c, pc);
+        } else {
+          hand_over(a, pc, static_cast<int64_t>(r + b) * a.hq + h0, ncol,
+                    a.counters + static_cast<int64_t>(b) * ngrp + grp, r_last - r_first + 1,
+                    static_cast<int64_t>(r_first + b) * a.hq + h0, a.hq, out_row0);
+        }
+        pos = pb + lt1;
+        pb += ntb;
+      }
+      ++b;
+    }
+  }
+
+  template <bool UNIFORM, bool EXT, bool BAL>
+  static __device__ void run(const DecodeArgs& a) {
+    if constexpr (BAL) run_balanced<UNIFORM, EXT>(a);
+    else run_fixed<UNIFORM, EXT>(a);
   }
 };
 
-template <int D, bool UNIFORM, bool EXT>
+// BAL: balanced ranges (merged decode) instead of fixed splits
+template <int D, bool UNIFORM, bool EXT, bool BAL>
 __global__ __launch_bounds__(256, 2) void decode_group_kernel(DecodeArgs a) {
-  DecodeGroupKernel<D>::template run<UNIFORM, EXT>(a);
+  DecodeGroupKernel<D>::template run<UNIFORM, EXT, BAL>(a);
 }
 
 // bf16 tiles fit two workgroups per CU (<= 256 VGPRs); fp32 tiles are twice
@@ -912,10 +1193,9 @@ static hipError_t launch_decode_t(const pkv::DecodeArgs& a, bool uniform, hipStr
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_decode_group(const pkv::DecodeArgs& a, hipStream_t stream) {
-  constexpr int HPW = pkv::DecodeGroupKernel<D>::HPW;
-  const dim3 grid(static_cast<unsigned>(a.hkv / HPW) * a.batch * a.num_splits);
+template <int D, bool BAL>
+static hipError_t launch_decode_group_t(const pkv::DecodeArgs& a, const dim3 grid,
+                                        hipStream_t stream) {
   constexpr unsigned lds = pkv::DecodeGroupKernel<D>::LDS_BYTES;
   // whole 16-token tiles on one page: page_size % 16 == 0 (splits start on pages)
   // (a sliding window, local chunks or dual chunk attention take the variant
@@ -924,33 +1204,49 @@ static hipError_t launch_decode_group(const pkv::DecodeArgs& a, hipStream_t stre
                       a.q_scale != nullptr;
   if (a.page_size % 16 == 0) {
     if (window)
-      hipLaunchKernelGGL((pkv::decode_group_kernel<D, true, true>), grid, dim3(256), lds, stream, a);
+      hipLaunchKernelGGL((pkv::decode_group_kernel<D, true, true, BAL>), grid, dim3(256), lds,
+                         stream, a);
     else
-      hipLaunchKernelGGL((pkv::decode_group_kernel<D, true, false>), grid, dim3(256), lds, stream,
-                         a);
+      hipLaunchKernelGGL((pkv::decode_group_kernel<D, true, false, BAL>), grid, dim3(256), lds,
+                         stream, a);
   } else {
     if (window)
-      hipLaunchKernelGGL((pkv::decode_group_kernel<D, false, true>), grid, dim3(256), lds, stream,
-                         a);
+      hipLaunchKernelGGL((pkv::decode_group_kernel<D, false, true, BAL>), grid, dim3(256), lds,
+                         stream, a);
     else
-      hipLaunchKernelGGL((pkv::decode_group_kernel<D, false, false>), grid, dim3(256), lds, stream,
-                         a);
+      hipLaunchKernelGGL((pkv::decode_group_kernel<D, false, false, BAL>), grid, dim3(256), lds,
+                         stream, a);
   }
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_decode_group(const pkv::DecodeArgs& a, hipStream_t stream) {
+  constexpr int HPW = pkv::DecodeGroupKernel<D>::HPW;
+  const unsigned groups = static_cast<unsigned>(a.hkv / HPW);
+  if (a.units > 0)
+    return launch_decode_group_t<D, true>(a, dim3(groups * static_cast<unsigned>(a.units)), stream);
+  return launch_decode_group_t<D, false>(
+      a, dim3(groups * static_cast<unsigned>(a.batch) * a.num_splits), stream);
+}
+
+// kv-head groups (bf16): HPW = 256 / D heads whose G query heads fit 16
+// columns, and slot numbers that fit 32 bits (per-token pages are shuffled as
+// int32). Returns the number of groups per request, or 0 when the general
+// kernel runs instead.
+int decode_groups(const pkv::DecodeArgs& a, int dtype, int head_dim) {
+  if (dtype != PKV_BF16) return 0;
+  const int hpw = 256 / head_dim;
+  const int G = a.hq / a.hkv;
+  const bool group = (a.hkv % hpw == 0) && (hpw * G <= 16) &&
+                     (a.num_pages * a.page_size <= INT_MAX);
+  return group ? a.hkv / hpw : 0;
+}
+
 hipError_t decode_splitkv(const pkv::DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
-  if (dtype == PKV_BF16) {
-    // kv-head groups: HPW = 256 / D heads whose G query heads fit 16 columns,
-    // and slot numbers that fit 32 bits (per-token pages are shuffled as int32)
-    const int hpw = 256 / head_dim;
-    const int G = a.hq / a.hkv;
-    const bool group = (a.hkv % hpw == 0) && (hpw * G <= 16) &&
-                       (a.num_pages * a.page_size <= INT_MAX);
-    if (group) {
-      if (head_dim == 128) return launch_decode_group<128>(a, stream);
-      return launch_decode_group<64>(a, stream);
-    }
+  if (decode_groups(a, dtype, head_dim) > 0) {
+    if (head_dim == 128) return launch_decode_group<128>(a, stream);
+    return launch_decode_group<64>(a, stream);
   }
   // tiles are 32 tokens starting at multiples of 32 inside a split; with
   // page_size % 32 == 0 and chunk % page_size == 0 a tile never crosses a page

@@ -20,6 +20,9 @@ hipError_t page_table(const pkv::PageTableArgs& a, hipStream_t stream);
 hipError_t merge_state(const float* o_parts, const float* lse_parts, int num_parts, int64_t rows,
                        int dv, void* out, int out_dtype, float* lse_out, hipStream_t stream);
 hipError_t decode_splitkv(const pkv::DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+// kv-head groups per request when the decode runs the bf16 group kernel (the
+// one that can merge its splits itself), else 0
+int decode_groups(const pkv::DecodeArgs& a, int dtype, int head_dim);
 hipError_t prefill(const pkv::PrefillArgs& a, int head_dim, hipStream_t stream);
 hipError_t kv_append(const void* k_new, const void* v_new, const int32_t* loc, int32_t n,
                      int64_t row_bytes, void* k_cache, void* v_cache, int64_t num_slots,

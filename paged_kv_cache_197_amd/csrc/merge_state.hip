@@ -77,16 +77,13 @@ __global__ __launch_bounds__(256) void merge_state_kernel(const float* __restric
 #pragma unroll
       for (int k = 0; k < BATCH; ++k) {
         const int s = min(s0 + k, num_parts - 1);
-        const float w =
-            (s0 + k < num_parts) ? fast_exp2((lse_parts[s * rows + row] - m) * kLog2e) : 0.f;
+        const float w = (s0 + k < num_parts) ? merge_weight(lse_parts[s * rows + row], m) : 0.f;
         if (w == 0.f) continue;
-        total += w;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[i] += w * v[k][i];
+        merge_add(w, v[k], acc, total);
       }
     }
   }
-  const float inv = total > 0.f ? 1.f / total : 0.f;
+  const float inv = merge_norm(total);
   TO* dst = out + row * dv + col;
   if (VEC == 4) {
     store_vec4<TO>(dst, make_float4(acc[0] * inv, acc[1 % VEC] * inv, acc[2 % VEC] * inv,
@@ -95,7 +92,7 @@ __global__ __launch_bounds__(256) void merge_state_kernel(const float* __restric
     store_one(dst, acc[0] * inv);
   }
   if (lse_out != nullptr && col == 0) {
-    lse_out[row] = (m == neg_inf()) ? neg_inf() : m + fast_log2(total) * kLn2;
+    lse_out[row] = merge_lse(m, total);
   }
 }
 

@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
                "sparse_topk_decode_workspace_size", "paged_kv_append",
                "paged_attn_varlen_prefill_append", "build_cascade_expand_table",
                "paged_attn_expand_merge", "paged_attn_cascade", "build_dca_decode_tables",
-               "paged_attn_dca_decode", "sparse_topk_decode_noalloc"]:
+               "paged_attn_dca_decode", "sparse_topk_decode_noalloc",
+               "paged_attn_decode_merged", "paged_attn_decode_merged_workspace_size"]:
         assert fn in names
 
 
@@ -291,3 +292,46 @@ def test_sparse_noalloc_argument_errors():
     assert b"scratch" in lib.pkv_last_error()
     text = open(os.path.join(os.path.dirname(LIB), "..", "include", "pkv.h")).read()
     assert "#define PKV_SPARSE_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
+
+
+def _merged(lib, **kw):
+    a = dict(q=None, dtype=1, k=None, v=None, num_pages=16, pt=None, pt_stride=8, kv_lens=None,
+             batch=2, hq=32, hkv=8, d=128, P=64, scale=0.1, wl=-1, ac=0, chunk=4096, S=2, ws=None,
+             ws_bytes=0, out=None, lse=None, stream=None)
+    a.update(kw)
+    return lib.paged_attn_decode_merged(a["q"], a["dtype"], a["k"], a["v"], a["num_pages"],
+                                        a["pt"], a["pt_stride"], a["kv_lens"], a["batch"], a["hq"],
+                                        a["hkv"], a["d"], a["P"], a["scale"], a["wl"], a["ac"],
+                                        a["chunk"], a["S"], a["ws"], a["ws_bytes"], a["out"],
+                                        a["lse"], a["stream"])
+
+
+def test_merged_decode_workspace_size():
+    """Counter region, then fp32 partials [S, B, Hq, D] and LSEs [S, B, Hq], each
+    rounded up to 256 bytes; nothing for one split or an empty batch."""
+    lib = pkv.load_library()
+    size = lib.paged_attn_decode_merged_workspace_size
+    up = lambda v: (v + 255) // 256 * 256
+    for B, hq, d, S in [(64, 32, 128, 8), (32, 64, 128, 8), (3, 5, 64, 7), (1, 1, 64, 2)]:
+        assert size(B, hq, d, S) == COUNTER_BYTES + up(S * B * hq * d * 4) + up(S * B * hq * 4)
+    assert size(64, 32, 128, 1) == 0
+    assert size(0, 32, 128, 8) == 0
+
+
+def test_merged_decode_argument_errors():
+    """The merged decode checks what the split decode checks, plus out and the
+    workspace size, before anything is enqueued (fake non-NULL pointers)."""
+    lib = pkv.load_library()
+    fake = ctypes.c_void_p(256)
+    dev = dict(q=fake, k=fake, v=fake, pt=fake, kv_lens=fake)
+    need = lib.paged_attn_decode_merged_workspace_size(2, 32, 128, 2)
+    assert _merged(lib, d=96, **dev) == EUNSUP
+    assert _merged(lib, hq=30, **dev) == EINVAL
+    assert _merged(lib, chunk=100, **dev) == EINVAL
+    assert _merged(lib, scale=-1.0, **dev) == EINVAL
+    assert _merged(lib, ws=fake, ws_bytes=need, **dev) == EINVAL        # out NULL
+    assert b"out" in lib.pkv_last_error()
+    assert _merged(lib, out=fake, ws=fake, ws_bytes=need - 1, **dev) == EINVAL
+    assert b"workspace" in lib.pkv_last_error()
+    assert _merged(lib, out=fake, ws=None, ws_bytes=need, **dev) == EINVAL
+    assert _merged(lib, batch=0) == 0                                   # empty batch
