@@ -249,23 +249,36 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
  * and its combine back to back; [DCA] _dual_chunk_flash_attn_decoding merges
  * the partial decodes it has just produced). Arguments as for
  * paged_attn_decode_splitkv, except:
+ * kv_chunk, num_splits: as for paged_attn_decode_splitkv, or both 0 for
+ *          balanced ranges: the visible keys of all requests, laid end to end
+ *          in 16-key tiles, are cut into equal ranges, one per workgroup of a
+ *          single round on a 256-CU device (512 workgroups in all), each of at
+ *          least 8 tiles; a range may end one request and start the next. A
+ *          request covered by one range is written directly; otherwise each
+ *          range's part is handed over and the last of them to finish merges
+ *          them in range order (so the result does not depend on timing).
+ *          Needs at most 2^24 keys per request (pt_stride * page_size); where
+ *          this or the group kernel (below) does not apply, the library picks
+ *          fixed splits of at most 8 per request instead.
  * workspace: device scratch of at least
  *          paged_attn_decode_merged_workspace_size(...) bytes (may be NULL when
  *          that size is 0, i.e. num_splits == 1): completion counters (one per
  *          request and group of 256 / head_dim kv heads, in the counter
- *          region), then the partials
- *          o [num_splits, batch, num_q_heads, head_dim] fp32 and lse
- *          [num_splits, batch, num_q_heads] fp32, each 256-byte aligned; layout
- *          and zeroing rule as stated at PKV_WORKSPACE_COUNTER_BYTES.
+ *          region), then the partials o [parts, num_q_heads, head_dim] fp32 and
+ *          lse [parts, num_q_heads] fp32, each 256-byte aligned, with parts =
+ *          num_splits * batch (fixed splits, split-major) or 512 + 8 * batch
+ *          (balanced ranges); layout and zeroing rule as stated at
+ *          PKV_WORKSPACE_COUNTER_BYTES.
  * out      [batch, num_q_heads, head_dim] dtype (out); lse [batch, num_q_heads]
  *          fp32 (out) or NULL.
- * The result is bit-identical to paged_attn_decode_splitkv followed by
- * merge_state on the same arguments. On the bf16 kv-head-group kernel (bf16,
- * 256 / head_dim kv heads whose query heads fit 16 columns) this is one launch:
- * the last of a request's non-empty splits to finish merges them. Otherwise
- * the two kernels run back to back. A request with no visible key gets
- * (0, -inf). Errors as for paged_attn_decode_splitkv, plus PKV_EINVAL for a
- * NULL out or a workspace smaller than the size function returns.
+ * With fixed splits the result is bit-identical to paged_attn_decode_splitkv
+ * followed by merge_state on the same arguments; with balanced ranges it is
+ * the same attention over other part boundaries (equal within rounding). On the
+ * bf16 kv-head-group kernel (bf16, 256 / head_dim kv heads whose query heads
+ * fit 16 columns) this is one launch; otherwise the decode and merge_state
+ * kernels run back to back. A request with no visible key gets (0, -inf).
+ * Errors as for paged_attn_decode_splitkv, plus PKV_EINVAL for a NULL out or a
+ * workspace smaller than the size function returns.
  */
 size_t paged_attn_decode_merged_workspace_size(int32_t batch, int32_t num_q_heads,
                                                int32_t head_dim, int32_t num_splits);

@@ -316,6 +316,11 @@ def test_merged_decode_workspace_size():
         assert size(B, hq, d, S) == COUNTER_BYTES + up(S * B * hq * d * 4) + up(S * B * hq * 4)
     assert size(64, 32, 128, 1) == 0
     assert size(0, 32, 128, 8) == 0
+    # balanced ranges (num_splits 0): 512 + 8 B partial rows
+    for B, hq, d in [(32, 64, 128), (1, 8, 64), (200, 16, 128)]:
+        parts = 512 + 8 * B
+        assert size(B, hq, d, 0) == COUNTER_BYTES + up(parts * hq * d * 4) + up(parts * hq * 4)
+    assert size(4, 8, 128, -1) == 0
 
 
 def test_merged_decode_argument_errors():
@@ -335,3 +340,10 @@ def test_merged_decode_argument_errors():
     assert b"workspace" in lib.pkv_last_error()
     assert _merged(lib, out=fake, ws=None, ws_bytes=need, **dev) == EINVAL
     assert _merged(lib, batch=0) == 0                                   # empty batch
+    # balanced ranges: kv_chunk 0 with num_splits 0, workspace sized for them
+    need0 = lib.paged_attn_decode_merged_workspace_size(2, 32, 128, 0)
+    assert _merged(lib, out=fake, ws=fake, ws_bytes=need0 - 1, chunk=0, S=0, **dev) == EINVAL
+    assert b"workspace" in lib.pkv_last_error()
+    assert _merged(lib, out=fake, ws=fake, ws_bytes=need0, chunk=4096, S=0, **dev) == EINVAL
+    # the split decode has no balanced mode
+    assert _decode(lib, chunk=0, S=0, **dev, op=fake, lp=fake) == EINVAL
