@@ -111,7 +111,7 @@ static PrefillPlan prefill_plan(int64_t batch, int64_t total_q, int64_t max_seql
   // one block of 32 rows per (split, q-tile slot, head)
   const size_t blocks = static_cast<size_t>(p.max_splits) * p.qtile_slots * hq;
   p.lse_bytes = round_up256(blocks * 32 * 4);
-  p.o_bytes = blocks * 32 * head_dim * 4;
+  p.o_bytes = blocks * 32 * head_dim * 2;   // bf16
   p.bytes = p.counter_bytes + p.lse_bytes + p.o_bytes;
   return p;
 }
@@ -512,7 +512,7 @@ static pkv_status_t prefill_prepare(const void* q, int32_t dtype, const void* k_
   char* ws = static_cast<char*>(workspace);
   a.counters = plan.bytes ? reinterpret_cast<int32_t*>(ws) : nullptr;
   a.ws_lse = plan.bytes ? reinterpret_cast<float*>(ws + plan.counter_bytes) : nullptr;
-  a.ws_o = plan.bytes ? reinterpret_cast<float*>(ws + plan.counter_bytes + plan.lse_bytes)
+  a.ws_o = plan.bytes ? static_cast<void*>(ws + plan.counter_bytes + plan.lse_bytes)
                       : nullptr;
   a.out = out;
   a.lse = lse;

@@ -88,7 +88,7 @@ struct PrefillArgs {
   int32_t max_splits;   // splits per q tile (grid extent)
   int32_t qtile_slots;  // >= the q tiles of all requests: ceil(total_q / 32) + batch, capped
   int32_t groups;       // groups of four waves per workgroup (1 or 2)
-  float* ws_o;          // [max_splits, qtile_slots, Hq] blocks of 32 rows x D partial outputs
+  void* ws_o;           // [max_splits, qtile_slots, Hq] blocks of 32 rows x D bf16 partial outputs
   float* ws_lse;        // [max_splits, qtile_slots, Hq, 32] partial LSEs (max_splits > 1)
   int32_t* counters;    // [qtile_slots, Hkv, ceil(G / 4)] in the workspace's counter region
   void* out;

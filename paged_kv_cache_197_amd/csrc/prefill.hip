@@ -80,6 +80,8 @@ struct PrefillKernel {
   static constexpr int MERGE_F4 = 4 * NB + 1;        // float4s of a lane in the merge: acc, (m, l)
   static constexpr int QPW = TILE / 2048;             // Q copies per wave (4 heads / 8 waves)
   static constexpr float kRescaleLog2 = 8.f;          // see softmax_pv
+  static constexpr int kMaxSplits = 16;               // key splits per q tile (planned by the host)
+  static constexpr int kMergeBatch = 2;               // splits whose partials a merge loads at once
   static_assert(KPW == 8, "a wave copies 8 keys of each tile");
   static_assert(GROUPS == 1 || 4 * MERGE_F4 * 64 * 16 <= 2 * GROUP_LDS, "merge buffer fits the rings");
   static_assert(4 * TILE / 1024 == 8 * QPW, "Q copies split evenly over the waves");
@@ -636,27 +638,34 @@ struct PrefillKernel {
       }
 
       // partial of this split, one block per (split, q-tile slot, head): the
-      // wave's 32 rows x D floats as 16-byte pieces p = 2 (4n + a4) + h, each
-      // piece's 32 rows consecutive, so every store (and the merge's loads)
-      // covers 1 KB of contiguous memory; the LSEs of the 32 rows follow
-      // each other. Stored at device scope (see coherent_rsrc).
-      const uint32_t o_bytes = static_cast<uint32_t>(QT * D * 4);
+      // wave's 32 rows x D as bf16 (the output precision), lane l's values
+      // acc[n][8k .. 8k + 8) at 16-byte piece (2n + k) * 64 + l, so that every
+      // store (and each of the merge's loads) covers 1 KB of contiguous
+      // memory; the LSEs of the 32 rows follow each other. Stored at device
+      // scope (see coherent_rsrc).
+      const uint32_t o_bytes = static_cast<uint32_t>(QT * D * 2);
       const uint32_t l_bytes = static_cast<uint32_t>(QT * 4);
-      const uint32_t o_lane = static_cast<uint32_t>((h * QT + q) * 16);
       const uint32_t l_lane = static_cast<uint32_t>(q * 4);
       auto block_of = [&](int sp) {
         return (static_cast<int64_t>(sp) * a.qtile_slots + slot) * a.hq + head;
       };
+      auto o_rsrc = [&](int sp) {
+        return coherent_rsrc(static_cast<char*>(a.ws_o) + block_of(sp) * o_bytes, o_bytes);
+      };
       if (grp == 0 && head_ok) {
         const int64_t blk = block_of(split);
-        const auto ro = coherent_rsrc(a.ws_o + blk * QT * D, o_bytes);
+        const auto ro = o_rsrc(split);
 #pragma unroll
         for (int n = 0; n < NB; ++n)
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4)
-            store_coherent(ro, o_lane + (8 * n + 2 * a4) * QT * 16,
-                           f32x4{acc[n][4 * a4] * inv, acc[n][4 * a4 + 1] * inv,
-                                 acc[n][4 * a4 + 2] * inv, acc[n][4 * a4 + 3] * inv});
+          for (int k = 0; k < 2; ++k) {
+            const u32x4 w = {pack_bf16x2(acc[n][8 * k] * inv, acc[n][8 * k + 1] * inv),
+                             pack_bf16x2(acc[n][8 * k + 2] * inv, acc[n][8 * k + 3] * inv),
+                             pack_bf16x2(acc[n][8 * k + 4] * inv, acc[n][8 * k + 5] * inv),
+                             pack_bf16x2(acc[n][8 * k + 6] * inv, acc[n][8 * k + 7] * inv)};
+            store_coherent(ro, static_cast<uint32_t>(((2 * n + k) * 64 + lane) * 16),
+                           __builtin_bit_cast(f32x4, w));
+          }
         if (h == 0) store_coherent(coherent_rsrc(a.ws_lse + blk * QT, l_bytes), l_lane, lse_val);
       }
       wait_all_vmem();
@@ -666,18 +675,23 @@ struct PrefillKernel {
       if (threadIdx.x == 0) sh_last = (counter_add(counter, 1) == n_split - 1);
       __syncthreads();
       if (!sh_last) continue;
-      // the last split of this (q tile, kv head, head block) merges all of them
+      // the last split of this (q tile, kv head, head block) merges all of
+      // them, in split order, kMergeBatch splits' pieces (and their LSEs) in
+      // flight together (n_split <= kMaxSplits)
       if (grp == 0 && head_ok && row_ok) {
-        float ls[16];
+        auto lse_of = [&](int s2) {
+          return s2 < n_split
+                     ? load_coherent1(coherent_rsrc(a.ws_lse + block_of(s2) * QT, l_bytes), l_lane)
+                     : neg_inf();
+        };
+        float mx = neg_inf();
+        {
+          float ls[kMaxSplits];
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2)
-          ls[s2] = s2 < n_split ? load_coherent1(
-                                      coherent_rsrc(a.ws_lse + block_of(s2) * QT, l_bytes),
-                                      l_lane)
-                                : neg_inf();
-        float mx = ls[0];
+          for (int s2 = 0; s2 < kMaxSplits; ++s2) ls[s2] = lse_of(s2);
 #pragma unroll
-        for (int s2 = 1; s2 < 16; ++s2) mx = fmaxf(mx, ls[s2]);
+          for (int s2 = 0; s2 < kMaxSplits; ++s2) mx = fmaxf(mx, ls[s2]);
+        }
         float o[16][NB];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -685,22 +699,36 @@ struct PrefillKernel {
           for (int n = 0; n < NB; ++n) o[r][n] = 0.f;
         float wsum = 0.f;
         if (mx != neg_inf()) {
-          for (int s2 = 0; s2 < n_split; ++s2) {
-            const float wgt = fast_exp2((ls[s2] - mx) * kLog2e);
-            wsum += wgt;
-            const auto ro = coherent_rsrc(a.ws_o + block_of(s2) * QT * D, o_bytes);
-            f32x4 v[NB][4];   // all loads in flight before the first use
+#pragma unroll 1
+          for (int s0 = 0; s0 < n_split; s0 += kMergeBatch) {
+            u32x4 v[kMergeBatch][2 * NB];
+            float l4[kMergeBatch];
 #pragma unroll
-            for (int n = 0; n < NB; ++n)
+            for (int k4 = 0; k4 < kMergeBatch; ++k4) {
+              const int s2 = min(s0 + k4, n_split - 1);   // (past the end: loaded, not used)
+              const auto ro = o_rsrc(s2);
 #pragma unroll
-              for (int a4 = 0; a4 < 4; ++a4)
-                v[n][a4] = load_coherent4(ro, o_lane + (8 * n + 2 * a4) * QT * 16);
+              for (int pi = 0; pi < 2 * NB; ++pi)
+                v[k4][pi] = __builtin_bit_cast(
+                    u32x4, load_coherent4(ro, static_cast<uint32_t>((pi * 64 + lane) * 16)));
+              l4[k4] = lse_of(s0 + k4);
+            }
 #pragma unroll
-            for (int n = 0; n < NB; ++n)
+            for (int k4 = 0; k4 < kMergeBatch; ++k4) {
+              const float wgt = l4[k4] == neg_inf() ? 0.f : fast_exp2((l4[k4] - mx) * kLog2e);
+              wsum += wgt;
 #pragma unroll
-              for (int a4 = 0; a4 < 4; ++a4)
+              for (int n = 0; n < NB; ++n)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) o[4 * a4 + c][n] += wgt * v[n][a4][c];
+                for (int k = 0; k < 2; ++k)
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = v[k4][2 * n + k][e];
+                    o[8 * k + 2 * e][n] = __builtin_fmaf(wgt, bf16lo(w), o[8 * k + 2 * e][n]);
+                    o[8 * k + 2 * e + 1][n] =
+                        __builtin_fmaf(wgt, bf16hi(w), o[8 * k + 2 * e + 1][n]);
+                  }
+            }
           }
         }
         store_out_row(static_cast<bf16_t*>(a.out) + (row * a.hq + head) * D, h, o,

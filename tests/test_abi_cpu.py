@@ -141,6 +141,10 @@ def test_prefill_workspace_plan():
     # two q tiles against 8192 cached keys: split, workspace scales with total_q
     small = size(1, 64, 64, 8192, 32, 8, 128)
     assert small > COUNTER_BYTES
+    # 256 key tiles over 2 q tiles x 8 kv heads: 16 splits of 16 tiles; blocks of
+    # 32 rows per (split, q-tile slot (3), head): fp32 LSEs, bf16 partial outputs
+    blocks = 16 * 3 * 32
+    assert small == COUNTER_BYTES + (blocks * 32 * 4 + 255) // 256 * 256 + blocks * 32 * 128 * 2
     assert size(1, 128, 64, 8192, 32, 8, 128) > small
     # a call that needs a workspace rejects a missing or short one before any
     # launch (fake non-NULL pointers: validation never touches them)
