@@ -24,7 +24,20 @@ import time
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dense bf16
 ROOT = os.path.dirname(os.path.abspath(__file__))
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_group_config3_counters.json")
+# HBM traffic per workload from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (written by
+# `bench.py --hbm-summary`), valid for the kernel sources whose hash it records
+HBM_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+# sources of each workload's kernels (their hash keys the stored traffic)
+WORKLOAD_SOURCES = {
+    "decode": ["decode.hip", "merge_state.hip", "page_table.hip", "common.hpp", "args.hpp"],
+    "decode_merged": ["decode.hip", "page_table.hip", "common.hpp", "args.hpp"],
+    "swa": ["decode.hip", "page_table.hip", "common.hpp", "args.hpp"],
+    "sparse": ["sparse_mla.hip", "common.hpp", "lanes.hpp", "lds_dma.hpp", "args.hpp"],
+    "cascade": ["cascade.hip", "prefill.hip", "common.hpp", "lanes.hpp", "lds_dma.hpp",
+                "args.hpp"],
+    "dca": ["dca.hip", "decode.hip", "merge_state.hip", "common.hpp", "args.hpp"],
+}
+COPY_BYTES = 1 << 30   # run_copy: bytes read and bytes written by the copy kernel
 
 
 def parse_args(argv=None):
@@ -37,6 +50,9 @@ def parse_args(argv=None):
                                       "sparse", "cascade", "dca", "copy"],
                    default="all", help="restrict to one workload (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--hbm-summary", metavar="DIR", default=None,
+                   help="reduce the rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR to the "
+                        "per-workload traffic summary (JSON on stdout); needs no GPU")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU work budget for the oracle sample")
     return p.parse_args(argv)
@@ -781,22 +797,81 @@ def cpu_oracle_sparse(torch, r, budget_s):
 
 # ---------------------------------------------------------------------------
 
-def stored_traffic(kernel_key, src_hash):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+def summarize_hbm_counters(out_dir):
+    """HBM bytes per dispatch of every library kernel from the counter runs
+    under out_dir (hbm_<workload>_<FETCH_SIZE|WRITE_SIZE>/*counter_collection.csv,
+    one rocprofv3 --pmc run per counter), each counter scaled by what it reads
+    for the 1 GiB copy kernel of `--only copy`. Returns the JSON-ready summary."""
+    import csv
+    import glob
+
+    def load(workload, counter):
+        files = glob.glob(os.path.join(out_dir, f"hbm_{workload}_{counter}", "*counter_collection.csv"))
+        if not files:
+            raise FileNotFoundError(f"no {counter} results for {workload} under {out_dir}")
+        per = {}
+        names = {}
+        for row in csv.DictReader(open(files[0])):
+            d = row["Dispatch_Id"]
+            per[d] = per.get(d, 0.0) + float(row["Counter_Value"])
+            names[d] = row["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+        out = {}
+        for d, v in per.items():
+            out.setdefault(names[d], []).append(v)
+        return out
+
+    cf, cw = load("copy", "FETCH_SIZE"), load("copy", "WRITE_SIZE")
+    copy_fetch = max(max(v) for v in cf.values())
+    copy_write = max(max(v) for v in cw.values())
+    ff = COPY_BYTES / 1024 / copy_fetch
+    wf = COPY_BYTES / 1024 / copy_write
+    summary = {"calibration": {"copy_bytes": COPY_BYTES, "copy_fetch_kib": round(copy_fetch, 1),
+                               "copy_write_kib": round(copy_write, 1),
+                               "fetch_factor": round(ff, 5), "write_factor": round(wf, 5)},
+               "workloads": {}}
+    for w, srcs in WORKLOAD_SOURCES.items():
+        fetch, write = load(w, "FETCH_SIZE"), load(w, "WRITE_SIZE")
+        kernels = {}
+        for name in sorted(set(fetch) | set(write)):
+            if not name.startswith("pkv::"):
+                continue
+            fk = sum(fetch.get(name, [0.0])) / max(len(fetch.get(name, [])), 1)
+            wk = sum(write.get(name, [0.0])) / max(len(write.get(name, [])), 1)
+            kernels[name] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                             "dispatches": len(fetch.get(name, [])),
+                             "bytes": int(round(fk * 1024 * ff + wk * 1024 * wf))}
+        summary["workloads"][w] = {"source_hash": source_hash(*srcs), "kernels": kernels,
+                                   "step_bytes": sum(k["bytes"] for k in kernels.values())}
+    return summary
+
+
+def stored_traffic(workload, algorithmic_bytes, kernel_prefix=None):
+    """HBM traffic of one step of `workload` (or of its kernel named by
+    `kernel_prefix`) from the committed counter summary, with its ratio to the
+    algorithmic bytes; None when the summary was taken on other kernel sources."""
     try:
-        with open(PROFILE_COUNTERS) as f:
-            data = json.load(f)
-    except (OSError, ValueError):
+        with open(HBM_TRAFFIC) as f:
+            ent = json.load(f)["workloads"][workload]
+    except (OSError, ValueError, KeyError):
         return None
-    ent = data.get(kernel_key)
-    if not ent or ent.get("source_hash") != src_hash:
+    if ent.get("source_hash") != source_hash(*WORKLOAD_SOURCES[workload]):
         return None
-    return ent.get("traffic_bytes")
+    if kernel_prefix is None:
+        b = ent["step_bytes"]
+    else:
+        hits = [k["bytes"] for n, k in ent["kernels"].items() if n.startswith(kernel_prefix)]
+        if not hits:
+            return None
+        b = hits[0]
+    return {"bytes": b, "per_algorithmic": round(b / algorithmic_bytes, 4) if algorithmic_bytes
+            else None, "source_hash": ent["source_hash"]}
 
 
 def main(argv=None):
     args = parse_args(argv)
+    if args.hbm_summary:
+        print(json.dumps(summarize_hbm_counters(args.hbm_summary), indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the hot path runs on a single MI355X here)", file=sys.stderr)
@@ -820,7 +895,6 @@ def main(argv=None):
         r = run_decode(torch, pkv, workloads, args)
         gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
         achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
-        src = source_hash("decode.hip", "common.hpp")
         line = {
             "metric": "decode KV GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)",
             "value": round(gbs, 2),
@@ -851,8 +925,7 @@ def main(argv=None):
                 "kernel_ms": round(r["kernel_ms"], 4),
                 "kernel_ms_median": round(r["kernel_ms_median"], 4),
                 "median_launches": r["median_launches"],
-                "traffic": stored_traffic("decode_config3", src),
-                "source_hash": src,
+                "traffic": stored_traffic("decode", r["bytes"], "pkv::decode_group_kernel"),
             },
         }
         if not args.no_cpu_baseline:
@@ -874,7 +947,8 @@ def main(argv=None):
                 "kernel_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
                 "kernel_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
                                          / HBM_PEAK_GBS, 4),
-                "algorithmic_bytes": r["bytes"], "split_mode": "balanced ranges"}
+                "algorithmic_bytes": r["bytes"], "split_mode": "balanced ranges",
+                "traffic": stored_traffic("decode_merged", r["bytes"])}
         except Exception as e:
             extra["decode_merged"] = {"error": repr(e)}
         torch.cuda.empty_cache()
@@ -914,7 +988,8 @@ def main(argv=None):
                 "kernel_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
                 "kernel_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
                                          / HBM_PEAK_GBS, 4),
-                "sum_kv_len": r["sum_kv_len"], "split_mode": "balanced ranges"}
+                "sum_kv_len": r["sum_kv_len"], "split_mode": "balanced ranges",
+                "traffic": stored_traffic("swa", r["bytes"])}
             if not args.no_cpu_baseline:
                 extra["swa_decode"]["cpu_oracle"] = cpu_oracle_swa(torch, r, 4.0)
         except Exception as e:  # report, do not hide
@@ -1004,7 +1079,8 @@ def main(argv=None):
                                           / HBM_PEAK_GBS, 4),
                 "TFLOP/s": round(r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12, 2),
                 "algorithmic_bytes": r["bytes"], "flops": r["flops"],
-                "sum_committed_len": r["sum_l"], "prefill_workspace_bytes": r["ws"]}
+                "sum_committed_len": r["sum_l"], "prefill_workspace_bytes": r["ws"],
+                "traffic": stored_traffic("cascade", r["bytes"])}
             if not args.no_cpu_baseline:
                 extra["cascade_verify"]["cpu_oracle"] = cpu_oracle_cascade(torch, r, 4.0)
         except Exception as e:
@@ -1024,7 +1100,7 @@ def main(argv=None):
                                          / HBM_PEAK_GBS, 4),
                 "step_GB/s": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 2),
                 "sum_kv_len": r["sum_l"], "num_splits": r["splits"],
-                "algorithmic_bytes": r["bytes"]}
+                "algorithmic_bytes": r["bytes"], "traffic": stored_traffic("dca", r["bytes"])}
             if not args.no_cpu_baseline:
                 extra["dca_decode"]["cpu_oracle"] = cpu_oracle_dca(torch, r, 4.0)
         except Exception as e:
@@ -1043,7 +1119,8 @@ def main(argv=None):
                                        4),
                 "warm_GB/s": round(r["bytes"] / (r["warm_ms"] * 1e-3) / 1e9, 2),
                 "cold_TFLOP/s": round(r["flops"] / (r["cold_ms"] * 1e-3) / 1e12, 2),
-                "bytes": r["bytes"], "flops": r["flops"]}
+                "bytes": r["bytes"], "flops": r["flops"],
+                "traffic": stored_traffic("sparse", r["bytes"])}
             if not args.no_cpu_baseline:
                 extra["sparse_mla"]["cpu_oracle"] = cpu_oracle_sparse(torch, r, 4.0)
         except Exception as e:

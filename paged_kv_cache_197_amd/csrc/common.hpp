@@ -94,10 +94,17 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ void retire(uint32_t v) { asm volatile("" ::"v"(v)); }
 
 // Data handed from one workgroup to another within a launch (split partials,
-// then a counter): stores and loads at device scope (cache-policy bit sc1), so
-// they are written through, and read past, the per-XCD L2 caches and need no
-// cache writeback or invalidate around the hand-off. The producer waits for
-// its stores (vmcnt(0)) before bumping the counter; the consumer reads after.
+// then a counter). Every handed-over word is stored and loaded at device scope
+// (cache-policy bit sc1): the AMDGPU memory model of the gfx942 generation,
+// which gfx950 follows, encodes relaxed agent-scope atomic stores and loads
+// this way, i.e. they are coherent across the per-XCD L2 caches. Ordering: each
+// producer wave waits until its stores have completed (vmcnt(0)), the
+// workgroup barrier follows, then one lane adds to the agent-scope counter;
+// the workgroup that sees the final count loads only after that add has
+// returned. This is a release / acquire pair without their cache maintenance
+// (write-back and invalidate of the whole XCD L2), which is not needed because
+// no handed-over word goes through an ordinary access; that maintenance would
+// also drop data other workgroups reuse from the L2.
 // Buffer resources need a wave-uniform base; the byte offsets are per lane.
 constexpr int kScopeDevice = 16;   // sc1
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
@@ -123,7 +130,8 @@ __device__ __forceinline__ f32x4 load_coherent4(__amdgpu_buffer_rsrc_t r, uint32
 }
 // all of this wave's memory operations have completed
 __device__ __forceinline__ void wait_all_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// device-scope counter, relaxed: ordering comes from wait_all_vmem and barriers
+// agent-scope counter, relaxed: the ordering comes from wait_all_vmem, the
+// barrier around the add, and the device-scope accesses of the data
 __device__ __forceinline__ int counter_add(int* c, int v) {
   return __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
