@@ -29,7 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # sources of each workload's kernels (their hash keys the stored traffic)
 WORKLOAD_SOURCES = {
-    "decode": ["decode.hip", "merge_state.hip", "page_table.hip", "common.hpp", "args.hpp"],
+    "decode": ["decode.hip", "page_table.hip", "common.hpp", "args.hpp"],
+    "decode_split": ["decode.hip", "merge_state.hip", "page_table.hip", "common.hpp", "args.hpp"],
     "decode_merged": ["decode.hip", "page_table.hip", "common.hpp", "args.hpp"],
     "swa": ["decode.hip", "page_table.hip", "common.hpp", "args.hpp"],
     "sparse": ["sparse_mla.hip", "common.hpp", "lanes.hpp", "lds_dma.hpp", "args.hpp"],
@@ -45,7 +46,8 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--only", choices=["all", "decode", "decode_merged", "decode_window", "prefill",
+    p.add_argument("--only", choices=["all", "decode", "decode_split", "decode_merged", "decode_window",
+                                      "prefill",
                                       "prefill_long", "prefill_window", "prefill_append", "swa",
                                       "sparse", "cascade", "dca", "copy"],
                    default="all", help="restrict to one workload (for profiler runs)")
@@ -194,7 +196,10 @@ def window_decode_bytes(seq_lens, window_left, batch, hq, hkv, d, page_size, ele
 # Workloads
 # ---------------------------------------------------------------------------
 
-def run_decode(torch, pkv, workloads, args, window_left=-1, kv_chunk=None, merged=False):
+def run_decode(torch, pkv, workloads, args, window_left=-1, kv_chunk=None, mode="split"):
+    """config3's step. mode "merged": the split-KV decode with the merge of its
+    splits in the same launch (bit-identical to "split"); "split": the decode,
+    then merge_state (two launches); "balanced": merged over balanced ranges."""
     dev = torch.device("cuda:0")
     c = workloads.config3(value_device=dev)
     r2t, rpi, sl = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev))
@@ -208,17 +213,19 @@ def run_decode(torch, pkv, workloads, args, window_left=-1, kv_chunk=None, merge
     lp = torch.empty((S, B, hq), dtype=torch.float32, device=dev)
     out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
-    ws = (torch.zeros(pkv.paged_attn_decode_merged_workspace_size(B, hq, d, 0), dtype=torch.uint8,
-                      device=dev) if merged else None)
+    merged = mode in ("merged", "balanced")
+    ws = (torch.zeros(pkv.paged_attn_decode_merged_workspace_size(
+        B, hq, d, S if mode == "merged" else 0), dtype=torch.uint8, device=dev) if merged else None)
 
     def step(timer):
         pkv.build_page_table(r2t, rpi, sl, P, c.table_width, page_table=pt, kv_lens=kl,
                              with_cu_seqlens=False)
         e0 = timer.mark() if timer else None
-        if merged:   # balanced ranges, decode and merge in one launch
-            pkv.paged_attn_decode_merged(c.q, c.k_cache, c.v_cache, pt, kl, c.scale, kv_chunk=0,
-                                         num_splits=0, window_left=window_left, workspace=ws,
-                                         out=out, lse=lse)
+        if merged:   # decode and merge in one launch
+            pkv.paged_attn_decode_merged(c.q, c.k_cache, c.v_cache, pt, kl, c.scale,
+                                         kv_chunk=chunk if mode == "merged" else 0,
+                                         num_splits=S if mode == "merged" else 0,
+                                         window_left=window_left, workspace=ws, out=out, lse=lse)
             if timer:
                 timer.pairs.append((e0, timer.mark()))
             return
@@ -892,7 +899,7 @@ def main(argv=None):
     line = {}
     extra = {}
     if args.only in ("all", "decode"):
-        r = run_decode(torch, pkv, workloads, args)
+        r = run_decode(torch, pkv, workloads, args, mode="merged")
         gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
         achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
         line = {
@@ -909,14 +916,15 @@ def main(argv=None):
             "dtype": "bf16",
             "data": "synthetic",
             "config": {
-                "workload": "config3: batched split-KV GQA decode (page-table build + decode + "
-                            "merge_state), B=64, L~U[1024,32768], 32 q / 8 kv heads, D=128, "
+                "workload": "config3: batched split-KV GQA decode (page-table build, then the "
+                            "split-KV decode with the merge_state combine of its splits in the "
+                            "same launch), B=64, L~U[1024,32768], 32 q / 8 kv heads, D=128, "
                             "page 64, 40000-page pool, 4096-token chunks",
                 "batch": r["batch"], "sum_kv_len": r["sum_l"], "num_splits": r["splits"],
                 "algorithmic_bytes_per_step": r["bytes"],
             },
             "roofline": {
-                "kernel": "decode_group_kernel<128, uniform page> (bf16)",
+                "kernel": "decode_group_kernel<128, uniform page> (bf16), merging its splits",
                 "bound": "hbm",
                 "achieved": round(achieved, 2),
                 "peak": HBM_PEAK_GBS,
@@ -933,9 +941,28 @@ def main(argv=None):
         del r
         torch.cuda.empty_cache()
 
+    if args.only in ("all", "decode_split"):
+        try:
+            r = run_decode(torch, pkv, workloads, args, mode="split")
+            extra["decode_split_merge"] = {
+                "workload": "config3 as two launches: page-table build, split-KV decode into "
+                            "fp32 partials, then merge_state (the same result bit for bit)",
+                "device_ms_per_step": round(r["ms"], 4),
+                "decode_kernel_ms": round(r["kernel_ms"], 4),
+                "decode_kernel_ms_median": round(r["kernel_ms_median"], 4),
+                "step_GB/s": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 2),
+                "kernel_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
+                "kernel_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": r["bytes"], "num_splits": r["splits"],
+                "traffic": stored_traffic("decode_split", r["bytes"])}
+        except Exception as e:
+            extra["decode_split_merge"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
     if args.only in ("all", "decode_merged"):
         try:
-            r = run_decode(torch, pkv, workloads, args, merged=True)
+            r = run_decode(torch, pkv, workloads, args, mode="balanced")
             extra["decode_merged"] = {
                 "workload": "config3's batch through the merged entry point with balanced "
                             "ranges (instead of 4096-token chunks): page-table build, then the "
