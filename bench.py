@@ -1006,8 +1006,9 @@ def main(argv=None):
             extra["swa_decode"] = {
                 "workload": "config4: prefill-aware sliding-window decode, B=32, window 4096, "
                             "64 q / 8 kv heads, D=128, page 1 (table built on GPU); merged "
-                            "decode over balanced ranges (the batch's visible keys cut into 512 "
-                            "equal workgroup shares, parts merged in the same launch)",
+                            "decode over balanced ranges (the batch's visible keys cut into 256 "
+                            "equal workgroup shares, one per CU, parts merged in the same "
+                            "launch)",
                 "device_ms_per_step": round(r["ms"], 4),
                 "decode_merge_kernel_ms": round(r["kernel_ms"], 4),
                 "table_build_ms": round(r["build_ms"], 4),

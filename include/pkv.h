@@ -252,8 +252,8 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
  * kv_chunk, num_splits: as for paged_attn_decode_splitkv, or both 0 for
  *          balanced ranges: the visible keys of all requests, laid end to end
  *          in 16-key tiles, are cut into equal ranges, one per workgroup of a
- *          single round on a 256-CU device (512 workgroups in all), each of at
- *          least 8 tiles; a range may end one request and start the next. A
+ *          single round on a 256-CU device (256 workgroups in all, one per
+ *          CU), each of at least 8 tiles; a range may end one request and start the next. A
  *          request covered by one range is written directly; otherwise each
  *          range's part is handed over and the last of them to finish merges
  *          them in range order (so the result does not depend on timing).
@@ -266,7 +266,7 @@ pkv_status_t paged_attn_decode_splitkv(const void* q, int32_t dtype, const void*
  *          request and group of 256 / head_dim kv heads, in the counter
  *          region), then the partials o [parts, num_q_heads, head_dim] fp32 and
  *          lse [parts, num_q_heads] fp32, each 256-byte aligned, with parts =
- *          num_splits * batch (fixed splits, split-major) or 512 + 8 * batch
+ *          num_splits * batch (fixed splits, split-major) or 256 + 8 * batch
  *          (balanced ranges); layout and zeroing rule as stated at
  *          PKV_WORKSPACE_COUNTER_BYTES.
  * out      [batch, num_q_heads, head_dim] dtype (out); lse [batch, num_q_heads]

@@ -126,15 +126,17 @@ using pkv_host::fail;
   } while (0)
 
 // Balanced merged decode: ranges per kv-head group so that groups x ranges
-// is one round of workgroups on a 256-CU device (two per CU), and the most
-// partial rows (ranges + batch, or 8 fixed splits x batch where the group
-// kernel does not run) its workspace must hold.
-constexpr int kBalancedSlots = 512;
+// is one workgroup per CU of a 256-CU device (measured faster than two per CU
+// on both the long-context and the windowed batch: fewer partial rows to
+// merge, and one workgroup's four-tile loads already cover its CU's share of
+// HBM bandwidth), and the most partial rows (ranges + batch, or 8 fixed splits
+// x batch where the group kernel does not run) its workspace must hold.
+constexpr int kBalancedSlots = 256;
 constexpr int kBalancedMaxSplits = 8;
 constexpr int64_t kBalancedMaxKeys = int64_t{1} << 24;
 
 // merged decode workspace: counters, then o [parts, Hq, D] fp32, then lse
-// [parts, Hq] fp32 with parts = S x B (fixed splits) or 512 + 8 B (balanced,
+// [parts, Hq] fp32 with parts = S x B (fixed splits) or 256 + 8 B (balanced,
 // num_splits == 0)
 static size_t decode_merged_ws_bytes(int64_t batch, int64_t num_q_heads, int64_t head_dim,
                                      int64_t num_splits) {

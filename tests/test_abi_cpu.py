@@ -320,9 +320,9 @@ def test_merged_decode_workspace_size():
         assert size(B, hq, d, S) == COUNTER_BYTES + up(S * B * hq * d * 4) + up(S * B * hq * 4)
     assert size(64, 32, 128, 1) == 0
     assert size(0, 32, 128, 8) == 0
-    # balanced ranges (num_splits 0): 512 + 8 B partial rows
+    # balanced ranges (num_splits 0): 256 + 8 B partial rows
     for B, hq, d in [(32, 64, 128), (1, 8, 64), (200, 16, 128)]:
-        parts = 512 + 8 * B
+        parts = 256 + 8 * B
         assert size(B, hq, d, 0) == COUNTER_BYTES + up(parts * hq * d * 4) + up(parts * hq * 4)
     assert size(4, 8, 128, -1) == 0
 
