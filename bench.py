@@ -29,14 +29,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # sources of each workload's kernels (their hash keys the stored traffic)
 WORKLOAD_SOURCES = {
-    "decode": ["decode.hip", "page_table.hip", "common.hpp", "args.hpp"],
-    "decode_split": ["decode.hip", "merge_state.hip", "page_table.hip", "common.hpp", "args.hpp"],
-    "decode_merged": ["decode.hip", "page_table.hip", "common.hpp", "args.hpp"],
-    "swa": ["decode.hip", "page_table.hip", "common.hpp", "args.hpp"],
+    "decode": ["decode.hip", "splits.hpp", "page_table.hip", "common.hpp", "args.hpp"],
+    "decode_split": ["decode.hip", "splits.hpp", "merge_state.hip", "page_table.hip",
+                     "common.hpp", "args.hpp"],
+    "decode_merged": ["decode.hip", "splits.hpp", "page_table.hip", "common.hpp", "args.hpp"],
+    "swa": ["decode.hip", "splits.hpp", "page_table.hip", "common.hpp", "args.hpp"],
     "sparse": ["sparse_mla.hip", "common.hpp", "lanes.hpp", "lds_dma.hpp", "args.hpp"],
-    "cascade": ["cascade.hip", "prefill.hip", "common.hpp", "lanes.hpp", "lds_dma.hpp",
+    "cascade": ["cascade.hip", "draft_prefix.hip", "splits.hpp", "common.hpp", "lanes.hpp",
                 "args.hpp"],
-    "dca": ["dca.hip", "decode.hip", "merge_state.hip", "common.hpp", "args.hpp"],
+    "dca": ["dca.hip", "decode.hip", "splits.hpp", "merge_state.hip", "common.hpp", "args.hpp"],
 }
 COPY_BYTES = 1 << 30   # run_copy: bytes read and bytes written by the copy kernel
 
@@ -375,7 +376,9 @@ def run_prefill_append(torch, pkv, workloads, args):
 
 def run_cascade(torch, pkv, workloads, args):
     """Draft-tree verification by cascade attention: expand-table build, then
-    the prefix pass (prefill kernel, non-causal) and the expand pass + merge."""
+    the prefix pass (each kv head's 4 heads x 8 drafts packed into one 32-row
+    MFMA tile, key splits merged by a short second launch) and the expand
+    pass + merge."""
     dev = torch.device("cuda:0")
     c = workloads.cascade_verify(value_device=dev)
     r2t, rpi, sl = (c.req_to_token.to(dev), c.req_pool_indices.to(dev), c.seq_lens.to(dev))
@@ -391,7 +394,7 @@ def run_cascade(torch, pkv, workloads, args):
     out = torch.empty_like(c.q)
     lse = torch.empty((B * n, hq), dtype=torch.float32, device=dev)
     max_k = int(c.seq_lens.max())
-    ws_bytes = pkv.paged_attn_varlen_prefill_workspace_size(B, B * n, n, max_k, hq, hkv, d)
+    ws_bytes = pkv.paged_attn_cascade_workspace_size(B, B * n, n, max_k, hq, hkv, d)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     build_t = Timer(torch)
 
@@ -1098,8 +1101,9 @@ def main(argv=None):
             extra["cascade_verify"] = {
                 "workload": "draft-tree verification by cascade attention: B=64, committed "
                             "L~U[1024,16384], 8 drafts per request (random tree), 32 q / 8 kv "
-                            "heads, D=128, page 64; expand-table build + prefix pass (prefill "
-                            "kernel, non-causal) + expand pass and merge",
+                            "heads, D=128, page 64; expand-table build + prefix pass (packed "
+                            "(head, draft) rows, key splits + their merge) + expand pass and "
+                            "merge",
                 "device_ms_per_step": round(r["ms"], 4),
                 "cascade_ms": round(r["kernel_ms"], 4), "table_build_ms": round(r["build_ms"], 4),
                 "cascade_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
@@ -1107,7 +1111,7 @@ def main(argv=None):
                                           / HBM_PEAK_GBS, 4),
                 "TFLOP/s": round(r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12, 2),
                 "algorithmic_bytes": r["bytes"], "flops": r["flops"],
-                "sum_committed_len": r["sum_l"], "prefill_workspace_bytes": r["ws"],
+                "sum_committed_len": r["sum_l"], "workspace_bytes": r["ws"],
                 "traffic": stored_traffic("cascade", r["bytes"])}
             if not args.no_cpu_baseline:
                 extra["cascade_verify"]["cpu_oracle"] = cpu_oracle_cascade(torch, r, 4.0)

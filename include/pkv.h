@@ -482,16 +482,28 @@ pkv_status_t paged_attn_expand_merge(const void* q, int32_t dtype, const void* k
 /*
  * paged_attn_cascade -- cascade attention in one call: the prefix pass, then
  * the expand pass with its merge ([FA] forward_extend / forward_decode with
- * use_cascade_attn). The prefix pass is paged_attn_varlen_prefill with
- * causal = 0: the rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of request b see
- * all kv_lens[b] committed keys through page_table (for draft-tree
- * verification, cu_seqlens_q steps by n and kv_lens are the committed
- * lengths); its O and LSE go to out / lse, then paged_attn_expand_merge over
- * the total_q rows merges each row's expand keys (slots in expand_table, the
- * cache viewed with page size 1) into them. Arguments as for those two
- * calls; lse is required. Every argument is checked before anything is
- * enqueued; then two kernels run on the stream.
+ * use_cascade_attn). The prefix pass computes what paged_attn_varlen_prefill
+ * with causal = 0 does: the rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of
+ * request b see all kv_lens[b] committed keys through page_table (for
+ * draft-tree verification, cu_seqlens_q steps by n and kv_lens are the
+ * committed lengths); then the expand pass over the total_q rows merges each
+ * row's expand keys (slots in expand_table, the cache viewed with page size
+ * 1) into its result, as paged_attn_expand_merge does. When
+ * (num_q_heads / num_kv_heads) * max_seqlen_q <= 32 (bf16, head_dim 64 or
+ * 128) the prefix pass packs each kv head's (head, draft) rows into one
+ * 32-row tile and splits the keys itself, its splits' partials going through
+ * the workspace and a short merge launch (split order) into out / lse;
+ * otherwise it is the prefill kernel. Arguments as for those two calls,
+ * except: workspace of at least paged_attn_cascade_workspace_size(...) bytes
+ * (0: NULL allowed; layout and zeroing rule as stated at
+ * PKV_WORKSPACE_COUNTER_BYTES); max_seqlen_k sizes the key splits (a smaller
+ * one than some kv_lens[b] is still correct, only slower); lse is required.
+ * Every argument is checked before anything is enqueued; then two kernels (three
+ * with a split packed prefix pass) run on the stream.
  */
+size_t paged_attn_cascade_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                         int32_t max_seqlen_k, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim);
 pkv_status_t paged_attn_cascade(const void* q, int32_t dtype, const void* k_cache,
                                 const void* v_cache, int64_t num_pages, const int32_t* page_table,
                                 int32_t pt_stride, const int32_t* cu_seqlens_q,

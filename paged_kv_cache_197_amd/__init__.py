@@ -19,6 +19,7 @@ import torch
 __all__ = [
     "PkvError", "PkvLibraryMissing", "load_library", "library_path", "declared_symbols",
     "build_page_table", "paged_attn_varlen_prefill", "paged_attn_varlen_prefill_workspace_size",
+    "paged_attn_cascade_workspace_size",
     "paged_kv_append",
     "paged_attn_decode_splitkv", "paged_attn_decode_merged",
     "paged_attn_decode_merged_workspace_size",
@@ -68,6 +69,7 @@ _SIGNATURES = {
                                         _P, _P, _P, _P]),
     "paged_attn_varlen_prefill_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32,
                                                         _I32]),
+    "paged_attn_cascade_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_attn_varlen_prefill": (ctypes.c_int, [_P, _I32, _P, _P, _I64, _P, _I32, _P, _P,
                                                  _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                  _F, _I32, _I32, _I32, _P, _SZ, _P, _P, _P]),
@@ -308,6 +310,12 @@ def paged_attn_varlen_prefill_workspace_size(batch, total_q, max_seqlen_q, max_s
         batch, total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim))
 
 
+def paged_attn_cascade_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k, num_q_heads,
+                                      num_kv_heads, head_dim):
+    return int(load_library().paged_attn_cascade_workspace_size(
+        batch, total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim))
+
+
 def paged_kv_append(k_new, v_new, out_cache_loc, k_cache, v_cache):
     """Write new tokens' K/V [n, Hkv, D] into the cache ([pages, P, Hkv, D],
     modified in place) at token slots out_cache_loc [n]."""
@@ -530,8 +538,8 @@ def paged_attn_cascade(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, m
     batch = kl.numel()
     if max_seqlen_k is None:
         max_seqlen_k = pt.shape[1] * page_size
-    need = paged_attn_varlen_prefill_workspace_size(batch, total_q, int(max_seqlen_q),
-                                                    int(max_seqlen_k), hq, hkv, d)
+    need = paged_attn_cascade_workspace_size(batch, total_q, int(max_seqlen_q), int(max_seqlen_k),
+                                             hq, hkv, d)
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -116,6 +116,43 @@ static PrefillPlan prefill_plan(int64_t batch, int64_t total_q, int64_t max_seql
   return p;
 }
 
+// Packed draft prefix pass (cascade): key splits of `chunk` keys (a multiple
+// of 32, at least kDraftMinChunk) so that the (kv-head group, request, split)
+// workgroups number about kDraftWorkgroups (two per CU) when every request
+// is max_seqlen_k long; the last split also takes any keys past
+// splits * chunk. On the tree-verification batch (64 requests, two kv-head
+// groups, lengths up to 16384) a sweep of 256..2048 put 512 first (4 splits:
+// 0.70 of HBM for the whole cascade step, 0.66 at 384 and 768, 0.65 at
+// 2048): more splits add partials and workgroup start-up, fewer leave CUs
+// idle. With more than one split the workspace holds the splits' partials
+// after its counter region: o [splits, total_q, Hq, D] bf16, then lse
+// [splits, total_q, Hq] fp32, each 256-byte aligned.
+constexpr int64_t kDraftWorkgroups = 512;
+constexpr int64_t kDraftMinChunk = 256;
+
+struct DraftPlan {
+  int32_t chunk, splits;
+  size_t o_bytes, bytes;
+};
+
+static DraftPlan draft_plan(int64_t batch, int64_t total_q, int64_t max_seqlen_k, int64_t hq,
+                            int64_t hkv, int64_t head_dim, int64_t heads_per_wg) {
+  DraftPlan p{};
+  const int64_t lmax = std::max<int64_t>(max_seqlen_k, 1);
+  const int64_t per_split = std::max<int64_t>(1, batch * (hkv / heads_per_wg));
+  const int64_t want = std::max<int64_t>(1, (kDraftWorkgroups + per_split - 1) / per_split);
+  int64_t chunk = (lmax + want - 1) / want;
+  chunk = std::max<int64_t>(kDraftMinChunk, (chunk + 31) / 32 * 32);
+  p.chunk = static_cast<int32_t>(std::min<int64_t>(chunk, int64_t{1} << 30));
+  p.splits = static_cast<int32_t>((lmax + p.chunk - 1) / p.chunk);
+  if (p.splits > 1) {
+    const size_t rows = static_cast<size_t>(p.splits) * total_q * hq;
+    p.o_bytes = round_up256(rows * head_dim * 2);
+    p.bytes = PKV_WORKSPACE_COUNTER_BYTES + p.o_bytes + round_up256(rows * 4);
+  }
+  return p;
+}
+
 }  // namespace pkv_host
 
 using pkv_host::fail;
@@ -446,7 +483,8 @@ static pkv_status_t prefill_prepare(const void* q, int32_t dtype, const void* k_
                                     float softmax_scale, int32_t causal, int32_t window_left,
                                     int32_t attn_chunk, void* workspace,
                                     size_t workspace_bytes, void* out, float* lse,
-                                    pkv::PrefillArgs& a, bool* nothing) {
+                                    pkv::PrefillArgs& a, bool* nothing,
+                                    bool plan_workspace = true) {
   *nothing = false;
   PKV_REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "prefill: dtype %d not supported (bf16)",
               dtype);
@@ -482,8 +520,10 @@ static pkv_status_t prefill_prepare(const void* q, int32_t dtype, const void* k_
   }
   PKV_REQUIRE(q && k_cache && v_cache && page_table && cu_seqlens_q && kv_lens && out,
               PKV_EINVAL, "prefill: NULL required pointer");
-  const pkv_host::PrefillPlan plan = pkv_host::prefill_plan(
-      batch, total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim);
+  const pkv_host::PrefillPlan plan =
+      plan_workspace ? pkv_host::prefill_plan(batch, total_q, max_seqlen_q, max_seqlen_k,
+                                              num_q_heads, num_kv_heads, head_dim)
+                     : pkv_host::PrefillPlan{};
   PKV_REQUIRE(plan.counters * 4 <= PKV_WORKSPACE_COUNTER_BYTES, PKV_EUNSUPPORTED,
               "prefill: %lld split counters exceed the workspace's counter region",
               (long long)plan.counters);
@@ -854,6 +894,23 @@ pkv_status_t paged_attn_expand_merge(const void* q, int32_t dtype, const void* k
                             "paged_attn_expand_merge launch");
 }
 
+size_t paged_attn_cascade_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                         int32_t max_seqlen_k, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim) {
+  if (batch <= 0 || total_q <= 0 || max_seqlen_q <= 0 || max_seqlen_k < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0)
+    return 0;
+  const int w = pkv_launch::draft_prefix_heads(PKV_BF16, head_dim, num_q_heads, num_kv_heads,
+                                               max_seqlen_q);
+  if (w > 0)
+    return pkv_host::draft_plan(batch, total_q, max_seqlen_k, num_q_heads, num_kv_heads,
+                                head_dim, w)
+        .bytes;
+  return pkv_host::prefill_plan(batch, total_q, max_seqlen_q, max_seqlen_k, num_q_heads,
+                                num_kv_heads, head_dim)
+      .bytes;
+}
+
 pkv_status_t paged_attn_cascade(const void* q, int32_t dtype, const void* k_cache,
                                 const void* v_cache, int64_t num_pages, const int32_t* page_table,
                                 int32_t pt_stride, const int32_t* cu_seqlens_q,
@@ -864,13 +921,17 @@ pkv_status_t paged_attn_cascade(const void* q, int32_t dtype, const void* k_cach
                                 int32_t expand_stride, const int32_t* expand_lens,
                                 void* workspace, size_t workspace_bytes, void* out, float* lse,
                                 void* stream) {
-  // every check before anything is enqueued
+  // every check before anything is enqueued; the prefix pass packs each kv
+  // head's (head, draft) rows into one MFMA tile when they fit (w > 0), else
+  // it is the prefill kernel with causal = 0
+  const int w = pkv_launch::draft_prefix_heads(dtype, head_dim, num_q_heads, num_kv_heads,
+                                               max_seqlen_q);
   pkv::PrefillArgs pa;
   bool nothing = false;
   pkv_status_t st = prefill_prepare(
       q, dtype, k_cache, v_cache, num_pages, page_table, pt_stride, cu_seqlens_q, kv_lens, batch,
       total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, page_size,
-      softmax_scale, 0, -1, 0, workspace, workspace_bytes, out, lse, pa, &nothing);
+      softmax_scale, 0, -1, 0, workspace, workspace_bytes, out, lse, pa, &nothing, w == 0);
   if (st != PKV_OK) return st;
   pkv::ExpandMergeArgs ea;
   st = expand_merge_prepare("paged_attn_cascade", q, dtype, k_cache, v_cache,
@@ -879,8 +940,45 @@ pkv_status_t paged_attn_cascade(const void* q, int32_t dtype, const void* k_cach
                             ea);
   if (st != PKV_OK || nothing) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = pkv_host::from_hip(pkv_launch::prefill(pa, head_dim, s),
-                          "paged_attn_cascade: prefix pass launch");
+  if (w == 0) {
+    st = pkv_host::from_hip(pkv_launch::prefill(pa, head_dim, s),
+                            "paged_attn_cascade: prefix pass launch");
+  } else {
+    const pkv_host::DraftPlan plan = pkv_host::draft_plan(
+        batch, total_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, w);
+    PKV_REQUIRE(plan.bytes == 0 || (workspace != nullptr && workspace_bytes >= plan.bytes),
+                PKV_EINVAL, "paged_attn_cascade: workspace of %zu bytes, need %zu",
+                workspace_bytes, plan.bytes);
+    pkv::DraftPrefixArgs da{};
+    pkv::DecodeArgs& d = da.d;
+    d.q = q;
+    d.k = k_cache;
+    d.v = v_cache;
+    d.pt = page_table;
+    d.pt_stride = pt_stride;
+    d.kv_lens = kv_lens;
+    d.batch = batch;
+    d.hq = num_q_heads;
+    d.hkv = num_kv_heads;
+    d.page_size = page_size;
+    d.num_pages = num_pages;
+    d.scale_log2 = pkv_host::scale_log2(softmax_scale);
+    d.chunk = plan.chunk;
+    d.num_splits = plan.splits;
+    d.out = out;
+    d.lse = lse;
+    d.window_left = -1;
+    d.attn_chunk = 0;
+    da.cu_q = cu_seqlens_q;
+    da.total_q = total_q;
+    if (plan.splits > 1) {
+      char* ws = static_cast<char*>(workspace);
+      da.part_o = ws + PKV_WORKSPACE_COUNTER_BYTES;
+      da.part_lse = reinterpret_cast<float*>(ws + PKV_WORKSPACE_COUNTER_BYTES + plan.o_bytes);
+    }
+    st = pkv_host::from_hip(pkv_launch::draft_prefix(da, head_dim, s),
+                            "paged_attn_cascade: prefix pass launch");
+  }
   if (st != PKV_OK) return st;
   return pkv_host::from_hip(pkv_launch::expand_merge(ea, head_dim, s),
                             "paged_attn_cascade: expand pass launch");

@@ -97,6 +97,18 @@ struct PrefillArgs {
   int32_t attn_chunk;   // > 0: chunked local attention; else none (causal only)
 };
 
+// Prefix pass of draft-tree (cascade) verification on packed query rows:
+// request b's M_b = cu_q[b+1] - cu_q[b] rows (G * M_b <= 32) see all kv_lens[b]
+// committed keys. The split fields of `d` (chunk, num_splits) and its page
+// table and lengths drive the split order; d.q, d.k, d.v are the tensors.
+struct DraftPrefixArgs {
+  DecodeArgs d;
+  const int32_t* cu_q;   // [batch + 1]
+  int32_t total_q;
+  void* part_o;          // [num_splits, total_q, Hq, D] bf16 (num_splits > 1)
+  float* part_lse;       // [num_splits, total_q, Hq]
+};
+
 struct SparseArgs {
   const void* q;
   const void* kv;

@@ -12,6 +12,7 @@ struct PrefillArgs;
 struct SparseArgs;
 struct CascadeExpandArgs;
 struct ExpandMergeArgs;
+struct DraftPrefixArgs;
 struct DcaTableArgs;
 }  // namespace pkv
 
@@ -36,5 +37,10 @@ hipError_t sparse_topk(const pkv::SparseArgs& a, hipStream_t stream);
 hipError_t sparse_topk_noalloc(const pkv::SparseArgs& a, bool split, hipStream_t stream);
 hipError_t cascade_expand(const pkv::CascadeExpandArgs& a, hipStream_t stream);
 hipError_t expand_merge(const pkv::ExpandMergeArgs& a, int head_dim, hipStream_t stream);
+// kv heads per workgroup of the packed draft prefix pass (4, 2 or 1), or 0
+// where it does not apply (then the prefill kernel runs the prefix pass)
+int draft_prefix_heads(int dtype, int head_dim, int num_q_heads, int num_kv_heads,
+                       int max_seqlen_q);
+hipError_t draft_prefix(const pkv::DraftPrefixArgs& a, int head_dim, hipStream_t stream);
 hipError_t dca_tables(const pkv::DcaTableArgs& a, hipStream_t stream);
 }  // namespace pkv_launch

@@ -24,7 +24,8 @@ def test_header_declares_the_entry_points():
                "paged_attn_varlen_prefill_append", "build_cascade_expand_table",
                "paged_attn_expand_merge", "paged_attn_cascade", "build_dca_decode_tables",
                "paged_attn_dca_decode", "sparse_topk_decode_noalloc",
-               "paged_attn_decode_merged", "paged_attn_decode_merged_workspace_size"]:
+               "paged_attn_decode_merged", "paged_attn_decode_merged_workspace_size",
+               "paged_attn_cascade_workspace_size"]:
         assert fn in names
 
 
@@ -211,6 +212,45 @@ def test_cascade_argument_errors():
     bad = list(base)
     bad[15] = 96
     assert cz(*bad, fake, 8, fake, None, 0, fake, fake, None) == EUNSUP
+
+
+def test_cascade_workspace_plan():
+    """Packed prefix pass (G * max_seqlen_q <= 32): key splits of a multiple of
+    32 keys (at least 256) sized for about 512 workgroups over (kv-head group
+    of 4, request, split) when every request is max_seqlen_k long; with more
+    than one split the workspace holds bf16 partials and fp32 LSEs per split.
+    Shapes the packed pass does not take size the prefill kernel's workspace."""
+    lib = pkv.load_library()
+    size = lib.paged_attn_cascade_workspace_size
+    up = lambda v: (v + 255) // 256 * 256
+    # tree verification: 64 requests x 8 drafts, 32 q / 8 kv heads (two groups
+    # of four), 16384 keys: 4 splits of 4096
+    rows = 4 * 512 * 32
+    assert size(64, 512, 8, 16384, 32, 8, 128) == COUNTER_BYTES + up(rows * 128 * 2) + up(rows * 4)
+    assert size(64, 512, 8, 16384, 32, 8, 64) == COUNTER_BYTES + up(rows * 64 * 2) + up(rows * 4)
+    # one split (256 keys): no workspace
+    assert size(64, 512, 8, 256, 32, 8, 128) == 0
+    # 2 requests x 2 groups: 128 splits wanted, 256 keys each -> 4096 keys in 16
+    rows = 16 * 16 * 32
+    assert size(2, 16, 8, 4096, 32, 8, 128) == COUNTER_BYTES + up(rows * 128 * 2) + up(rows * 4)
+    # kv heads not a multiple of 4 take groups of 2 (or 1): 8 requests x 1 group
+    # want 64 splits; the 256-key floor leaves 16
+    rows = 16 * 40 * 8
+    assert size(8, 40, 5, 4096, 8, 2, 128) == COUNTER_BYTES + up(rows * 128 * 2) + up(rows * 4)
+    # G * max_seqlen_q = 36 > 32: the prefill kernel's plan
+    prefill = lib.paged_attn_varlen_prefill_workspace_size
+    assert size(1, 9, 9, 8192, 32, 8, 128) == prefill(1, 9, 9, 8192, 32, 8, 128)
+    assert size(0, 16, 8, 4096, 32, 8, 128) == 0
+    # a packed call that needs a workspace rejects a missing or short one
+    # before any launch
+    fake = ctypes.c_void_p(256)
+    cz = lib.paged_attn_cascade
+    base = [fake, 1, fake, fake, 64, fake, 64, fake, fake, 2, 16, 8, 4096, 32, 8, 128, 64, 0.1,
+            fake, 8, fake]
+    need = size(2, 16, 8, 4096, 32, 8, 128)
+    assert cz(*base, None, 0, fake, fake, None) == EINVAL
+    assert b"workspace" in lib.pkv_last_error()
+    assert cz(*base, fake, need - 1, fake, fake, None) == EINVAL
 
 
 def test_dca_argument_errors():

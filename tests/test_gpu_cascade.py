@@ -76,6 +76,43 @@ def test_cascade_vs_tree_attention(D, P, hq, hkv, n, tree):
     assert_close("lse", np_f(lse), rl, LSE_TOL)
 
 
+@pytest.mark.parametrize("D,P,hq,hkv,prefix,extend,zero,mk", [
+    # G * max M <= 32: the packed prefix pass; kv heads per workgroup 4, 2, 1
+    (128, 16, 32, 8, [0, 33, 300, 1029, 2000], [8, 1, 5, 8, 3], None, None),
+    (128, 1, 16, 4, [1, 31, 32, 255, 256, 257], [2, 8, 3, 1, 8, 4], 2, None),
+    (128, 3, 8, 2, [40, 700, 0], [8, 5, 4], None, 300),   # max_seqlen_k below the longest
+    (64, 64, 4, 1, [0, 5, 2000], [8, 7, 5], 0, None),
+    (64, 16, 32, 4, [100, 1500], [4, 3], None, 256),
+])
+def test_packed_prefix_pass_vs_noncausal_prefill(D, P, hq, hkv, prefix, extend, zero, mk):
+    """With every expand list empty, paged_attn_cascade is its prefix pass
+    alone: each request's rows see all its keys (non-causal prefill). Ragged
+    draft counts, lengths around the 32-key tiles and the 256-key splits, a
+    request with no key (`zero`), and a max_seqlen_k below the longest request
+    (its last split then runs to the end)."""
+    lens = [p + e for p, e in zip(prefix, extend)]
+    pages = sum(-(-L // P) for L in lens) + len(lens) + 4
+    c = to_device(workloads.make_prefill_case(780 + D + P + hq, prefix_lens=prefix,
+                                              extend_lens=extend, num_q_heads=hq,
+                                              num_kv_heads=hkv, head_dim=D, page_size=P,
+                                              num_pages=pages), DEV)
+    say(f"packed prefix pass D={D} P={P} Hq={hq} Hkv={hkv} M={extend} L={lens} mk={mk}")
+    pt, kl, _ = pkv.build_page_table(c.req_to_token, c.req_pool_indices, c.seq_lens, P,
+                                     c.table_width)
+    if zero is not None:
+        kl[zero] = 0
+    total_q = c.q.shape[0]
+    tab = torch.zeros((total_q, 1), dtype=torch.int32, device=DEV)
+    lens_e = torch.zeros((total_q,), dtype=torch.int32, device=DEV)
+    out, lse = pkv.paged_attn_cascade(c.q, c.k_cache, c.v_cache, pt, c.cu_seqlens_q, kl,
+                                      c.max_seqlen_q, c.scale, tab, lens_e, max_seqlen_k=mk)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_prefill(np_f(c.q), np_f(c.k_cache), np_f(c.v_cache), np_i(pt),
+                                  np_i(c.cu_seqlens_q), np_i(kl), P, c.scale, causal=False)
+    assert_close("out", np_f(out), ro, O_TOL)
+    assert_close("lse", np_f(lse), rl, LSE_TOL)
+
+
 def test_expand_merge_alone_vs_staged_oracle():
     """The separate entry point: prefix pass by the prefill call (non-causal),
     then paged_attn_expand_merge in place, against the oracle's three steps."""

@@ -119,8 +119,7 @@ def test_cascade_step_graph():
     tab = torch.empty((B * n, n), dtype=torch.int32, device=DEV)
     lens = torch.empty((B * n,), dtype=torch.int32, device=DEV)
     cu_q = torch.arange(0, B * n + 1, n, dtype=torch.int32, device=DEV)
-    need = pkv.paged_attn_varlen_prefill_workspace_size(B, B * n, n, c.table_width * 16, 16, 4,
-                                                        128)
+    need = pkv.paged_attn_cascade_workspace_size(B, B * n, n, c.table_width * 16, 16, 4, 128)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=DEV)
     out = torch.empty_like(c.q)
     lse = torch.empty((B * n, 16), dtype=torch.float32, device=DEV)
