@@ -1,7 +1,8 @@
 // build_page_table: req_to_token rows -> per-request page table, kv_lens and
-// cu_seqlens_k, in one launch. Strided mode follows the "strided format"
-// conversion of [FA] init_forward_metadata; the prefill-aware sliding-window
-// mode follows [FA] _build_pa_page_table_kernel.
+// cu_seqlens_k, in one launch. Strided mode reduces each request's token
+// slots to the ids of its pages ([FA] init_forward_metadata); the
+// prefill-aware sliding-window mode keeps the prompt and the newest window of
+// decoded positions ([FA] _build_pa_page_table_kernel).
 //
 // Grid: x = request, y = column blocks of 256 over `width`. Every element of
 // page_table is written (zero past the request's length). Block (0, 0)
