@@ -75,11 +75,38 @@ def device_clock_mhz():
         return None
 
 
+def code_text(src):
+    """C/C++ source without its comments, whitespace runs collapsed: the part of a
+    file that decides the compiled kernel (string and character literals kept)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(*names):
+    """Hash of the code (comments and layout excluded) of the named csrc files."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "paged_kv_cache_197_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_197_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 
