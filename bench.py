@@ -33,6 +33,7 @@ WORKLOAD_SOURCES = {
     "decode_split": ["decode.hip", "splits.hpp", "merge_state.hip", "page_table.hip",
                      "common.hpp", "args.hpp"],
     "decode_merged": ["decode.hip", "splits.hpp", "page_table.hip", "common.hpp", "args.hpp"],
+    "decode_window": ["decode.hip", "splits.hpp", "page_table.hip", "common.hpp", "args.hpp"],
     "swa": ["decode.hip", "splits.hpp", "page_table.hip", "common.hpp", "args.hpp"],
     "sparse": ["sparse_mla.hip", "common.hpp", "lanes.hpp", "lds_dma.hpp", "args.hpp"],
     "cascade": ["cascade.hip", "draft_prefix.hip", "splits.hpp", "common.hpp", "lanes.hpp",
@@ -1013,17 +1014,21 @@ def main(argv=None):
     if args.only in ("all", "decode_window"):
         try:
             W = 4095
-            r = run_decode(torch, pkv, workloads, args, window_left=W, kv_chunk=2048)
+            r = run_decode(torch, pkv, workloads, args, window_left=W, kv_chunk=2048,
+                           mode="balanced")
             extra["decode_window"] = {
                 "workload": "config3 under an in-kernel sliding window (W, 0) with W = 4095 "
                             "(each query sees its last 4096 keys) over the strided table; "
-                            "2048-token chunks, 16 splits",
-                "device_ms_per_step": round(r["ms"], 4), "decode_kernel_ms": round(r["kernel_ms"], 4),
+                            "merged decode over balanced ranges (the visible keys cut into 256 "
+                            "equal workgroup shares, one per CU, parts merged in the same launch)",
+                "device_ms_per_step": round(r["ms"], 4),
+                "decode_merge_kernel_ms": round(r["kernel_ms"], 4),
                 "kernel_GB/s": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 2),
                 "kernel_frac_hbm": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
                                          / HBM_PEAK_GBS, 4),
                 "visible_keys": r["sum_l"], "algorithmic_bytes": r["bytes"],
-                "num_splits": r["splits"]}
+                "split_mode": "balanced ranges",
+                "traffic": stored_traffic("decode_window", r["bytes"])}
             if not args.no_cpu_baseline:
                 extra["decode_window"]["cpu_oracle"] = cpu_oracle_decode_window(torch, r, W, 4.0)
         except Exception as e:
