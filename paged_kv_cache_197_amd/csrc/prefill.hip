@@ -89,12 +89,17 @@ struct PrefillKernel {
   // key of S^T accumulator register r for lane half h
   static __device__ __forceinline__ int rho(int h, int r) { return 8 * (r >> 2) + 4 * h + (r & 3); }
   // LDS chunk position of global chunk c of key row k (an involution in c).
-  // u = row index within a 256-byte bank span, rotated left by one bit: the
-  // 16 rows of a K operand read get distinct chunk positions, and so do the
-  // chunk pairs of 4 consecutive rows read by a transposed V read.
+  // The LDS serves 256 bytes (64 banks) per cycle: 16 lanes of a 16-byte read
+  // or 32 lanes of an 8-byte one. u = the row's index among the CH rows whose
+  // chunks a position cycle covers (SWZ rows share one 256-byte bank span);
+  // the chunk is XORed with u transposed on a (CH/4) x 4 grid, so that the
+  // 16 rows of one K operand read pass (one chunk each) land on 16 distinct
+  // positions, and so do the 4 rows x 4 chunks of one 32-lane pass of a
+  // transposed V read (whose rows form an aligned group of four).
   static __device__ __forceinline__ int swz(int k, int c) {
+    constexpr int A = CH / 4;
     const int u = (k / SWZ) % CH;
-    return c ^ (((2 * u) % CH) | ((2 * u) / CH));
+    return c ^ (4 * (u % A) + u / A);
   }
 
   static __device__ __forceinline__ int page_col(const PrefillArgs& a, int t) {
