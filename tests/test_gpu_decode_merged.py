@@ -300,6 +300,25 @@ def test_balanced_config3_full_size():
     assert_close("lse vs fixed splits", np_f(lse), np_f(fl), LSE_TOL)
 
 
+def test_balanced_config3_window_full_size():
+    """config3 decoded under a (4095, 0) window with balanced ranges (the
+    windowed decode workload in the launch configuration the benchmark times):
+    sampled requests against the oracle, every request against split decode
+    with 2048-token chunks followed by merge_state (within the output
+    tolerance of each other: the two cut the keys differently)."""
+    c = to_device(workloads.config3(value_device=DEV), DEV)
+    W = 4095
+    say(f"balanced config3 window W={W} full")
+    pt, kl = strided_table(c)
+    lens = np_i(c.seq_lens)
+    rows = sorted({int(lens.argmin()), int(lens.argmax()), 5, 40})
+    out, lse = check_balanced(c, pt, kl, rows=rows, window_left=W)
+    S = (int(lens.max()) + 2047) // 2048
+    uo, ul = unfused(c, pt, kl, 2048, S, window_left=W)
+    assert_close("out vs split decode", np_f(out), np_f(uo), O_TOL)
+    assert_close("lse vs split decode", np_f(lse), np_f(ul), LSE_TOL)
+
+
 def test_balanced_workspace_reused_across_shapes():
     a = to_device(workloads.make_decode_case(91, seq_lens=[700, 5, 0, 1300], num_q_heads=16,
                                              num_kv_heads=2, head_dim=128, page_size=16,
