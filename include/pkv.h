@@ -13,7 +13,8 @@
  *   - Every array argument is a caller-owned DEVICE pointer (hipMalloc'd or a
  *     torch tensor's data_ptr()), dense and row-major in the layout given.
  *     The library allocates nothing, keeps no state between calls and is
- *     reentrant.
+ *     reentrant; the one exception is sparse_topk_decode_noalloc, whose
+ *     per-GPU static device array holds its split workspace (see there).
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on
  *     it and the call returns without synchronising.
  *   - Return value is a pkv_status_t. Argument errors that the host can see
