@@ -13,14 +13,14 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def gpu_prefill(c, causal=True, workspace=None):
+def gpu_prefill(c, causal=True, workspace=None, window_left=-1):
     pt, kl, _ = pkv.build_page_table(c.req_to_token, c.req_pool_indices, c.seq_lens, c.page_size,
                                      c.table_width)
     out = torch.full_like(c.q, float("nan"))
     lse = torch.full(c.q.shape[:2], float("nan"), device=DEV)
     pkv.paged_attn_varlen_prefill(c.q, c.k_cache, c.v_cache, pt, c.cu_seqlens_q, kl,
                                   c.max_seqlen_q, c.scale, causal=causal, workspace=workspace,
-                                  out=out, lse=lse)
+                                  window_left=window_left, out=out, lse=lse)
     torch.cuda.synchronize()
     return out, lse, pt, kl
 
@@ -109,16 +109,18 @@ def test_prefill_deterministic_and_page_permutation_invariant():
     assert torch.equal(a[0], d[0]) and torch.equal(a[1], d[1])
 
 
-def test_long_prompt_sampled_rows():
-    """The long-prompt bench workload (4 x 4096 new tokens, every q tile of
-    the last request sees up to 128 key tiles): sampled rows against the
-    oracle, each row posed as a one-row extend over its visible prefix."""
+@pytest.mark.parametrize("window_left", [-1, 1023])
+def test_long_prompt_sampled_rows(window_left):
+    """The long-prompt bench workloads (4 x 4096 new tokens, every q tile of
+    the last request sees up to 128 key tiles; plain and under the (1023, 0)
+    window): sampled rows against the oracle, each row posed as a one-row
+    extend over its prefix with the same window."""
     c = to_device(workloads.long_prompt_prefill(value_device=DEV), DEV)
     B, n = 4, 4096
     need = pkv.paged_attn_varlen_prefill_workspace_size(B, c.q.shape[0], n, n, 32, 8, 128)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=DEV)
-    say(f"long prompt prefill 4 x 4096, workspace {need}")
-    out, lse, pt, kl = gpu_prefill(c, workspace=ws)
+    say(f"long prompt prefill 4 x 4096 window_left={window_left}, workspace {need}")
+    out, lse, pt, kl = gpu_prefill(c, workspace=ws, window_left=window_left)
     pt_np = np_i(pt)
     g = np.random.default_rng(3)
     rows = [(0, 0), (0, 31), (1, 32), (2, 1000), (3, 4095)] + \
@@ -130,7 +132,8 @@ def test_long_prompt_sampled_rows():
         v = np_f(c.v_cache[slots])
         r = b * n + j
         ro, rl = oracle.paged_prefill(np_f(c.q[r:r + 1]), k, v, np.arange(L)[None, :],
-                                      np.array([0, 1]), np.array([L]), 1, c.scale, causal=True)
+                                      np.array([0, 1]), np.array([L]), 1, c.scale, causal=True,
+                                      window_left=window_left)
         assert_close(f"out row {b},{j}", np_f(out[r:r + 1]), ro, O_TOL)
         assert_close(f"lse row {b},{j}", np_f(lse[r:r + 1]), rl, LSE_TOL)
 
